@@ -1,0 +1,262 @@
+"""Benchmark of the paged decode hot path on one MI355X.
+
+A step is one decode step of one layer for the whole batch: cache_write of
+every sequence's new token into its slot, then paged decode attention of
+every sequence over its context (new token included).  Steps rotate over
+`--layers` layer slices of one pool so that the KV read each step is not
+served from the 256 MB last-level cache.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+
+Prints one JSON line.  `value` is the step's algorithmic bytes (K/V of the
+attended tokens, queries, outputs, tables, the written K/V) per second;
+`roofline` relates the attention call's algorithmic bytes to its average
+duration (HIP events on the launch stream) and the 8 TB/s HBM peak;
+`cpu_baseline` times the CPU oracle on a bounded sample of the same batch.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention: achieved HBM GB/s (% of peak) + seq·layer steps/s"
+HBM_PEAK_GBS = 8000.0
+DEFAULT_LAYERS = {1: 1, 2: 2, 3: 1, 4: 4, 5: 2}  # layer slices so that each step reads >= ~1 GB
+KERNEL_SOURCES = ("decode_mfma.hip", "decode_valu.hip", "decode_reduce.hip", "cache_write.hip", "internal.h",
+                  "kvpool_api.cpp")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_37_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(config: int, variant: str):
+    """Counter-measured HBM bytes per attention call, if the profiles were
+    taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_config{config}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_hash") != kernel_hash() or rec.get("variant") != variant:
+        return None
+    return rec.get("hbm_bytes_per_call")
+
+
+def copy_probe(mib: int) -> None:
+    """A plain device-to-device copy of known size (counter calibration)."""
+    import torch
+
+    n = mib * (1 << 20)
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copied {mib} MiB x3")
+
+
+def cpu_baseline(w, budget_s: float = 12.0) -> dict:
+    """Time the CPU oracle (as it is, one thread) on whole sequences of the
+    batch until the budget is spent."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    done, kv_bytes = 0, 0
+    per_token = 2 * w.num_kv_heads * w.head_dim * w.elt_bytes
+    valid = w.valid_tokens()
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for s in range(w.num_seqs):
+            oracle.decode_attention_seq(w.pool, 0, w.q[s], w.block_tables[s], int(w.seq_lens[s]), w.window, w.scale)
+            done += 1
+            kv_bytes += int(valid[s]) * per_token
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+    return {
+        "value": kv_bytes / dt / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done} of {w.num_seqs} sequences, all {w.num_q_heads} query heads, layer 0 "
+                  f"(fp64 numpy, one thread): {done / dt:.2f} seq-layer steps/s",
+        "seconds": dt,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--layers", type=int, default=None, help="layer slices to rotate over")
+    ap.add_argument("--variant", default="auto", choices=["auto", "mfma", "valu"])
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a device copy of MIB MiB (counter calibration) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (see the sharding notes "
+              "in DESIGN.md); run it with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return 0
+
+    import workloads as W
+    from paged_kv_cache_37_amd import ops
+
+    dev = torch.device("cuda:0")
+    L = args.layers or DEFAULT_LAYERS[args.config]
+    log(f"generating config {args.config} with {L} layer slice(s)")
+    t0 = time.time()
+    w = W.make(args.config, args.seed, num_layers=L)
+    W.with_next_token(w, w.unused_blocks)
+    log(f"generated in {time.time() - t0:.1f}s: {w.name}, {w.num_blocks} blocks/layer")
+
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if dt == torch.bfloat16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    pool = ops.KVPool(L, w.num_blocks, w.num_kv_heads, w.head_dim, dt, dev)
+    pool.load_logical(torch.from_numpy(w.pool.view(np.int16)).view(torch.bfloat16) if dt == torch.bfloat16
+                      else torch.from_numpy(w.pool))
+    q = up(w.q)
+    k_new, v_new = up(w.k_new), up(w.v_new)
+    slots = torch.from_numpy(w.slot_mapping).to(dev)
+    tables = torch.from_numpy(w.block_tables_after).to(dev)
+    lens = torch.from_numpy(w.seq_lens_after).to(dev)
+    out = torch.empty_like(q)
+    ws = ops.make_workspace(pool, w.num_seqs, w.num_q_heads, tables.shape[1], args.partition_tokens)
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+
+    def step(i):
+        layer = i % L
+        ops.cache_write(pool, layer, k_new, v_new, slots, stream=stream)
+        ops.paged_decode_attention(pool, layer, q, tables, lens, w.scale, out=out, sliding_window=w.window,
+                                   partition_tokens=args.partition_tokens, variant=args.variant, workspace=ws,
+                                   stream=stream)
+
+    log(f"warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"timing {K} steps")
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        layer = i % L
+        ev[i][0].record(stream)
+        ops.cache_write(pool, layer, k_new, v_new, slots, stream=stream)
+        ev[i][1].record(stream)
+        ops.paged_decode_attention(pool, layer, q, tables, lens, w.scale, out=out, sliding_window=w.window,
+                                   partition_tokens=args.partition_tokens, variant=args.variant, workspace=ws,
+                                   stream=stream)
+        ev[i][2].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    write_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    attn_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    ms_per_step = total_ms / K
+    log(f"step {ms_per_step * 1e3:.1f} us (write {write_ms * 1e3:.1f} us, attention {attn_ms * 1e3:.1f} us)")
+
+    # algorithmic bytes
+    S, Hq, D, Hkv, eb = w.num_seqs, w.num_q_heads, w.head_dim, w.num_kv_heads, w.elt_bytes
+    valid_after = np.minimum(w.seq_lens_after, w.window) if w.window else w.seq_lens_after
+    kv_read = int(valid_after.astype(np.int64).sum()) * 2 * Hkv * D * eb
+    attn_bytes = kv_read + 2 * S * Hq * D * eb + int(np.asarray(w.row_blocks_after).sum()) * 4 + S * 4
+    write_bytes = 2 * 2 * S * Hkv * D * eb + S * 4
+    step_bytes = attn_bytes + write_bytes
+    achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    variant = args.variant if args.variant != "auto" else ("mfma" if w.dtype == "bf16" else "valu")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "num_seqs": S,
+            "num_q_heads": Hq,
+            "num_kv_heads": Hkv,
+            "head_dim": D,
+            "block_size": 16,
+            "context_tokens_total": int(valid_after.sum()),
+            "sliding_window": w.window,
+            "layer_slices": L,
+            "variant": variant,
+            "partition_tokens": args.partition_tokens,
+            "seed": w.seed,
+        },
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "seq_layer_steps_per_s": round(S / (ms_per_step * 1e-3), 1),
+        "attention_us": round(attn_ms * 1e3, 2),
+        "cache_write_us": round(write_ms * 1e3, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_profiles(args.config, variant),
+            "kernel": "paged_decode_attention (decode + split-K reduce launches)",
+            "bytes_per_call": attn_bytes,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

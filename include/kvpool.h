@@ -1,0 +1,226 @@
+/*
+ * kvpool.h -- C ABI of the MI355X (gfx950) paged KV-cache library.
+ *
+ * One hot path: decode attention over a KV cache held in a pool of fixed
+ * 16-token blocks, and the cache write that stores each new token's K and V
+ * into its slot.  Sources (page titles as printed):
+ *
+ *  [Optimizing] "Optimizing KV Cache Memory Management in vLLM with
+ *     PagedAttention and Dynamic Block Allocation"
+ *       - section "PagedAttention: Virtual Memory for LLMs": logical block
+ *         index floor(i / B), offset i mod B, the kernel looks the physical
+ *         block up in the sequence's block table and computes the address;
+ *       - section "The Block Manager and Dynamic Allocation Lifecycle"
+ *         (Prefill / Decode phases): prompt and decode K/V are written into
+ *         the physical blocks; decode appends into the last block;
+ *       - section "The Math of the KV Cache Bottleneck": GQA/MQA, fewer KV
+ *         heads than query heads.
+ *  [Paged] the paged-attention post on zhangchitc.github.io
+ *       - section "What a physical block looks like": the pool is split per
+ *         layer into num_blocks blocks of [2, block_size, num_kv_heads,
+ *         head_dim]; a block id names the same block in every layer.
+ *  [Memory] "The memory behind the next token"
+ *       - section "Why the next token needs yesterday's state": exact layouts
+ *         depend on the attention backend; a sliding window drops the blocks
+ *         it no longer needs.
+ *  [Pool] "How the block pool manages KV memory"
+ *       - section "Hybrid models get groups": a sliding-window layer keeps
+ *         only the blocks inside the last window.
+ *
+ * The pages give no formula for attention itself; the library computes the
+ * standard decode attention out_h = softmax(q_h K^T * scale) V for every
+ * query head h, with KV head h / G (G = num_q_heads / num_kv_heads).
+ *
+ * Conventions
+ *  - Every device pointer is caller-owned memory (e.g. a torch tensor); the
+ *    library allocates no device memory and keeps no pointer past a call,
+ *    except the pool handle, which borrows its base pointer.
+ *  - All work is enqueued asynchronously on the given hipStream_t (NULL = the
+ *    default stream); the calls return after the launch.
+ *  - Status codes are int32_t (kvp_status).  Arguments are checked before any
+ *    launch; on error nothing is launched and kvp_last_error() returns a
+ *    thread-local message.
+ *  - Device data are not validated on the fast path, but kernels never
+ *    read or write outside the pool, the table row, or the output: a slot or
+ *    block id outside [0, num_blocks*16) / [0, num_blocks) is skipped.
+ */
+#ifndef KVPOOL_H
+#define KVPOOL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVP_OK = 0,
+  KVP_ERR_INVALID_ARG = -1,      /* a pointer, size or index is out of range */
+  KVP_ERR_UNSUPPORTED = -2,      /* a valid but unimplemented shape or dtype */
+  KVP_ERR_WORKSPACE_TOO_SMALL = -3,
+  KVP_ERR_HIP = -4               /* the HIP runtime refused a launch */
+} kvp_status;
+
+typedef enum { KVP_F32 = 0, KVP_BF16 = 1 } kvp_dtype;
+
+/* Kernel variant for paged_decode_attention. */
+typedef enum {
+  KVP_VARIANT_AUTO = 0,  /* MFMA for bf16 with head_dim 64/128, else VALU  */
+  KVP_VARIANT_VALU = 1,  /* vector ALU dot products, any supported dtype    */
+  KVP_VARIANT_MFMA = 2   /* matrix cores for QK^T and PV (bf16 only)        */
+} kvp_variant;
+
+/*
+ * Pool geometry.  block_size must be 16 (the pages' default block).
+ * head_dim 64 or 128.  dtype KVP_F32 or KVP_BF16.
+ */
+typedef struct {
+  int32_t num_layers;
+  int32_t num_blocks;     /* physical blocks per layer */
+  int32_t block_size;     /* == 16 */
+  int32_t num_kv_heads;
+  int32_t head_dim;       /* 64 or 128 */
+  int32_t dtype;          /* kvp_dtype */
+} kvp_pool_desc;
+
+typedef struct kvp_pool_s* kvp_pool;  /* opaque, immutable after create */
+
+/*
+ * Device layout of the pool (elements of the pool dtype).  For layer l,
+ * physical block b, KV head h, slot t (0..15) and dimension d:
+ *
+ *   blk   = (l * num_blocks + b) * 2 * num_kv_heads * 16 * head_dim
+ *   K(t,d) = blk + (              h) * 16 * head_dim + t * head_dim + d
+ *   V(t,d) = blk + (num_kv_heads + h) * 16 * head_dim
+ *                + ((t / 4) * head_dim + d) * 4 + (t % 4)
+ *
+ * i.e. per block all K tiles, then all V tiles; a (block, head) K tile is
+ * one contiguous row-major [16][head_dim] array and a V tile is
+ * [4][head_dim][4]: for each group of four slots, the four slots' values
+ * of one dimension sit next to each other.  This is the pages' block shape
+ * [2, block_size, num_kv_heads, head_dim] with heads moved outside slots
+ * (one contiguous tile per head) and V's slots interleaved in fours, which
+ * the attention backend is free to choose ([Memory], "Why the next token
+ * needs yesterday's state").
+ */
+
+/* Bytes a pool of this geometry occupies; 0 if the geometry is invalid. */
+size_t kv_pool_bytes(const kvp_pool_desc* desc);
+
+/*
+ * Create a handle over caller-owned device memory `dev_base` of `bytes`
+ * bytes (>= kv_pool_bytes(desc), 256-byte aligned).  The memory is not
+ * touched.  The handle borrows dev_base and must not outlive it.
+ * Errors: KVP_ERR_INVALID_ARG (null pointers, misalignment, too small),
+ * KVP_ERR_UNSUPPORTED (block_size != 16, head_dim not 64/128, dtype).
+ */
+int32_t kv_pool_create(const kvp_pool_desc* desc, void* dev_base, size_t bytes, kvp_pool* out);
+
+/* Release the handle (not the memory).  NULL is accepted. */
+int32_t kv_pool_destroy(kvp_pool pool);
+
+/* Copy the geometry of a handle into *desc. */
+int32_t kv_pool_describe(kvp_pool pool, kvp_pool_desc* desc);
+
+/*
+ * Element offset (from dev_base) of K (kv = 0) or V (kv = 1) of
+ * (layer, block, head, slot, dim), per the layout above; -1 if any index is
+ * out of range.  Host-side helper for loaders and tests.
+ */
+int64_t kv_pool_offset(kvp_pool pool, int32_t layer, int32_t block, int32_t kv, int32_t head,
+                       int32_t slot, int32_t dim);
+
+/*
+ * cache_write -- store new tokens' K and V into their slots of one layer.
+ *   [Optimizing] "The Block Manager and Dynamic Allocation Lifecycle": in
+ *   prefill the kernel writes the prompt's K/V into the allocated blocks; in
+ *   decode the new token's K/V go to the free slot of the last block.
+ *
+ *   k_new, v_new : device, [num_tokens][num_kv_heads][head_dim], pool dtype,
+ *                  contiguous.
+ *   slot_mapping : device int32 [num_tokens]; slot = block * 16 + offset
+ *                  ([Optimizing] "PagedAttention": floor(i/B), i mod B).
+ *                  A negative slot (padding) writes nothing; a slot
+ *                  >= num_blocks*16 writes nothing.  Two tokens naming the
+ *                  same slot in one call leave that slot undefined.
+ *   The copy is bit-exact.  num_tokens == 0 launches nothing.
+ */
+int32_t cache_write(kvp_pool pool, int32_t layer, const void* k_new, const void* v_new,
+                    const int32_t* slot_mapping, int32_t num_tokens, hipStream_t stream);
+
+/* Arguments of paged_decode_attention (all device pointers caller-owned). */
+typedef struct {
+  int32_t layer;
+  const void* q;                /* [num_seqs][num_q_heads][head_dim], pool dtype */
+  void* out;                    /* same shape and dtype as q                    */
+  const int32_t* block_tables;  /* [num_seqs][max_blocks_per_seq]               */
+  int32_t max_blocks_per_seq;   /* row stride of block_tables (>= 1)            */
+  const int32_t* seq_lens;      /* [num_seqs], absolute context lengths (>= 0)  */
+  int32_t sliding_window;       /* 0 = attend to the whole context              */
+  int32_t num_seqs;
+  int32_t num_q_heads;          /* multiple of the pool's num_kv_heads          */
+  float scale;                  /* softmax scale, e.g. 1/sqrt(head_dim)         */
+  int32_t partition_tokens;     /* 0 = auto; else a multiple of 16 <= 1024      */
+  int32_t variant;              /* kvp_variant                                  */
+  void* workspace;              /* device scratch, may be NULL if not needed    */
+  size_t workspace_bytes;
+} kvp_decode_args;
+
+/*
+ * Bytes of workspace paged_decode_attention needs for these sizes (0 when a
+ * single pass suffices, i.e. every row fits in one partition).
+ */
+size_t paged_decode_workspace_bytes(kvp_pool pool, int32_t num_seqs, int32_t num_q_heads,
+                                    int32_t max_blocks_per_seq, int32_t partition_tokens);
+
+/*
+ * paged_decode_attention -- one decode step of one layer.
+ *   [Optimizing] "PagedAttention: Virtual Memory for LLMs": for each
+ *   sequence the kernel walks its block table (row s of block_tables,
+ *   [Paged] "Two lookup structures": req_to_blocks is the ordered
+ *   logical-to-physical list) and reads each key and value where the table
+ *   says it lives.
+ *
+ *   Rows.  With sliding_window == 0, row s lists logical blocks
+ *   0 .. (ctx-1)/16 and all ctx = seq_lens[s] tokens are attended.  With a
+ *   window W > 0 ([Pool] "Hybrid models get groups") row s lists only the
+ *   blocks covering positions max(0, ctx-W) .. ctx-1: logical blocks
+ *   max(0,ctx-W)/16 .. (ctx-1)/16; the first max(0,ctx-W) % 16 slots of
+ *   its first block are not attended.  Entries past the row's length are
+ *   never read.  A row with ctx == 0 yields zeros.
+ *
+ *   out[s][h] = sum_i p_i V_i with p = softmax(K q[s][h] * scale) over the
+ *   attended keys of KV head h / G; fp32 accumulation, output rounded to
+ *   the pool dtype (round to nearest even for bf16).
+ *
+ *   Long rows are split into partitions of partition_tokens table slots;
+ *   each partition leaves its partial result (running max, sum and
+ *   unnormalised output) in `workspace` (paged_decode_workspace_bytes()
+ *   bytes) and the last partition of a row to finish merges them.  The
+ *   workspace ends with one arrival counter per (sequence, query head): it
+ *   must be zero-filled before its first use, and every call leaves it
+ *   zero-filled again.  Calls that share one workspace must not overlap.
+ *
+ *   Environment: KVP_DECODE_DEPTH (1..3) overrides how many blocks each
+ *   wave keeps in flight ahead of the one it computes (a tuning knob).
+ *
+ *   Errors: KVP_ERR_INVALID_ARG (nulls, layer, heads, partition size),
+ *   KVP_ERR_UNSUPPORTED (variant/dtype/head group combination),
+ *   KVP_ERR_WORKSPACE_TOO_SMALL, KVP_ERR_HIP.
+ */
+int32_t paged_decode_attention(kvp_pool pool, const kvp_decode_args* args, hipStream_t stream);
+
+/* Static text of a status code. */
+const char* kvp_status_str(int32_t status);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char* kvp_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVPOOL_H */

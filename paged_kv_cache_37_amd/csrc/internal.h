@@ -1,0 +1,68 @@
+// Internal declarations shared by the kernels and the C-ABI layer of
+// libkvpool.  Not part of the public interface (see include/kvpool.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvp {
+
+constexpr int kBlock = 16;      // tokens per block (the pages' default block size)
+constexpr int kWaves = 4;       // waves per decode workgroup
+constexpr int kThreads = 64 * kWaves;
+
+// Geometry and arguments of one decode launch, resolved on the host.
+struct DecodeParams {
+  const void* pool_layer;       // first element of this layer's blocks
+  const void* q;                // [S][Hq][D]
+  void* out;                    // [S][Hq][D]
+  const int32_t* block_tables;  // [S][max_blocks]
+  const int32_t* seq_lens;      // [S]
+  float* part_o;                // [S][Hq][num_parts][D]      (split only)
+  float* part_ml;               // [S][Hq][num_parts][2]      (split only)
+  int* counters;                // [S][Hq] arrival counts, zero between calls (split only)
+  int32_t max_blocks;           // row stride of block_tables
+  int32_t window;               // 0 = full context
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t num_blocks;           // physical blocks per layer (bounds check)
+  int32_t group;                // query heads per KV head (G)
+  int32_t heads_per_wg;         // query heads one workgroup serves (<= 16)
+  int32_t qgroups;              // workgroups per KV head = ceil(G / heads_per_wg)
+  int32_t part_blocks;          // table entries per partition
+  int32_t num_parts;            // partitions of the longest possible row
+  float scale_log2;             // scale * log2(e): scores are kept in base 2
+  int32_t depth;                // blocks of K/V a wave keeps in flight ahead of the one it computes
+};
+
+// Span of one block-table row: leading slots of the first block that are
+// not attended (sliding window only), attended keys, and entries used.
+struct RowSpan {
+  int start_off;
+  int n;
+  int nblocks;
+};
+
+__device__ __forceinline__ RowSpan row_span(int ctx, int window, int max_blocks) {
+  RowSpan r{0, 0, 0};
+  if (ctx <= 0) return r;
+  const int first = (window > 0 && ctx > window) ? ctx - window : 0;
+  r.start_off = first & (kBlock - 1);
+  r.n = ctx - first;
+  r.nblocks = (r.start_off + r.n + kBlock - 1) / kBlock;
+  if (r.nblocks > max_blocks) {  // row longer than the table: attend what the table holds
+    r.nblocks = max_blocks;
+    r.n = max_blocks * kBlock - r.start_off;
+  }
+  return r;
+}
+
+// Launchers (each defined next to its kernel).
+hipError_t launch_cache_write(void* pool_layer, int dtype, int num_blocks, int num_kv_heads,
+                              int head_dim, const void* k_new, const void* v_new,
+                              const int32_t* slots, int num_tokens, hipStream_t stream);
+hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int head_dim, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t stream);
+
+}  // namespace kvp

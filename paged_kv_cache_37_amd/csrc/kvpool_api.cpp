@@ -1,0 +1,273 @@
+// C-ABI of libkvpool: argument checks, geometry, variant and partition
+// choice, launches.  Declared in include/kvpool.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "internal.h"
+#include "kvpool.h"
+
+struct kvp_pool_s {
+  kvp_pool_desc desc;
+  void* base;
+  size_t bytes;
+};
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int32_t ok() {
+  g_err[0] = '\0';
+  return KVP_OK;
+}
+
+size_t elt_bytes(int32_t dtype) { return dtype == KVP_F32 ? 4 : 2; }
+
+// Elements of one layer: num_blocks * 2 * Hkv * 16 * D.
+size_t layer_elems(const kvp_pool_desc& d) {
+  return (size_t)d.num_blocks * 2 * (size_t)d.num_kv_heads * kvp::kBlock * (size_t)d.head_dim;
+}
+
+int32_t check_desc(const kvp_pool_desc* d) {
+  if (!d) return fail(KVP_ERR_INVALID_ARG, "desc is NULL");
+  if (d->num_layers < 1 || d->num_blocks < 1 || d->num_kv_heads < 1)
+    return fail(KVP_ERR_INVALID_ARG, "num_layers, num_blocks and num_kv_heads must be >= 1");
+  if (d->block_size != kvp::kBlock) return fail(KVP_ERR_UNSUPPORTED, "block_size must be 16 (got %d)", d->block_size);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(KVP_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", d->head_dim);
+  if (d->dtype != KVP_F32 && d->dtype != KVP_BF16) return fail(KVP_ERR_UNSUPPORTED, "dtype must be F32 or BF16");
+  if ((size_t)d->num_blocks * kvp::kBlock > (size_t)INT32_MAX)
+    return fail(KVP_ERR_INVALID_ARG, "num_blocks * 16 must fit in int32 slot numbers");
+  return KVP_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Partition size in table entries.
+int32_t resolve_part_blocks(int32_t partition_tokens, int32_t num_seqs, int32_t wg_per_seq_head_part,
+                            int32_t max_blocks) {
+  if (partition_tokens > 0) return partition_tokens / kvp::kBlock;
+  // Auto: 512-token partitions; shorter when the grid would not fill the chip.
+  int32_t pb = 32;
+  const long wgs = (long)num_seqs * wg_per_seq_head_part * ((max_blocks + pb - 1) / pb);
+  if (wgs < 2048) pb = 16;
+  return pb;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kv_pool_bytes(const kvp_pool_desc* desc) {
+  if (check_desc(desc) != KVP_OK) return 0;
+  return (size_t)desc->num_layers * layer_elems(*desc) * elt_bytes(desc->dtype);
+}
+
+int32_t kv_pool_create(const kvp_pool_desc* desc, void* dev_base, size_t bytes, kvp_pool* out) {
+  if (!out) return fail(KVP_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  const int32_t st = check_desc(desc);
+  if (st != KVP_OK) return st;
+  if (!dev_base) return fail(KVP_ERR_INVALID_ARG, "dev_base is NULL");
+  if (!aligned(dev_base, 256)) return fail(KVP_ERR_INVALID_ARG, "dev_base must be 256-byte aligned");
+  const size_t need = kv_pool_bytes(desc);
+  if (bytes < need) return fail(KVP_ERR_INVALID_ARG, "pool memory too small: %zu < %zu bytes", bytes, need);
+  kvp_pool_s* p = new (std::nothrow) kvp_pool_s{*desc, dev_base, bytes};
+  if (!p) return fail(KVP_ERR_INVALID_ARG, "out of host memory");
+  *out = p;
+  return ok();
+}
+
+int32_t kv_pool_destroy(kvp_pool pool) {
+  delete pool;
+  return ok();
+}
+
+int32_t kv_pool_describe(kvp_pool pool, kvp_pool_desc* desc) {
+  if (!pool || !desc) return fail(KVP_ERR_INVALID_ARG, "NULL argument");
+  *desc = pool->desc;
+  return ok();
+}
+
+int64_t kv_pool_offset(kvp_pool pool, int32_t layer, int32_t block, int32_t kv, int32_t head, int32_t slot,
+                       int32_t dim) {
+  if (!pool) return -1;
+  const kvp_pool_desc& d = pool->desc;
+  if (layer < 0 || layer >= d.num_layers || block < 0 || block >= d.num_blocks || kv < 0 || kv > 1 || head < 0 ||
+      head >= d.num_kv_heads || slot < 0 || slot >= kvp::kBlock || dim < 0 || dim >= d.head_dim)
+    return -1;
+  const int64_t tile = (int64_t)kvp::kBlock * d.head_dim;
+  const int64_t blk = ((int64_t)layer * d.num_blocks + block) * 2 * d.num_kv_heads * tile;
+  if (kv == 0) return blk + (int64_t)head * tile + (int64_t)slot * d.head_dim + dim;
+  return blk + (int64_t)(d.num_kv_heads + head) * tile + ((int64_t)(slot / 4) * d.head_dim + dim) * 4 + slot % 4;
+}
+
+int32_t cache_write(kvp_pool pool, int32_t layer, const void* k_new, const void* v_new,
+                    const int32_t* slot_mapping, int32_t num_tokens, hipStream_t stream) {
+  if (!pool) return fail(KVP_ERR_INVALID_ARG, "pool is NULL");
+  const kvp_pool_desc& d = pool->desc;
+  if (layer < 0 || layer >= d.num_layers) return fail(KVP_ERR_INVALID_ARG, "layer %d out of range", layer);
+  if (num_tokens < 0) return fail(KVP_ERR_INVALID_ARG, "num_tokens < 0");
+  if (num_tokens == 0) return ok();
+  if (!k_new || !v_new || !slot_mapping) return fail(KVP_ERR_INVALID_ARG, "NULL k_new, v_new or slot_mapping");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(slot_mapping, 4))
+    return fail(KVP_ERR_INVALID_ARG, "k_new/v_new must be 16-byte aligned");
+  char* base = (char*)pool->base + (size_t)layer * layer_elems(d) * elt_bytes(d.dtype);
+  const hipError_t e = kvp::launch_cache_write(base, d.dtype, d.num_blocks, d.num_kv_heads, d.head_dim, k_new,
+                                               v_new, slot_mapping, num_tokens, stream);
+  if (e != hipSuccess) return fail(KVP_ERR_HIP, "cache_write launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+static int32_t plan(kvp_pool pool, int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks, int32_t partition_tokens,
+                    int32_t variant, kvp::DecodeParams* p, int32_t* use_mfma) {
+  const kvp_pool_desc& d = pool->desc;
+  if (num_seqs < 0 || num_seqs > 65535) return fail(KVP_ERR_INVALID_ARG, "num_seqs must be in [0, 65535]");
+  if (num_q_heads < 1 || num_q_heads % d.num_kv_heads != 0)
+    return fail(KVP_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                num_q_heads, d.num_kv_heads);
+  if (max_blocks < 1) return fail(KVP_ERR_INVALID_ARG, "max_blocks_per_seq must be >= 1");
+  if (partition_tokens != 0 &&
+      (partition_tokens % kvp::kBlock != 0 || partition_tokens < kvp::kBlock || partition_tokens > 64 * kvp::kBlock))
+    return fail(KVP_ERR_INVALID_ARG, "partition_tokens must be 0 or a multiple of 16 in [16, 1024]");
+  const int32_t G = num_q_heads / d.num_kv_heads;
+  int32_t mfma = 0;
+  if (variant == KVP_VARIANT_AUTO)
+    mfma = d.dtype == KVP_BF16;
+  else if (variant == KVP_VARIANT_MFMA) {
+    if (d.dtype != KVP_BF16) return fail(KVP_ERR_UNSUPPORTED, "the MFMA variant needs a bf16 pool");
+    mfma = 1;
+  } else if (variant != KVP_VARIANT_VALU)
+    return fail(KVP_ERR_INVALID_ARG, "unknown variant %d", variant);
+  int32_t hpw;
+  if (mfma) {
+    hpw = G < 16 ? G : 16;
+  } else {
+    hpw = 1;
+    while (hpw < G && hpw < 8) hpw *= 2;
+  }
+  const int32_t qgroups = (G + hpw - 1) / hpw;
+  if ((long)d.num_kv_heads * qgroups > 65535) return fail(KVP_ERR_UNSUPPORTED, "too many head groups");
+  // the partition size depends on the row geometry only, never on the variant,
+  // so paged_decode_workspace_bytes() is valid for every variant
+  const int32_t pb = resolve_part_blocks(partition_tokens, num_seqs, d.num_kv_heads, max_blocks);
+  std::memset(p, 0, sizeof(*p));
+  p->max_blocks = max_blocks;
+  p->num_seqs = num_seqs;
+  p->num_q_heads = num_q_heads;
+  p->num_kv_heads = d.num_kv_heads;
+  p->num_blocks = d.num_blocks;
+  p->group = G;
+  p->heads_per_wg = hpw;
+  p->qgroups = qgroups;
+  p->part_blocks = pb;
+  p->num_parts = (max_blocks + pb - 1) / pb;
+  *use_mfma = mfma;
+  return KVP_OK;
+}
+
+// Workspace of a split launch: unnormalised partial outputs, their (max,
+// sum) pairs, and one arrival counter per (sequence, query head).  The
+// counters must be zero before the first call; every call leaves them zero.
+static size_t workspace_layout(const kvp::DecodeParams& p, int32_t head_dim, size_t* ml_off, size_t* ctr_off) {
+  if (p.num_parts <= 1) {
+    *ml_off = *ctr_off = 0;
+    return 0;
+  }
+  const size_t rows = (size_t)p.num_seqs * p.num_q_heads * p.num_parts;
+  const size_t o_bytes = (rows * head_dim * sizeof(float) + 255) & ~(size_t)255;
+  const size_t ml_bytes = (rows * 2 * sizeof(float) + 255) & ~(size_t)255;
+  *ml_off = o_bytes;
+  *ctr_off = o_bytes + ml_bytes;
+  return o_bytes + ml_bytes + (size_t)p.num_seqs * p.num_q_heads * sizeof(int);
+}
+
+static int32_t decode_depth(int32_t mfma) {
+  // Blocks of K/V each wave keeps in flight ahead of the one it computes.
+  static const int env = [] {
+    const char* e = getenv("KVP_DECODE_DEPTH");
+    return e ? atoi(e) : 0;
+  }();
+  if (env >= 1 && env <= (mfma ? 3 : 2)) return env;
+  return mfma ? 2 : 1;
+}
+
+size_t paged_decode_workspace_bytes(kvp_pool pool, int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                    int32_t partition_tokens) {
+  if (!pool) return 0;
+  kvp::DecodeParams p;
+  int32_t mfma;
+  if (plan(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, KVP_VARIANT_AUTO, &p, &mfma) != KVP_OK)
+    return 0;
+  size_t ml_off, ctr_off;
+  return workspace_layout(p, pool->desc.head_dim, &ml_off, &ctr_off);
+}
+
+int32_t paged_decode_attention(kvp_pool pool, const kvp_decode_args* a, hipStream_t stream) {
+  if (!pool || !a) return fail(KVP_ERR_INVALID_ARG, "NULL pool or args");
+  const kvp_pool_desc& d = pool->desc;
+  if (a->layer < 0 || a->layer >= d.num_layers) return fail(KVP_ERR_INVALID_ARG, "layer %d out of range", a->layer);
+  if (a->sliding_window < 0) return fail(KVP_ERR_INVALID_ARG, "sliding_window < 0");
+  if (!std::isfinite(a->scale)) return fail(KVP_ERR_INVALID_ARG, "scale is not finite");
+  kvp::DecodeParams p;
+  int32_t mfma = 0;
+  int32_t st = plan(pool, a->num_seqs, a->num_q_heads, a->max_blocks_per_seq, a->partition_tokens, a->variant, &p, &mfma);
+  if (st != KVP_OK) return st;
+  if (a->num_seqs == 0) return ok();
+  if (!a->q || !a->out || !a->block_tables || !a->seq_lens)
+    return fail(KVP_ERR_INVALID_ARG, "NULL q, out, block_tables or seq_lens");
+  if (!aligned(a->q, 16) || !aligned(a->out, 16) || !aligned(a->block_tables, 4) || !aligned(a->seq_lens, 4))
+    return fail(KVP_ERR_INVALID_ARG, "q/out must be 16-byte aligned, tables and lengths 4-byte aligned");
+  size_t ml_off = 0, ctr_off = 0;
+  const size_t ws = workspace_layout(p, d.head_dim, &ml_off, &ctr_off);
+  if (ws > 0) {
+    if (!a->workspace || a->workspace_bytes < ws)
+      return fail(KVP_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes needed (%zu given)", ws,
+                  a->workspace ? a->workspace_bytes : (size_t)0);
+    if (!aligned(a->workspace, 256)) return fail(KVP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    p.part_o = (float*)a->workspace;
+    p.part_ml = (float*)((char*)a->workspace + ml_off);
+    p.counters = (int*)((char*)a->workspace + ctr_off);
+  }
+  p.pool_layer = (const char*)pool->base + (size_t)a->layer * layer_elems(d) * elt_bytes(d.dtype);
+  p.q = a->q;
+  p.out = a->out;
+  p.block_tables = a->block_tables;
+  p.seq_lens = a->seq_lens;
+  p.window = a->sliding_window;
+  p.scale_log2 = a->scale * 1.4426950408889634f;
+  p.depth = decode_depth(mfma);
+  const hipError_t e = mfma ? kvp::launch_decode_mfma(p, d.head_dim, stream)
+                      : kvp::launch_decode_valu(p, d.dtype, d.head_dim, stream);
+  if (e != hipSuccess) return fail(KVP_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+const char* kvp_status_str(int32_t status) {
+  switch (status) {
+    case KVP_OK: return "ok";
+    case KVP_ERR_INVALID_ARG: return "invalid argument";
+    case KVP_ERR_UNSUPPORTED: return "unsupported";
+    case KVP_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case KVP_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* kvp_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,186 @@
+"""Python face of libkvpool: the C-ABI calls under the same names, taking
+torch tensors.  Argument marshalling only -- shapes are checked, pointers and
+the current HIP stream are handed to the library, every computation runs in
+the library's kernels.  torch provides device memory and streams.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import DecodeArgs, KVPoolError, PoolDesc, check, lib
+
+BLOCK_SIZE = 16
+
+_DTYPES = {torch.float32: _lib.KVP_F32, torch.bfloat16: _lib.KVP_BF16}
+_VARIANTS = {"auto": _lib.KVP_VARIANT_AUTO, "valu": _lib.KVP_VARIANT_VALU, "mfma": _lib.KVP_VARIANT_MFMA}
+
+
+def _stream(device: torch.device, stream: Optional[torch.cuda.Stream]) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, device=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the pool on {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+class KVPool:
+    """A pool of 16-token KV blocks in one torch allocation, with the
+    library handle over it.  Layout: include/kvpool.h."""
+
+    def __init__(self, num_layers: int, num_blocks: int, num_kv_heads: int, head_dim: int,
+                 dtype: torch.dtype = torch.bfloat16, device="cuda"):
+        if dtype not in _DTYPES:
+            raise ValueError(f"unsupported pool dtype {dtype}")
+        self.desc = PoolDesc(num_layers, num_blocks, BLOCK_SIZE, num_kv_heads, head_dim, _DTYPES[dtype])
+        nbytes = lib.kv_pool_bytes(ctypes.byref(self.desc))
+        if nbytes == 0:
+            check(_lib.KVP_ERR_UNSUPPORTED if head_dim not in (64, 128) else _lib.KVP_ERR_INVALID_ARG,
+                  "kv_pool_bytes")
+        self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
+        self.dtype = dtype
+        self.num_layers, self.num_blocks = num_layers, num_blocks
+        self.num_kv_heads, self.head_dim = num_kv_heads, head_dim
+        self.nbytes = int(nbytes)
+        self.storage = torch.empty(self.nbytes, dtype=torch.uint8, device=self.device)
+        handle = ctypes.c_void_p()
+        check(lib.kv_pool_create(ctypes.byref(self.desc), ctypes.c_void_p(self.storage.data_ptr()),
+                                 self.nbytes, ctypes.byref(handle)), "kv_pool_create")
+        self.handle = handle
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value:
+            lib.kv_pool_destroy(h)
+            self.handle = None
+
+    # -- layout helpers (host side; loading and inspecting pools) --------
+
+    def flat(self) -> torch.Tensor:
+        """The pool as a flat tensor of its dtype."""
+        return self.storage.view(self.dtype)
+
+    def offset(self, layer: int, block: int, kv: int, head: int, slot: int, dim: int) -> int:
+        return int(lib.kv_pool_offset(self.handle, layer, block, kv, head, slot, dim))
+
+    def _tiles(self) -> torch.Tensor:
+        L, NB, H, D = self.num_layers, self.num_blocks, self.num_kv_heads, self.head_dim
+        return self.flat().view(L, NB, 2, H, BLOCK_SIZE * D)
+
+    def load_logical(self, logical: torch.Tensor) -> None:
+        """Fill the pool from a tensor in the logical block shape
+        [L, NB, 2, 16, Hkv, D] (K = 0, V = 1)."""
+        L, NB, H, D = self.num_layers, self.num_blocks, self.num_kv_heads, self.head_dim
+        if tuple(logical.shape) != (L, NB, 2, BLOCK_SIZE, H, D):
+            raise ValueError(f"logical pool must be {(L, NB, 2, BLOCK_SIZE, H, D)}, got {tuple(logical.shape)}")
+        src = logical.to(device=self.device)
+        if src.dtype != self.dtype:
+            raise ValueError(f"logical pool dtype {src.dtype} != pool dtype {self.dtype}")
+        tiles = self._tiles()
+        # K tile [16][D] per (block, head); V tile [4][D][4] (slot t -> (t//4, d, t%4))
+        tiles[:, :, 0].view(L, NB, H, BLOCK_SIZE, D).copy_(src[:, :, 0].permute(0, 1, 3, 2, 4))
+        tiles[:, :, 1].view(L, NB, H, 4, D, 4).copy_(
+            src[:, :, 1].reshape(L, NB, 4, 4, H, D).permute(0, 1, 4, 2, 5, 3))
+
+    def to_logical(self) -> torch.Tensor:
+        """The pool in the logical block shape [L, NB, 2, 16, Hkv, D]."""
+        L, NB, H, D = self.num_layers, self.num_blocks, self.num_kv_heads, self.head_dim
+        tiles = self._tiles()
+        k = tiles[:, :, 0].reshape(L, NB, H, BLOCK_SIZE, D).permute(0, 1, 3, 2, 4)
+        v = tiles[:, :, 1].reshape(L, NB, H, 4, D, 4).permute(0, 1, 3, 5, 2, 4).reshape(L, NB, BLOCK_SIZE, H, D)
+        return torch.stack([k, v], dim=2).contiguous()
+
+
+def kv_pool_create(num_layers: int, num_blocks: int, num_kv_heads: int, head_dim: int,
+                   dtype: torch.dtype = torch.bfloat16, device="cuda") -> KVPool:
+    return KVPool(num_layers, num_blocks, num_kv_heads, head_dim, dtype, device)
+
+
+def cache_write(pool: KVPool, layer: int, k_new: torch.Tensor, v_new: torch.Tensor,
+                slot_mapping: torch.Tensor, stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Store token t's K/V ([T, Hkv, D]) at slot slot_mapping[t] of `layer`."""
+    T = int(slot_mapping.shape[0]) if slot_mapping.dim() == 1 else -1
+    if T < 0:
+        raise ValueError("slot_mapping must be 1-D")
+    shape = (T, pool.num_kv_heads, pool.head_dim)
+    _need(k_new, "k_new", pool.dtype, pool.device, shape)
+    _need(v_new, "v_new", pool.dtype, pool.device, shape)
+    _need(slot_mapping, "slot_mapping", torch.int32, pool.device)
+    check(lib.cache_write(pool.handle, layer, ctypes.c_void_p(k_new.data_ptr()),
+                          ctypes.c_void_p(v_new.data_ptr()), ctypes.c_void_p(slot_mapping.data_ptr()), T,
+                          _stream(pool.device, stream)), "cache_write")
+
+
+def paged_decode_workspace_bytes(pool: KVPool, num_seqs: int, num_q_heads: int, max_blocks_per_seq: int,
+                                 partition_tokens: int = 0) -> int:
+    return int(lib.paged_decode_workspace_bytes(pool.handle, num_seqs, num_q_heads, max_blocks_per_seq,
+                                                partition_tokens))
+
+
+def make_workspace(pool: KVPool, num_seqs: int, num_q_heads: int, max_blocks_per_seq: int,
+                   partition_tokens: int = 0) -> Optional[torch.Tensor]:
+    """Zero-filled workspace (its arrival counters must start at zero; every
+    call leaves them zero).  Calls that share one workspace must not overlap."""
+    n = paged_decode_workspace_bytes(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens)
+    return torch.zeros(n, dtype=torch.uint8, device=pool.device) if n else None
+
+
+def paged_decode_attention(pool: KVPool, layer: int, q: torch.Tensor, block_tables: torch.Tensor,
+                           seq_lens: torch.Tensor, scale: float, out: Optional[torch.Tensor] = None,
+                           sliding_window: int = 0, partition_tokens: int = 0, variant: str = "auto",
+                           workspace: Optional[torch.Tensor] = None,
+                           stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Decode attention of q [S, Hq, D] over the pool through block_tables
+    [S, max_blocks] and seq_lens [S]; returns out [S, Hq, D]."""
+    if q.dim() != 3:
+        raise ValueError("q must be [num_seqs, num_q_heads, head_dim]")
+    S, Hq, D = q.shape
+    _need(q, "q", pool.dtype, pool.device)
+    if D != pool.head_dim:
+        raise ValueError(f"q head_dim {D} != pool head_dim {pool.head_dim}")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    _need(block_tables, "block_tables", torch.int32, pool.device)
+    _need(seq_lens, "seq_lens", torch.int32, pool.device, (S,))
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", pool.dtype, pool.device, tuple(q.shape))
+    if variant not in _VARIANTS:
+        raise ValueError(f"variant must be one of {sorted(_VARIANTS)}")
+    mb = int(block_tables.shape[1])
+    if workspace is None:
+        workspace = make_workspace(pool, S, Hq, mb, partition_tokens)
+    elif workspace.device != pool.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the pool's device")
+    args = DecodeArgs(
+        layer=layer, q=q.data_ptr(), out=out.data_ptr(), block_tables=block_tables.data_ptr(),
+        max_blocks_per_seq=mb, seq_lens=seq_lens.data_ptr(), sliding_window=sliding_window,
+        num_seqs=S, num_q_heads=Hq, scale=float(scale), partition_tokens=partition_tokens,
+        variant=_VARIANTS[variant],
+        workspace=workspace.data_ptr() if workspace is not None else None,
+        workspace_bytes=workspace.numel() * workspace.element_size() if workspace is not None else 0,
+    )
+    check(lib.paged_decode_attention(pool.handle, ctypes.byref(args), _stream(pool.device, stream)),
+          "paged_decode_attention")
+    return out
+
+
+__all__ = ["KVPool", "KVPoolError", "kv_pool_create", "cache_write", "paged_decode_workspace_bytes",
+           "make_workspace", "paged_decode_attention", "BLOCK_SIZE"]

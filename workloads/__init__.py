@@ -357,30 +357,32 @@ def custom(seed: int, ctx, num_q_heads: int, num_kv_heads: int, head_dim: int,
 def with_next_token(w: Workload, fresh_blocks) -> Workload:
     """Add one next-token K/V per sequence at position seq_lens[s]; a
     sequence whose last block is full takes the next block of `fresh_blocks`
-    (the decode-append rule: a block boundary allocates).  Values and the
-    slot of each token (physical block * block_size + offset) are recorded;
-    the pool itself is left untouched."""
-    if w.window:
-        raise ValueError("next-token writes are drawn for full-attention workloads only")
+    (the decode-append rule: a block boundary allocates).  Values, the slot
+    of each token (physical block * block_size + offset) and the tables for
+    context seq_lens + 1 are recorded (under a window the row then starts at
+    the block holding position seq_lens + 1 - window); the pool itself is
+    left untouched."""
     B = w.block_size
     fresh = list(fresh_blocks)
     T = w.num_seqs
     slots = np.empty(T, dtype=np.int32)
-    rows = [list(w.block_tables[s, : w.row_blocks[s]]) for s in range(T)]
+    rows = []
     for s in range(T):
         pos = int(w.seq_lens[s])
-        lb, off = divmod(pos, B)
-        if lb == len(rows[s]):
-            rows[s].append(fresh.pop(0))
-        slots[s] = rows[s][lb] * B + off
+        row = list(w.block_tables[s, : w.row_blocks[s]])
+        first_block = _row_span(pos, w.window, B)[0] if pos > 0 else 0
+        lb = pos // B - first_block
+        if lb == len(row):
+            row.append(fresh.pop(0))
+        slots[s] = row[lb] * B + pos % B
+        new_first = _row_span(pos + 1, w.window, B)[0]
+        rows.append(row[new_first - first_block:])
     w.k_new = _store(_normal_f32(w.seed, 11, (T, w.num_kv_heads, w.head_dim)), w.dtype)
     w.v_new = _store(_normal_f32(w.seed, 12, (T, w.num_kv_heads, w.head_dim)), w.dtype)
     w.slot_mapping = slots
     width = max(w.block_tables.shape[1], max(len(r) for r in rows))
-    bt = np.array(w.block_tables[:, :width]) if w.block_tables.shape[1] >= width else None
-    if bt is None:
-        bt = np.full((T, width), w.block_tables[0, -1], dtype=np.int32)
-        bt[:, : w.block_tables.shape[1]] = w.block_tables
+    bt = np.full((T, width), w.block_tables[0, -1], dtype=np.int32)
+    bt[:, : w.block_tables.shape[1]] = w.block_tables
     for s, r in enumerate(rows):
         bt[s, : len(r)] = r
     w.block_tables_after = bt
