@@ -29,8 +29,8 @@ sys.path.insert(0, ROOT)
 METRIC = "paged decode attention: achieved HBM GB/s (% of peak) + seq·layer steps/s"
 HBM_PEAK_GBS = 8000.0
 DEFAULT_LAYERS = {1: 1, 2: 2, 3: 1, 4: 4, 5: 2}  # layer slices so that each step reads >= ~1 GB
-KERNEL_SOURCES = ("decode_mfma.hip", "decode_valu.hip", "decode_reduce.hip", "cache_write.hip", "internal.h",
-                  "kvpool_api.cpp")
+KERNEL_SOURCES = ("decode_stream.hip", "decode_mfma.hip", "decode_valu.hip", "decode_reduce.hip", "cache_write.hip",
+                  "mfma_tile.h", "decode_common.h", "internal.h", "kvpool_api.cpp")
 
 
 def log(*a):
@@ -111,7 +111,7 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None, help="layer slices to rotate over")
-    ap.add_argument("--variant", default="auto", choices=["auto", "mfma", "valu"])
+    ap.add_argument("--variant", default="auto", choices=["auto", "stream", "mfma", "valu"])
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -206,7 +206,9 @@ def main() -> int:
     step_bytes = attn_bytes + write_bytes
     achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    variant = args.variant if args.variant != "auto" else ("mfma" if w.dtype == "bf16" else "valu")
+    variant = args.variant
+    if variant == "auto":
+        variant = "valu" if w.dtype == "f32" else ("mfma" if args.partition_tokens else "stream")
 
     result = {
         "metric": METRIC,
@@ -246,7 +248,7 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_from_profiles(args.config, variant),
-            "kernel": "paged_decode_attention (decode + split-K reduce launches)",
+            "kernel": "paged_decode_attention (decode + merge launches)",
             "bytes_per_call": attn_bytes,
         },
         "cpu_baseline": None,

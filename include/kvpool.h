@@ -68,9 +68,13 @@ typedef enum { KVP_F32 = 0, KVP_BF16 = 1 } kvp_dtype;
 
 /* Kernel variant for paged_decode_attention. */
 typedef enum {
-  KVP_VARIANT_AUTO = 0,  /* MFMA for bf16 with head_dim 64/128, else VALU  */
-  KVP_VARIANT_VALU = 1,  /* vector ALU dot products, any supported dtype    */
-  KVP_VARIANT_MFMA = 2   /* matrix cores for QK^T and PV (bf16 only)        */
+  KVP_VARIANT_AUTO = 0,   /* bf16: STREAM (MFMA with partition_tokens > 0 or
+                             more than 4096 sequences); fp32: VALU            */
+  KVP_VARIANT_VALU = 1,   /* vector ALU dot products, partitioned rows        */
+  KVP_VARIANT_MFMA = 2,   /* matrix cores for QK^T and PV, partitioned rows
+                             (bf16 only)                                      */
+  KVP_VARIANT_STREAM = 3  /* matrix cores, persistent waves that split the
+                             batch's blocks evenly (bf16, <= 4096 sequences)  */
 } kvp_variant;
 
 /*
@@ -199,10 +203,8 @@ size_t paged_decode_workspace_bytes(kvp_pool pool, int32_t num_seqs, int32_t num
  *   Long rows are split into partitions of partition_tokens table slots;
  *   each partition leaves its partial result (running max, sum and
  *   unnormalised output) in `workspace` (paged_decode_workspace_bytes()
- *   bytes) and the last partition of a row to finish merges them.  The
- *   workspace ends with one arrival counter per (sequence, query head): it
- *   must be zero-filled before its first use, and every call leaves it
- *   zero-filled again.  Calls that share one workspace must not overlap.
+ *   bytes, contents need no initialisation) and a second kernel on the same
+ *   stream merges them.  Calls that share one workspace must not overlap.
  *
  *   Environment: KVP_DECODE_DEPTH (1..3) overrides how many blocks each
  *   wave keeps in flight ahead of the one it computes (a tuning knob).

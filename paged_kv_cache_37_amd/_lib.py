@@ -26,6 +26,7 @@ KVP_BF16 = 1
 KVP_VARIANT_AUTO = 0
 KVP_VARIANT_VALU = 1
 KVP_VARIANT_MFMA = 2
+KVP_VARIANT_STREAM = 3
 
 EXPORTS = (
     "kv_pool_bytes",

@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvpool.so")
 
-SOURCES = ["kvpool_api.cpp", "cache_write.hip", "decode_mfma.hip", "decode_valu.hip"]
+SOURCES = ["kvpool_api.cpp", "cache_write.hip", "decode_mfma.hip", "decode_valu.hip", "decode_reduce.hip",
+           "decode_stream.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -1,7 +1,6 @@
-// Device helpers shared by the two decode kernels: cross-lane reductions,
-// bf16 rounding, and the end of a partition (merge of the workgroup's
-// waves, then either the final normalisation or the split-K partial with a
-// last-arriving-workgroup merge).
+// Device helpers shared by the decode kernels: cross-lane reductions, bf16
+// rounding, and the end of a partition (merge of the workgroup's waves,
+// then either the final normalisation or the split-K partial).
 #pragma once
 
 #include "internal.h"
@@ -60,16 +59,12 @@ __device__ __forceinline__ void store_out(void* out, size_t idx, float v) {
 // m_s[w][h] (base 2), weight sum l_s[w][h] and unnormalised output
 // o_s[w][h][d] in LDS (synchronised by the caller).  With M = max_w m_w,
 //   num = sum_w 2^(m_w - M) o_w,   den = sum_w 2^(m_w - M) l_w.
-// A row held by one partition stores num/den.  Otherwise the partition
-// writes (M, den, num) to the workspace; the workgroup that completes a row
-// last (a device-scope counter per row and head group) merges all of the
-// row's partitions the same way and stores the output, then resets the
-// counter to zero for the next call.
+// A row held by one partition stores num/den; otherwise the partition's
+// (M, den, num) go to the workspace for decode_reduce.
 template <typename OutT, int D, int ROWS>
 __device__ __forceinline__ void finish_partition(const DecodeParams& P, float (*o_s)[ROWS][D + 1],
                                                  float (*m_s)[ROWS], float (*l_s)[ROWS], int s, int h0, int nh,
                                                  int part, int nparts) {
-  __shared__ int last_flag;
   for (int i = threadIdx.x; i < nh * D; i += kThreads) {
     const int hh = i / D, d = i - hh * D;
     float M = -INFINITY;
@@ -94,34 +89,6 @@ __device__ __forceinline__ void finish_partition(const DecodeParams& P, float (*
         P.part_ml[(row_h * P.num_parts + part) * 2 + 1] = den;
       }
     }
-  }
-  if (nparts == 1) return;
-  __threadfence();  // partials visible device-wide before the count
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int* ctr = P.counters + (size_t)s * P.num_q_heads + h0;
-    last_flag = atomicAdd(ctr, 1) == nparts - 1;
-    if (last_flag) *ctr = 0;
-  }
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();  // acquire: read the other workgroups' partials from L2
-  for (int i = threadIdx.x; i < nh * D; i += kThreads) {
-    const int hh = i / D, d = i - hh * D;
-    const size_t row_h = (size_t)s * P.num_q_heads + h0 + hh;
-    const float* ml = P.part_ml + row_h * P.num_parts * 2;
-    const float* o = P.part_o + row_h * P.num_parts * D + d;
-    float M = -INFINITY;
-    for (int p = 0; p < nparts; ++p) M = fmaxf(M, __builtin_nontemporal_load(ml + 2 * p));
-    float num = 0.f, den = 0.f;
-    if (M != -INFINITY) {
-      for (int p = 0; p < nparts; ++p) {
-        const float f = __builtin_amdgcn_exp2f(__builtin_nontemporal_load(ml + 2 * p) - M);
-        num += f * __builtin_nontemporal_load(o + (size_t)p * D);
-        den += f * __builtin_nontemporal_load(ml + 2 * p + 1);
-      }
-    }
-    store_out<OutT>(P.out, row_h * D + d, den > 0.f ? num / den : 0.f);
   }
 }
 

@@ -1,0 +1,388 @@
+// Paged decode attention on the CDNA4 matrix cores (bf16 pools), streaming
+// form: a persistent grid of exactly the resident waves splits the batch's
+// work evenly, whatever the mix of sequence lengths.
+//
+// The work is the list of tiles (head group, sequence, table entry): row
+// (hg, s) has one tile per block-table entry of sequence s, each tile being
+// one 16-token block of K/V for that KV head ("PagedAttention: Virtual
+// Memory for LLMs" in "Optimizing KV Cache Memory Management in vLLM with
+// PagedAttention and Dynamic Block Allocation": the kernel walks the
+// sequence's block table to find each block).  Wave w streams the
+// contiguous tile range [w T / W, (w+1) T / W).  Its loads run DEPTH tiles
+// ahead of its compute across row boundaries: every in-flight tile carries
+// its row context, and the next row's table entries and queries are fetched
+// while the current row streams.  A row that lies wholly inside a wave's
+// range is normalised and stored by that wave; the (at most two) rows cut by
+// a range boundary leave a partial result (running max, sum, unnormalised
+// output) that decode_stream_reduce merges.
+//
+// Ranges are contiguous per XCD (workgroup i runs on XCD i mod 8): the
+// tiles of one head group, which share physical blocks across sequences
+// with a common prefix, stay in one XCD's L2.
+#include "mfma_tile.h"
+
+namespace kvp {
+namespace {
+
+#ifndef KVP_STREAM_WAVES_PER_EU
+#define KVP_STREAM_WAVES_PER_EU 2
+#endif
+
+// Index of this workgroup when the grid is ordered XCD by XCD.
+__device__ __forceinline__ int xcd_major_index(int wg, int nwg) {
+  const int x = wg & 7, k = wg >> 3;
+  return x * (nwg >> 3) + min(x, nwg & 7) + k;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_scan(int v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(v, off);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// A row of the work list and what the waves need to know about it.
+struct RowCtx {
+  int hg, s;      // head group, sequence
+  int nb;         // table entries (tiles) of the row
+  long long a;    // first tile of the row in the work list
+};
+
+// Tile ring entry: loads in flight plus the tile's place in its row.
+template <int D>
+struct StreamTile {
+  MfmaTiles<D> t;
+  int j;       // table entry within the row
+  int row_id;  // rows of this wave counted from 0
+};
+
+template <int D, int DEPTH>
+__global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stream_kernel(const DecodeParams P) {
+  constexpr int NBUF = DEPTH + 1;
+  __shared__ int pre[kMaxStreamSeqs + 1];  // pre[s] = table entries of sequences < s
+  __shared__ int wsum[kWaves];
+  const int S = P.num_seqs;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  // Entries per sequence and their prefix sums: each thread a contiguous run
+  // of sequences, a wave scan of the runs, then the waves' totals.
+  {
+    const int per = (S + kThreads - 1) / kThreads;
+    const int s0 = threadIdx.x * per;
+    int local = 0;
+    for (int i = 0; i < per; ++i) {
+      const int s = s0 + i;
+      if (s < S) {
+        const int nb = row_span(P.seq_lens[s], P.window, P.max_blocks).nblocks;
+        pre[s + 1] = nb;
+        local += nb;
+      }
+    }
+    const int incl = wave_scan(local, lane);
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int run = incl - local;
+    for (int w = 0; w < wave; ++w) run += wsum[w];
+    if (threadIdx.x == 0) pre[0] = 0;
+    for (int i = 0; i < per; ++i) {
+      const int s = s0 + i;
+      if (s < S) {
+        run += pre[s + 1];
+        pre[s + 1] = run;
+      }
+    }
+    __syncthreads();
+  }
+  const int per_row = pre[S];
+  const int HG = P.num_kv_heads * P.qgroups;
+  const long long T = (long long)per_row * HG;
+
+  if (blockIdx.x == 0) {
+    // publish the prefix sums for the merge pass; zero the rows of empty sequences
+    for (int i = threadIdx.x; i <= S; i += kThreads) P.prefix[i] = pre[i];
+    for (int s = 0; s < S; ++s)
+      if (pre[s + 1] == pre[s])
+        for (int i = threadIdx.x; i < P.num_q_heads * D; i += kThreads)
+          ((uint16_t*)P.out)[(size_t)s * P.num_q_heads * D + i] = 0;
+  }
+
+  const long long W = (long long)gridDim.x * kWaves;
+  const long long widx = (long long)xcd_major_index(blockIdx.x, gridDim.x) * kWaves + wave;
+  const long long t_begin = widx * T / W, t_end = (widx + 1) * T / W;
+  const int n_tiles = (int)(t_end - t_begin);
+  if (n_tiles <= 0) return;
+
+  const uint16_t* pool = (const uint16_t*)P.pool_layer;
+  const uint16_t* q = (const uint16_t*)P.q;
+
+  auto row_at = [&](long long t) {  // row holding tile t
+    RowCtx r;
+    r.hg = (int)(t / per_row);
+    const int rr = (int)(t - (long long)r.hg * per_row);
+    int lo = 0, hi = S;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (pre[mid] <= rr) lo = mid; else hi = mid;
+    }
+    r.s = lo;
+    r.nb = pre[lo + 1] - pre[lo];
+    r.a = (long long)r.hg * per_row + pre[lo];
+    return r;
+  };
+  auto row_after = [&](const RowCtx& r) {  // next non-empty row of the work list
+    return row_at(r.a + r.nb < T ? r.a + r.nb : T - 1);
+  };
+  auto head0 = [&](int hg) {
+    const int kvh = hg / P.qgroups;
+    return kvh * P.group + (hg - kvh * P.qgroups) * P.heads_per_wg;
+  };
+  auto heads = [&](int hg) {
+    const int kvh = hg / P.qgroups;
+    return min(P.heads_per_wg, P.group - (hg - kvh * P.qgroups) * P.heads_per_wg);
+  };
+
+  // ---- issue side: walks the range DEPTH tiles ahead of the compute ----
+  RowCtx ir = row_at(t_begin);  // row of the next tile to issue
+  int ij = (int)(t_begin - ir.a);
+  int irow_id = 0;
+  const int32_t* irow = P.block_tables + (size_t)ir.s * P.max_blocks;
+  int ids_a = ij + lane < ir.nb ? irow[ij + lane] : 0;            // entries ij .. ij+63
+  int ids_b = ij + 64 + lane < ir.nb ? irow[ij + 64 + lane] : 0;  // entries ij+64 .. ij+127
+  int ids_base = ij;                                               // entry held by lane 0 of ids_a
+  RowCtx nr = row_after(ir);                                       // the row after, prefetched
+  int ids_n = lane < nr.nb ? P.block_tables[(size_t)nr.s * P.max_blocks + lane] : 0;
+  MfmaLanes ila = mfma_lanes<D>(P.num_kv_heads, ir.hg / P.qgroups, lane);
+  int issued = 0;
+
+  auto issue = [&](StreamTile<D>& x) {
+    if (issued >= n_tiles) {  // past the range: re-issue the last tile (a cache hit), same context
+      mfma_issue<D>(x.t, pool, ila, __builtin_amdgcn_readlane(ij - 1 - ids_base < 64 ? ids_a : ids_b,
+                                                               (ij - 1 - ids_base) & 63),
+                    P.num_blocks);
+      x.j = -1;
+      return;
+    }
+    if (ij == ir.nb) {  // row change: the prefetched row becomes current
+      ir = nr;
+      ij = 0;
+      ++irow_id;
+      irow = P.block_tables + (size_t)ir.s * P.max_blocks;
+      ids_a = ids_n;
+      ids_b = 64 + lane < ir.nb ? irow[64 + lane] : 0;
+      ids_base = 0;
+      nr = row_after(ir);
+      ids_n = lane < nr.nb ? P.block_tables[(size_t)nr.s * P.max_blocks + lane] : 0;
+      ila = mfma_lanes<D>(P.num_kv_heads, ir.hg / P.qgroups, lane);
+    } else if (ij - ids_base == 64) {  // next chunk of 64 entries: rotate, fetch the one after
+      ids_a = ids_b;
+      ids_base += 64;
+      ids_b = ids_base + 64 + lane < ir.nb ? irow[ids_base + 64 + lane] : 0;
+    }
+    mfma_issue<D>(x.t, pool, ila, __builtin_amdgcn_readlane(ids_a, ij - ids_base), P.num_blocks);
+    x.j = ij;
+    x.row_id = irow_id;
+    ++ij;
+    ++issued;
+  };
+
+  // ---- compute side ----
+  RowCtx cr = row_at(t_begin);
+  int crow_id = 0;
+  int c_h0 = head0(cr.hg), c_nh = heads(cr.hg);
+  RowSpan crs = row_span(P.seq_lens[cr.s], P.window, P.max_blocks);
+  MfmaRow<D> st;
+  st.load_q(q, (size_t)cr.s * P.num_q_heads + c_h0, c_nh, lane);
+  st.reset();
+  // queries and length of the next row, fetched ahead
+  RowCtx qn = row_after(cr);
+  int ctx_next = P.seq_lens[qn.s];
+  uint4_v q_next[D / 32];
+  {
+    const int g = lane & 15, nh_n = heads(qn.hg);
+    const uint16_t* qp = q + ((size_t)qn.s * P.num_q_heads + head0(qn.hg) + g) * D + 8 * (lane >> 4);
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) q_next[kk] = g < nh_n ? *(const uint4_v*)(qp + 32 * kk) : uint4_v{0, 0, 0, 0};
+  }
+
+  auto finish_row = [&]() {
+    const float l_tot = rows_sum(st.l_run);
+    const int q4 = lane >> 4;
+    const long long ra = cr.a, rb = cr.a + cr.nb;
+    if (ra >= t_begin && rb <= t_end) {
+      // the whole row is here: normalise and store (two bf16 per store)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int g = 4 * q4 + r4;
+        const float lg = __shfl(l_tot, g);
+        const float inv = lg > 0.f ? 1.f / lg : 0.f;
+        if (g < c_nh) {
+          unsigned* o = (unsigned*)((uint16_t*)P.out + ((size_t)cr.s * P.num_q_heads + c_h0 + g) * D);
+#pragma unroll
+          for (int m = 0; m < D / 32; ++m)
+            o[16 * m + (lane & 15)] = pack_bf16x2(st.acc[2 * m][r4] * inv, st.acc[2 * m + 1][r4] * inv);
+        }
+      }
+    } else {
+      const int slot = ra <= t_begin ? 0 : 1;
+      const size_t pbase = (size_t)(widx * 2 + slot) * P.heads_per_wg;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int g = 4 * q4 + r4;
+        if (g < c_nh) {
+          float2* o = (float2*)(P.part_o + (pbase + g) * D);
+#pragma unroll
+          for (int m = 0; m < D / 32; ++m)
+            o[16 * m + (lane & 15)] = make_float2(st.acc[2 * m][r4], st.acc[2 * m + 1][r4]);
+        }
+      }
+      if (lane < c_nh) {
+        P.part_ml[(pbase + lane) * 2 + 0] = st.m_run;
+        P.part_ml[(pbase + lane) * 2 + 1] = l_tot;
+      }
+    }
+  };
+
+  auto compute = [&](StreamTile<D>& x) {
+    if (x.row_id != crow_id) {  // first tile of the next row
+      finish_row();
+      cr = qn;
+      ++crow_id;
+      c_h0 = head0(cr.hg);
+      c_nh = heads(cr.hg);
+      crs = row_span(ctx_next, P.window, P.max_blocks);
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) st.qop[kk] = q_next[kk];
+      st.reset();
+      qn = row_after(cr);
+      ctx_next = P.seq_lens[qn.s];
+      const int g = lane & 15, nh_n = heads(qn.hg);
+      const uint16_t* qp = q + ((size_t)qn.s * P.num_q_heads + head0(qn.hg) + g) * D + 8 * (lane >> 4);
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) q_next[kk] = g < nh_n ? *(const uint4_v*)(qp + 32 * kk) : uint4_v{0, 0, 0, 0};
+    }
+    st.step(x.t, x.j, crs.start_off, crs.start_off + crs.n, crs.nblocks, P.scale_log2, lane);
+  };
+
+  StreamTile<D> buf[NBUF];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) {
+    issue(buf[d]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int k0 = 0; k0 < n_tiles; k0 += NBUF) {
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u) {
+      if (k0 + u >= n_tiles) break;
+      issue(buf[(u + DEPTH) % NBUF]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(buf[u]);
+    }
+  }
+  finish_row();
+}
+
+// Merge of the rows cut by range boundaries.  One wave per (sequence,
+// query head): the row's tiles [a, b) were covered by the waves w_first ..
+// w_last; each left its partial in slot 0 (the row held the wave's first
+// tile) or slot 1 (the row was the wave's last).  Rows inside one wave were
+// stored by the first pass.  The partials' loads go out eight at a time.
+template <int D>
+__global__ __launch_bounds__(256) void decode_stream_reduce_kernel(const DecodeParams P) {
+  const int s = blockIdx.y;
+  const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (h >= P.num_q_heads) return;
+  const int lane = threadIdx.x & 63;
+  const int S = P.num_seqs;
+  const int pre_s = P.prefix[s], nb = P.prefix[s + 1] - pre_s, per_row = P.prefix[S];
+  if (nb == 0) return;
+  const int kvh = h / P.group, g_in = h - kvh * P.group;
+  const int qg = g_in / P.heads_per_wg, hh = g_in - qg * P.heads_per_wg;
+  const int hg = kvh * P.qgroups + qg;
+  const long long T = (long long)per_row * P.num_kv_heads * P.qgroups;
+  const long long W = (long long)P.stream_wgs * kWaves;
+  const long long a = (long long)hg * per_row + pre_s, b = a + nb;
+  const long long w_first = ((a + 1) * W - 1) / T, w_last = (b * W - 1) / T;
+  if (w_first == w_last) return;
+
+  constexpr int PER = D / 64;
+  constexpr int CH = 8;
+  float M = -INFINITY, den = 0.f, num[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) num[e] = 0.f;
+  for (long long w0 = w_first; w0 <= w_last; w0 += CH) {
+    float m[CH], l[CH], v[CH][PER];
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const long long w = w0 + u <= w_last ? w0 + u : w_last;
+      const long long start = w * T / W, stop = (w + 1) * T / W;
+      const bool use = w0 + u <= w_last && start < stop;  // empty ranges leave no partial
+      const size_t pb = (size_t)(w * 2 + (start >= a ? 0 : 1)) * P.heads_per_wg + hh;
+      m[u] = use ? P.part_ml[pb * 2] : -INFINITY;
+      l[u] = use ? P.part_ml[pb * 2 + 1] : 0.f;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) v[u][e] = use ? P.part_o[pb * D + lane + 64 * e] : 0.f;
+    }
+    float Mc = M;
+#pragma unroll
+    for (int u = 0; u < CH; ++u) Mc = fmaxf(Mc, m[u]);
+    if (Mc == -INFINITY) continue;
+    const float ao = __builtin_amdgcn_exp2f(M - Mc);
+    den *= ao;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) num[e] *= ao;
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const float f = __builtin_amdgcn_exp2f(m[u] - Mc);
+      den += f * l[u];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) num[e] += f * v[u][e];
+    }
+    M = Mc;
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  uint16_t* out = (uint16_t*)P.out + ((size_t)s * P.num_q_heads + h) * D;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) out[lane + 64 * e] = bf16_rne(num[e] * inv);
+}
+
+template <int D, int DEPTH>
+hipError_t launch_sd(const DecodeParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_stream_kernel<D, DEPTH>), dim3(p.stream_wgs), dim3(kThreads), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid((p.num_q_heads + 3) / 4, p.num_seqs);
+  hipLaunchKernelGGL((decode_stream_reduce_kernel<D>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_s(const DecodeParams& p, hipStream_t stream) {
+  switch (p.depth) {
+    case 1: return launch_sd<D, 1>(p, stream);
+    case 2: return launch_sd<D, 2>(p, stream);
+    case 3: return launch_sd<D, 3>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+const void* stream_kernel_symbol(int head_dim, int depth) {
+  if (head_dim == 128)
+    return depth == 1 ? (const void*)decode_stream_kernel<128, 1>
+                      : depth == 2 ? (const void*)decode_stream_kernel<128, 2> : (const void*)decode_stream_kernel<128, 3>;
+  return depth == 1 ? (const void*)decode_stream_kernel<64, 1>
+                    : depth == 2 ? (const void*)decode_stream_kernel<64, 2> : (const void*)decode_stream_kernel<64, 3>;
+}
+
+hipError_t launch_decode_stream(const DecodeParams& p, int head_dim, hipStream_t stream) {
+  if (head_dim == 128) return launch_s<128>(p, stream);
+  if (head_dim == 64) return launch_s<64>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvp

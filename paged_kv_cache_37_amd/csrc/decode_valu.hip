@@ -56,16 +56,25 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
   __shared__ float m_s[kWaves][GT];
   __shared__ float l_s[kWaves][GT];
 
-  const int part = blockIdx.x;
-  const int kvh = blockIdx.y / P.qgroups;
-  const int qg = blockIdx.y - kvh * P.qgroups;
-  const int s = blockIdx.z;
+  // Grid (head groups, sequences, partitions): consecutive workgroups, which
+  // the dispatcher deals round robin to the eight XCDs, differ in head group
+  // first, so every XCD gets the same share of every row.
+  const int kvh = blockIdx.x / P.qgroups;
+  const int qg = blockIdx.x - kvh * P.qgroups;
+  const int s = blockIdx.y;
+  const int part = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h0 = kvh * P.group + qg * GT;
   const int nh = min(GT, P.group - qg * GT);
 
-  const RowSpan rs = row_span(P.seq_lens[s], P.window, P.max_blocks);
+  // The sequence length, this partition's table entries (lane i holds entry
+  // part * part_blocks + i, read whenever it lies inside the table row) and
+  // the queries are independent loads, issued together.
+  const int ctx = P.seq_lens[s];
+  const int32_t* row = P.block_tables + (size_t)s * P.max_blocks + part * P.part_blocks;
+  const int my_id = lane < P.part_blocks && part * P.part_blocks + lane < P.max_blocks ? row[lane] : 0;
+  const RowSpan rs = row_span(ctx, P.window, P.max_blocks);
   const int nparts = (rs.nblocks + P.part_blocks - 1) / P.part_blocks;
   T* out = (T*)P.out;
   if (rs.nblocks == 0) {
@@ -76,8 +85,6 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
   if (part >= nparts) return;
   const int jb = part * P.part_blocks;
   const int nbp = min(P.part_blocks, rs.nblocks - jb);
-  const int32_t* row = P.block_tables + (size_t)s * P.max_blocks + jb;
-  const int my_id = lane < nbp ? row[lane] : 0;
 
   const int kt_tok = lane >> 2;  // token whose K row this lane reads
   const int kc = lane & 3;
@@ -279,7 +286,7 @@ hipError_t launch_g(const DecodeParams& p, const dim3& grid, hipStream_t stream)
 
 template <typename T, int D>
 hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
-  const dim3 grid(p.num_parts, p.num_kv_heads * p.qgroups, p.num_seqs);
+  const dim3 grid(p.num_kv_heads * p.qgroups, p.num_seqs, p.num_parts);
   switch (p.heads_per_wg) {
     case 1: return launch_g<T, D, 1>(p, grid, stream);
     case 2: return launch_g<T, D, 2>(p, grid, stream);

@@ -10,6 +10,7 @@ namespace kvp {
 constexpr int kBlock = 16;      // tokens per block (the pages' default block size)
 constexpr int kWaves = 4;       // waves per decode workgroup
 constexpr int kThreads = 64 * kWaves;
+constexpr int kMaxStreamSeqs = 4096;  // sequences one streaming launch can take (LDS prefix sums)
 
 // Geometry and arguments of one decode launch, resolved on the host.
 struct DecodeParams {
@@ -20,7 +21,6 @@ struct DecodeParams {
   const int32_t* seq_lens;      // [S]
   float* part_o;                // [S][Hq][num_parts][D]      (split only)
   float* part_ml;               // [S][Hq][num_parts][2]      (split only)
-  int* counters;                // [S][Hq] arrival counts, zero between calls (split only)
   int32_t max_blocks;           // row stride of block_tables
   int32_t window;               // 0 = full context
   int32_t num_seqs;
@@ -34,6 +34,8 @@ struct DecodeParams {
   int32_t num_parts;            // partitions of the longest possible row
   float scale_log2;             // scale * log2(e): scores are kept in base 2
   int32_t depth;                // blocks of K/V a wave keeps in flight ahead of the one it computes
+  int32_t* prefix;              // [S + 1] table entries before each sequence   (streaming only)
+  int32_t stream_wgs;           // persistent workgroups of a streaming launch   (streaming only)
 };
 
 // Span of one block-table row: leading slots of the first block that are
@@ -64,5 +66,8 @@ hipError_t launch_cache_write(void* pool_layer, int dtype, int num_blocks, int n
                               const int32_t* slots, int num_tokens, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_decode_reduce(const DecodeParams& p, int dtype, int head_dim, hipStream_t stream);
+hipError_t launch_decode_stream(const DecodeParams& p, int head_dim, hipStream_t stream);
+const void* stream_kernel_symbol(int head_dim, int depth);
 
 }  // namespace kvp

@@ -133,8 +133,41 @@ int32_t cache_write(kvp_pool pool, int32_t layer, const void* k_new, const void*
   return ok();
 }
 
+static int32_t decode_depth(int32_t mfma) {
+  // Blocks of K/V each wave keeps in flight ahead of the one it computes.
+  static const int env = [] {
+    const char* e = getenv("KVP_DECODE_DEPTH");
+    return e ? atoi(e) : 0;
+  }();
+  if (env >= 1 && env <= (mfma ? 3 : 2)) return env;
+  return mfma ? 2 : 1;
+}
+
+// Resident workgroups of the streaming kernel on the current device:
+// compute units x workgroups per compute unit at the kernel's occupancy.
+// 0 if there is no device to ask.
+static int32_t stream_workgroups(int32_t head_dim, int32_t depth) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  static thread_local int cached_dev = -1, cached_d = 0, cached_depth = 0, cached_wgs = 0;
+  if (dev == cached_dev && head_dim == cached_d && depth == cached_depth) return cached_wgs;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kvp::stream_kernel_symbol(head_dim, depth), kvp::kThreads,
+                                                   0) != hipSuccess ||
+      per_cu <= 0)
+    return 0;
+  cached_dev = dev;
+  cached_d = head_dim;
+  cached_depth = depth;
+  cached_wgs = cus * per_cu;
+  return cached_wgs;
+}
+
+enum { PATH_VALU = 0, PATH_MFMA = 1, PATH_STREAM = 2 };
+
 static int32_t plan(kvp_pool pool, int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks, int32_t partition_tokens,
-                    int32_t variant, kvp::DecodeParams* p, int32_t* use_mfma) {
+                    int32_t variant, kvp::DecodeParams* p, int32_t* path) {
   const kvp_pool_desc& d = pool->desc;
   if (num_seqs < 0 || num_seqs > 65535) return fail(KVP_ERR_INVALID_ARG, "num_seqs must be in [0, 65535]");
   if (num_q_heads < 1 || num_q_heads % d.num_kv_heads != 0)
@@ -145,16 +178,31 @@ static int32_t plan(kvp_pool pool, int32_t num_seqs, int32_t num_q_heads, int32_
       (partition_tokens % kvp::kBlock != 0 || partition_tokens < kvp::kBlock || partition_tokens > 64 * kvp::kBlock))
     return fail(KVP_ERR_INVALID_ARG, "partition_tokens must be 0 or a multiple of 16 in [16, 1024]");
   const int32_t G = num_q_heads / d.num_kv_heads;
-  int32_t mfma = 0;
-  if (variant == KVP_VARIANT_AUTO)
-    mfma = d.dtype == KVP_BF16;
-  else if (variant == KVP_VARIANT_MFMA) {
-    if (d.dtype != KVP_BF16) return fail(KVP_ERR_UNSUPPORTED, "the MFMA variant needs a bf16 pool");
-    mfma = 1;
-  } else if (variant != KVP_VARIANT_VALU)
-    return fail(KVP_ERR_INVALID_ARG, "unknown variant %d", variant);
+  const bool bf16 = d.dtype == KVP_BF16;
+  int32_t pth;
+  switch (variant) {
+    case KVP_VARIANT_AUTO:
+      pth = !bf16 ? PATH_VALU
+                  : (partition_tokens == 0 && num_seqs <= kvp::kMaxStreamSeqs &&
+                     stream_workgroups(d.head_dim, decode_depth(1)) > 0)
+                        ? PATH_STREAM
+                        : PATH_MFMA;
+      break;
+    case KVP_VARIANT_VALU: pth = PATH_VALU; break;
+    case KVP_VARIANT_MFMA:
+      if (!bf16) return fail(KVP_ERR_UNSUPPORTED, "the MFMA variant needs a bf16 pool");
+      pth = PATH_MFMA;
+      break;
+    case KVP_VARIANT_STREAM:
+      if (!bf16) return fail(KVP_ERR_UNSUPPORTED, "the STREAM variant needs a bf16 pool");
+      if (num_seqs > kvp::kMaxStreamSeqs)
+        return fail(KVP_ERR_UNSUPPORTED, "the STREAM variant takes at most %d sequences", kvp::kMaxStreamSeqs);
+      pth = PATH_STREAM;
+      break;
+    default: return fail(KVP_ERR_INVALID_ARG, "unknown variant %d", variant);
+  }
   int32_t hpw;
-  if (mfma) {
+  if (pth != PATH_VALU) {
     hpw = G < 16 ? G : 16;
   } else {
     hpw = 1;
@@ -176,45 +224,54 @@ static int32_t plan(kvp_pool pool, int32_t num_seqs, int32_t num_q_heads, int32_
   p->qgroups = qgroups;
   p->part_blocks = pb;
   p->num_parts = (max_blocks + pb - 1) / pb;
-  *use_mfma = mfma;
+  p->depth = decode_depth(pth != PATH_VALU);
+  if (pth == PATH_STREAM) {
+    p->stream_wgs = stream_workgroups(d.head_dim, p->depth);
+    if (p->stream_wgs <= 0) return fail(KVP_ERR_HIP, "cannot size the streaming grid (no device?)");
+  }
+  *path = pth;
   return KVP_OK;
 }
 
-// Workspace of a split launch: unnormalised partial outputs, their (max,
-// sum) pairs, and one arrival counter per (sequence, query head).  The
-// counters must be zero before the first call; every call leaves them zero.
-static size_t workspace_layout(const kvp::DecodeParams& p, int32_t head_dim, size_t* ml_off, size_t* ctr_off) {
+static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Workspace of the partitioned kernels: unnormalised partial outputs and
+// their (max, sum) pairs per (sequence, query head, partition).
+static size_t grid_workspace(const kvp::DecodeParams& p, int32_t head_dim, size_t* ml_off) {
   if (p.num_parts <= 1) {
-    *ml_off = *ctr_off = 0;
+    *ml_off = 0;
     return 0;
   }
   const size_t rows = (size_t)p.num_seqs * p.num_q_heads * p.num_parts;
-  const size_t o_bytes = (rows * head_dim * sizeof(float) + 255) & ~(size_t)255;
-  const size_t ml_bytes = (rows * 2 * sizeof(float) + 255) & ~(size_t)255;
+  const size_t o_bytes = align256(rows * head_dim * sizeof(float));
   *ml_off = o_bytes;
-  *ctr_off = o_bytes + ml_bytes;
-  return o_bytes + ml_bytes + (size_t)p.num_seqs * p.num_q_heads * sizeof(int);
+  return o_bytes + rows * 2 * sizeof(float);
 }
 
-static int32_t decode_depth(int32_t mfma) {
-  // Blocks of K/V each wave keeps in flight ahead of the one it computes.
-  static const int env = [] {
-    const char* e = getenv("KVP_DECODE_DEPTH");
-    return e ? atoi(e) : 0;
-  }();
-  if (env >= 1 && env <= (mfma ? 3 : 2)) return env;
-  return mfma ? 2 : 1;
+// Workspace of the streaming kernel: prefix sums, then two partial slots per
+// wave for up to heads_per_wg heads: (max, sum) pairs and outputs.
+static size_t stream_workspace(const kvp::DecodeParams& p, int32_t head_dim, size_t* ml_off, size_t* o_off) {
+  const size_t slots = (size_t)p.stream_wgs * kvp::kWaves * 2 * p.heads_per_wg;
+  *ml_off = align256((size_t)(p.num_seqs + 1) * sizeof(int32_t));
+  *o_off = *ml_off + align256(slots * 2 * sizeof(float));
+  return *o_off + slots * head_dim * sizeof(float);
 }
 
 size_t paged_decode_workspace_bytes(kvp_pool pool, int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
                                     int32_t partition_tokens) {
   if (!pool) return 0;
-  kvp::DecodeParams p;
-  int32_t mfma;
-  if (plan(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, KVP_VARIANT_AUTO, &p, &mfma) != KVP_OK)
-    return 0;
-  size_t ml_off, ctr_off;
-  return workspace_layout(p, pool->desc.head_dim, &ml_off, &ctr_off);
+  // enough for every variant that could run with these sizes
+  size_t need = 0, a, b;
+  for (int32_t v : {KVP_VARIANT_VALU, KVP_VARIANT_MFMA, KVP_VARIANT_STREAM}) {
+    kvp::DecodeParams p;
+    int32_t path;
+    if (plan(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, v, &p, &path) != KVP_OK) continue;
+    const size_t n = path == PATH_STREAM ? stream_workspace(p, pool->desc.head_dim, &a, &b)
+                                         : grid_workspace(p, pool->desc.head_dim, &a);
+    if (n > need) need = n;
+  }
+  g_err[0] = '\0';
+  return need;
 }
 
 int32_t paged_decode_attention(kvp_pool pool, const kvp_decode_args* a, hipStream_t stream) {
@@ -224,24 +281,31 @@ int32_t paged_decode_attention(kvp_pool pool, const kvp_decode_args* a, hipStrea
   if (a->sliding_window < 0) return fail(KVP_ERR_INVALID_ARG, "sliding_window < 0");
   if (!std::isfinite(a->scale)) return fail(KVP_ERR_INVALID_ARG, "scale is not finite");
   kvp::DecodeParams p;
-  int32_t mfma = 0;
-  int32_t st = plan(pool, a->num_seqs, a->num_q_heads, a->max_blocks_per_seq, a->partition_tokens, a->variant, &p, &mfma);
+  int32_t path = PATH_VALU;
+  int32_t st = plan(pool, a->num_seqs, a->num_q_heads, a->max_blocks_per_seq, a->partition_tokens, a->variant, &p, &path);
   if (st != KVP_OK) return st;
   if (a->num_seqs == 0) return ok();
   if (!a->q || !a->out || !a->block_tables || !a->seq_lens)
     return fail(KVP_ERR_INVALID_ARG, "NULL q, out, block_tables or seq_lens");
   if (!aligned(a->q, 16) || !aligned(a->out, 16) || !aligned(a->block_tables, 4) || !aligned(a->seq_lens, 4))
     return fail(KVP_ERR_INVALID_ARG, "q/out must be 16-byte aligned, tables and lengths 4-byte aligned");
-  size_t ml_off = 0, ctr_off = 0;
-  const size_t ws = workspace_layout(p, d.head_dim, &ml_off, &ctr_off);
+  size_t ml_off = 0, o_off = 0;
+  const size_t ws = path == PATH_STREAM ? stream_workspace(p, d.head_dim, &ml_off, &o_off)
+                                        : grid_workspace(p, d.head_dim, &ml_off);
   if (ws > 0) {
     if (!a->workspace || a->workspace_bytes < ws)
       return fail(KVP_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes needed (%zu given)", ws,
                   a->workspace ? a->workspace_bytes : (size_t)0);
     if (!aligned(a->workspace, 256)) return fail(KVP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-    p.part_o = (float*)a->workspace;
-    p.part_ml = (float*)((char*)a->workspace + ml_off);
-    p.counters = (int*)((char*)a->workspace + ctr_off);
+    char* w = (char*)a->workspace;
+    if (path == PATH_STREAM) {
+      p.prefix = (int32_t*)w;
+      p.part_ml = (float*)(w + ml_off);
+      p.part_o = (float*)(w + o_off);
+    } else {
+      p.part_o = (float*)w;
+      p.part_ml = (float*)(w + ml_off);
+    }
   }
   p.pool_layer = (const char*)pool->base + (size_t)a->layer * layer_elems(d) * elt_bytes(d.dtype);
   p.q = a->q;
@@ -250,10 +314,19 @@ int32_t paged_decode_attention(kvp_pool pool, const kvp_decode_args* a, hipStrea
   p.seq_lens = a->seq_lens;
   p.window = a->sliding_window;
   p.scale_log2 = a->scale * 1.4426950408889634f;
-  p.depth = decode_depth(mfma);
-  const hipError_t e = mfma ? kvp::launch_decode_mfma(p, d.head_dim, stream)
-                      : kvp::launch_decode_valu(p, d.dtype, d.head_dim, stream);
+  hipError_t e;
+  if (path == PATH_STREAM) {
+    e = kvp::launch_decode_stream(p, d.head_dim, stream);
+    if (e != hipSuccess) return fail(KVP_ERR_HIP, "stream decode launch: %s", hipGetErrorString(e));
+    return ok();
+  }
+  e = path == PATH_MFMA ? kvp::launch_decode_mfma(p, d.head_dim, stream)
+                        : kvp::launch_decode_valu(p, d.dtype, d.head_dim, stream);
   if (e != hipSuccess) return fail(KVP_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  if (p.num_parts > 1) {
+    e = kvp::launch_decode_reduce(p, d.dtype, d.head_dim, stream);
+    if (e != hipSuccess) return fail(KVP_ERR_HIP, "reduce launch: %s", hipGetErrorString(e));
+  }
   return ok();
 }
 

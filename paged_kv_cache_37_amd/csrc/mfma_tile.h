@@ -1,0 +1,168 @@
+// One wave's paged-attention step over a 16-token block on the CDNA4 matrix
+// cores (bf16 pools), shared by the partitioned and the streaming kernels.
+//
+// Operand layouts (16x16 MFMA, lane l, row group q = l / 16):
+//   A of 16x16x32 : A[l % 16][8q .. 8q+7]      -> K[token l%16][32kk + 8q ..]
+//   B of 16x16x32 : B[8q .. 8q+7][l % 16]      -> Q[head l%16][32kk + 8q ..]
+//   C             : C[4q + r][l % 16], r<4     -> S[token 4q+r][head l%16]
+//   A of 16x16x16 : A[l % 16][4q .. 4q+3]      -> P[head l%16][token 4q..4q+3]
+//                   (exactly the C layout above, no shuffle needed)
+//   B of 16x16x16 : B[4q .. 4q+3][l % 16]      -> V[token 4q..4q+3][dim]
+// The V tile is stored as [4][D][4] (four slots of one dimension adjacent),
+// so one 16-byte load gives a lane two dimensions x four tokens: the B
+// operands of two PV MFMAs (column j of MFMA 2m+e is dimension 32m+2j+e).
+// The accumulator of PV MFMA n, register r, lane l is therefore
+//   O[head 4q + r][dim 32(n/2) + 2(l%16) + n%2].
+#pragma once
+
+#include "decode_common.h"
+
+namespace kvp {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_v;
+typedef __attribute__((ext_vector_type(4))) short short4_v;
+typedef __attribute__((ext_vector_type(8))) short short8_v;
+typedef __attribute__((ext_vector_type(4))) float float4_v;
+typedef __attribute__((ext_vector_type(4))) unsigned uint4_v;
+typedef __attribute__((ext_vector_type(2))) unsigned uint2_v;
+
+// A block's K and V operands for one wave.
+template <int D>
+struct MfmaTiles {
+  uint4_v k[D / 32];  // token l%16, dims 32kk + 8q .. +7
+  uint4_v v[D / 32];  // tokens 4q..4q+3 of dims 32m + 2(l%16), +1
+  bool bad;           // block id outside the pool: contributes nothing
+};
+
+// Per-wave addressing of one KV head's tiles inside a block.
+struct MfmaLanes {
+  size_t blk_stride;  // elements per physical block (all heads, K and V)
+  size_t k_off;       // this head's K tile inside a block
+  size_t v_rel;       // V tile = K tile + v_rel
+  int k_lane;         // this lane's K element offset (+ 32 kk)
+  int v_lane;         // this lane's V element offset (+ 128 m)
+};
+
+template <int D>
+__device__ __forceinline__ MfmaLanes mfma_lanes(int num_kv_heads, int kvh, int lane) {
+  const size_t tile = (size_t)16 * D;
+  MfmaLanes a;
+  a.blk_stride = 2 * (size_t)num_kv_heads * tile;
+  a.k_off = (size_t)kvh * tile;
+  a.v_rel = (size_t)num_kv_heads * tile;
+  a.k_lane = (lane & 15) * D + 8 * (lane >> 4);
+  a.v_lane = ((lane >> 4) * D + 2 * (lane & 15)) * 4;
+  return a;
+}
+
+// Issue the loads of physical block `id` (checked against the pool size).
+template <int D>
+__device__ __forceinline__ void mfma_issue(MfmaTiles<D>& t, const uint16_t* __restrict__ pool, const MfmaLanes& a,
+                                           int id, int num_blocks) {
+  t.bad = (unsigned)id >= (unsigned)num_blocks;
+  if (t.bad) id = 0;
+  const uint16_t* kt = pool + (size_t)id * a.blk_stride + a.k_off;
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) t.k[kk] = *(const uint4_v*)(kt + a.k_lane + 32 * kk);
+#pragma unroll
+  for (int m = 0; m < D / 32; ++m) t.v[m] = *(const uint4_v*)(kt + a.v_rel + a.v_lane + 128 * m);
+}
+
+// Running softmax state of one wave for up to 16 query heads of a group.
+template <int D>
+struct MfmaRow {
+  uint4_v qop[D / 32];  // Q as the B operand: column = head l%16
+  float m_run;          // running max of head l%16 (base 2), uniform over row groups
+  float l_run;          // this lane's share of head l%16's weight sum
+  float4_v acc[D / 16];
+
+  __device__ __forceinline__ void reset() {
+    m_run = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n) acc[n] = float4_v{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Queries of heads h0 .. h0+nh-1 of sequence s (zero for the padding columns).
+  __device__ __forceinline__ void load_q(const uint16_t* __restrict__ q, size_t row_base, int nh, int lane) {
+    const int g = lane & 15;
+    const uint16_t* qp = q + (row_base + g) * D + 8 * (lane >> 4);
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) qop[kk] = g < nh ? *(const uint4_v*)(qp + 32 * kk) : uint4_v{0, 0, 0, 0};
+  }
+
+  // One block: table entry J of a row whose attended table slots are
+  // [so, send) and which uses `nblocks` entries.
+  __device__ __forceinline__ void step(MfmaTiles<D>& t, int J, int so, int send, int nblocks, float scale_log2,
+                                       int lane) {
+    const int q4 = lane >> 4;
+    float4_v sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, t.k[kk]),
+                                                     __builtin_bit_cast(bf16x8_v, qop[kk]), sacc, 0, 0, 0);
+    float sv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sv[r] = sacc[r] * scale_log2;
+    const bool edge = t.bad || (J == 0 && so > 0) || (J == nblocks - 1 && (send & 15) != 0);
+    if (edge) {
+      unsigned vm[2];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int u0 = J * 16 + 4 * q4 + 2 * half;
+        const bool a = !t.bad && u0 >= so && u0 < send;
+        const bool b = !t.bad && u0 + 1 >= so && u0 + 1 < send;
+        if (!a) sv[2 * half] = -INFINITY;
+        if (!b) sv[2 * half + 1] = -INFINITY;
+        vm[half] = (a ? 0xffffu : 0u) | (b ? 0xffff0000u : 0u);
+      }
+#pragma unroll
+      for (int m = 0; m < D / 32; ++m) {
+        t.v[m].x &= vm[0];
+        t.v[m].y &= vm[1];
+        t.v[m].z &= vm[0];
+        t.v[m].w &= vm[1];
+      }
+    }
+    // The running max is raised only when a score exceeds it by more than
+    // 2^kRescaleSlack; then the accumulators are rescaled.
+    const float lmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    if (__any(lmax > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, rows_max(lmax));
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float ar = __shfl(alpha, 4 * q4 + r);  // rows of O here are heads 4*q4 + r
+#pragma unroll
+        for (int n = 0; n < D / 16; ++n) acc[n][r] *= ar;
+      }
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sv[r] - m_use);
+    l_run += (p[0] + p[1]) + (p[2] + p[3]);
+    // P = P_hi + P_lo, both bf16: the two PV products together carry the
+    // weights to ~2^-17 relative instead of bf16's 2^-9.
+    const unsigned h01 = pack_bf16x2(p[0], p[1]), h23 = pack_bf16x2(p[2], p[3]);
+    const unsigned l01 = pack_bf16x2(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
+    const unsigned l23 = pack_bf16x2(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
+    const short4_v pa_hi = __builtin_bit_cast(short4_v, uint2_v{h01, h23});
+    const short4_v pa_lo = __builtin_bit_cast(short4_v, uint2_v{l01, l23});
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) {
+      const short8_v vv = __builtin_bit_cast(short8_v, t.v[m]);
+      const short4_v v0 = __builtin_shufflevector(vv, vv, 0, 1, 2, 3);
+      const short4_v v1 = __builtin_shufflevector(vv, vv, 4, 5, 6, 7);
+      acc[2 * m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa_hi, v0, acc[2 * m], 0, 0, 0);
+      acc[2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa_hi, v1, acc[2 * m + 1], 0, 0, 0);
+      acc[2 * m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa_lo, v0, acc[2 * m], 0, 0, 0);
+      acc[2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa_lo, v1, acc[2 * m + 1], 0, 0, 0);
+    }
+  }
+};
+
+}  // namespace kvp

@@ -16,7 +16,8 @@ from ._lib import DecodeArgs, KVPoolError, PoolDesc, check, lib
 BLOCK_SIZE = 16
 
 _DTYPES = {torch.float32: _lib.KVP_F32, torch.bfloat16: _lib.KVP_BF16}
-_VARIANTS = {"auto": _lib.KVP_VARIANT_AUTO, "valu": _lib.KVP_VARIANT_VALU, "mfma": _lib.KVP_VARIANT_MFMA}
+_VARIANTS = {"auto": _lib.KVP_VARIANT_AUTO, "valu": _lib.KVP_VARIANT_VALU, "mfma": _lib.KVP_VARIANT_MFMA,
+             "stream": _lib.KVP_VARIANT_STREAM}
 
 
 def _stream(device: torch.device, stream: Optional[torch.cuda.Stream]) -> ctypes.c_void_p:
@@ -136,10 +137,10 @@ def paged_decode_workspace_bytes(pool: KVPool, num_seqs: int, num_q_heads: int, 
 
 def make_workspace(pool: KVPool, num_seqs: int, num_q_heads: int, max_blocks_per_seq: int,
                    partition_tokens: int = 0) -> Optional[torch.Tensor]:
-    """Zero-filled workspace (its arrival counters must start at zero; every
-    call leaves them zero).  Calls that share one workspace must not overlap."""
+    """Workspace for split launches of these sizes (None when a single pass
+    suffices).  Calls that share one workspace must not overlap."""
     n = paged_decode_workspace_bytes(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens)
-    return torch.zeros(n, dtype=torch.uint8, device=pool.device) if n else None
+    return torch.empty(n, dtype=torch.uint8, device=pool.device) if n else None
 
 
 def paged_decode_attention(pool: KVPool, layer: int, q: torch.Tensor, block_tables: torch.Tensor,

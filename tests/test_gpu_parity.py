@@ -147,9 +147,10 @@ def test_prefill_write_fills_pool_like_loader(gpu, D, dtype, window):
 
 @pytest.mark.parametrize("config,variant,part", [
     (1, "valu", 0), (1, "valu", 16), (1, "auto", 32),
-    (2, "mfma", 0), (2, "mfma", 512), (2, "mfma", 256), (2, "mfma", 1024), (2, "valu", 0), (2, "valu", 512),
-    (4, "mfma", 0), (4, "valu", 0),
-    (5, "mfma", 512), (5, "mfma", 0), (5, "valu", 512),
+    (2, "auto", 0), (2, "stream", 0), (2, "mfma", 0), (2, "mfma", 512), (2, "mfma", 256), (2, "mfma", 1024),
+    (2, "valu", 0), (2, "valu", 512),
+    (4, "stream", 0), (4, "mfma", 0), (4, "valu", 0),
+    (5, "stream", 0), (5, "mfma", 512), (5, "mfma", 0), (5, "valu", 512),
 ])
 def test_decode_parity(gpu, config, variant, part):
     w = workload(config)
@@ -169,7 +170,7 @@ def _ref_cached(config):
     return _REF[config]
 
 
-@pytest.mark.parametrize("variant,part", [("mfma", 0), ("mfma", 512), ("valu", 0)])
+@pytest.mark.parametrize("variant,part", [("stream", 0), ("mfma", 0), ("mfma", 512), ("valu", 0)])
 def test_decode_parity_config3_sampled(gpu, variant, part):
     """The 70B-shaped layer at full size; the oracle checks 6 sequences."""
     w = workload(3)
@@ -205,7 +206,7 @@ def test_workspace_too_small_is_rejected(gpu):
 # probes
 
 
-@pytest.mark.parametrize("variant", ["mfma", "valu"])
+@pytest.mark.parametrize("variant", ["stream", "mfma", "valu"])
 @pytest.mark.parametrize("window", [0, 40])
 def test_needle_is_returned_exactly(gpu, variant, window):
     """q_h = 32 e_d and K[t*] = 32 e_d for the group's KV head make one key
@@ -245,7 +246,7 @@ def test_needle_is_returned_exactly(gpu, variant, window):
             assert got[s, h].tobytes() == pool[0, blk, 1, pstar % 16, h // G].tobytes(), (s, h, pstar)
 
 
-@pytest.mark.parametrize("variant", ["mfma", "valu"])
+@pytest.mark.parametrize("variant", ["stream", "mfma", "valu"])
 def test_masked_slots_never_count(gpu, variant):
     """Needles planted where no position maps (after the last token, before
     a window's first position) leave the output bit-identical."""
@@ -270,7 +271,7 @@ def test_masked_slots_never_count(gpu, variant):
     assert torch_to_bits(dev2.attend(variant=variant)).tobytes() == base.tobytes()
 
 
-@pytest.mark.parametrize("variant", ["mfma", "valu"])
+@pytest.mark.parametrize("variant", ["stream", "mfma", "valu"])
 def test_constant_values(gpu, variant):
     w = small(91, [1, 16, 17, 300, 1000], window=0)
     pool = w.pool.copy()
@@ -280,7 +281,7 @@ def test_constant_values(gpu, variant):
     assert torch.all(out.float() == 1.0)
 
 
-@pytest.mark.parametrize("variant", ["mfma", "valu"])
+@pytest.mark.parametrize("variant", ["stream", "mfma", "valu"])
 def test_relabelling_is_bitwise_invisible(gpu, variant):
     w = small(92, [3, 16, 45, 200, 777], Hq=16, Hkv=4)
     a = torch_to_bits(Dev(w).attend(variant=variant, partition_tokens=128))
@@ -292,7 +293,7 @@ def test_relabelling_is_bitwise_invisible(gpu, variant):
     assert a.tobytes() == b.tobytes()
 
 
-@pytest.mark.parametrize("variant", ["mfma", "valu"])
+@pytest.mark.parametrize("variant", ["stream", "mfma", "valu"])
 def test_shared_prefix_equals_private_copies(gpu, variant):
     w = W.config4(seed=4, num_seqs=12)
     a = torch_to_bits(Dev(w).attend(variant=variant))
@@ -315,19 +316,26 @@ def test_shared_prefix_equals_private_copies(gpu, variant):
 @pytest.mark.parametrize("variant", ["mfma", "valu"])
 def test_split_matches_single_pass(gpu, variant):
     """Rows of up to 1024 tokens: one partition versus 512/256/128-token
-    partitions agree to within one bf16 ulp (of the larger of the two)."""
+    partitions.  Both round the same fp32-accumulated result to bf16, so
+    they agree to one bf16 ulp plus the fp32 accumulation-order noise,
+    bounded by 1e-5 of the row's rms (near-zero outputs of a row come from
+    cancellation, where an ulp of the output means nothing)."""
     from gpu_helpers import ulp_bf16
 
     w = small(93, [1, 100, 511, 512, 513, 1000, 1024], Hq=16, Hkv=2)
     dev = Dev(w)
     single = to_f64(dev.attend(variant=variant, partition_tokens=1024))
+    rms = np.sqrt(np.mean(single ** 2, axis=-1, keepdims=True))
     for part in (512, 256, 128):
         split = to_f64(dev.attend(variant=variant, partition_tokens=part))
-        ulp = np.maximum(ulp_bf16(single), ulp_bf16(split))
-        assert np.all(np.abs(split - single) <= ulp), part
+        bound = np.maximum(ulp_bf16(single), ulp_bf16(split)) + 1e-5 * rms
+        ratio = np.abs(split - single) / bound
+        worst = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+        say("split", variant, part, "max/bound", float(ratio.max()), "at", worst, single[worst], split[worst])
+        assert np.all(ratio <= 1.0), part
 
 
-@pytest.mark.parametrize("variant", ["mfma", "valu"])
+@pytest.mark.parametrize("variant", ["stream", "mfma", "valu"])
 def test_gqa_heads_with_equal_queries_agree(gpu, variant):
     w = small(94, [9, 64, 130], Hq=16, Hkv=2)
     q = w.q.copy()
@@ -359,7 +367,7 @@ def test_write_then_attend(gpu):
 # edge cases and shape sweeps
 
 
-@pytest.mark.parametrize("variant", ["mfma", "valu"])
+@pytest.mark.parametrize("variant", ["stream", "mfma", "valu"])
 def test_empty_and_tiny_sequences(gpu, variant):
     w = small(95, [0, 1, 0, 2, 16, 0], Hq=8, Hkv=2)
     out = Dev(w).attend(variant=variant)
@@ -368,7 +376,7 @@ def test_empty_and_tiny_sequences(gpu, variant):
     assert torch.all(out[[0, 2, 5]].float() == 0)
 
 
-@pytest.mark.parametrize("variant", ["mfma", "valu"])
+@pytest.mark.parametrize("variant", ["stream", "mfma", "valu"])
 @pytest.mark.parametrize("window", [0, 33])
 def test_length_sweep_around_block_edges(gpu, variant, window):
     ctx = list(range(1, 66)) + [255, 256, 257, 511, 512, 513]
@@ -377,7 +385,7 @@ def test_length_sweep_around_block_edges(gpu, variant, window):
     compare(out, reference(w), "bf16", f"lengths/{variant}/w{window}")
 
 
-@pytest.mark.parametrize("variant", ["mfma", "valu"])
+@pytest.mark.parametrize("variant", ["stream", "mfma", "valu"])
 def test_window_offsets_sweep(gpu, variant):
     """Windowed rows whose first attended slot sits at every offset 0..15."""
     W_ = 64
@@ -387,7 +395,7 @@ def test_window_offsets_sweep(gpu, variant):
     compare(out, reference(w), "bf16", f"window-offsets/{variant}")
 
 
-@pytest.mark.parametrize("variant", ["mfma", "valu"])
+@pytest.mark.parametrize("variant", ["stream", "mfma", "valu"])
 @pytest.mark.parametrize("Hq,Hkv", [(4, 4), (4, 2), (8, 2), (16, 2), (32, 2), (24, 8), (64, 2)])
 @pytest.mark.parametrize("D", [64, 128])
 def test_head_group_and_dim_sweep(gpu, variant, Hq, Hkv, D):
@@ -411,3 +419,15 @@ def test_multi_layer_pool(gpu):
     for layer in (0, 2):
         out = dev.attend(layer=layer)
         compare(out, reference(w, layer=layer), "bf16", f"layer{layer}")
+
+
+def test_workspace_is_reusable(gpu):
+    """One workspace serves call after call and both variants."""
+    w = small(35, [100, 700, 1000, 33], Hq=8, Hkv=2)
+    dev = Dev(w)
+    ws = dev.ops.make_workspace(dev.pool, w.num_seqs, w.num_q_heads, w.block_tables.shape[1], 128)
+    ws.fill_(0xFF)  # contents need no initialisation
+    ref = reference(w)
+    for variant in ("mfma", "valu", "stream", "mfma"):
+        out = dev.attend(variant=variant, partition_tokens=128 if variant != "stream" else 0, workspace=ws)
+        compare(out, ref, "bf16", f"reuse/{variant}")
