@@ -44,6 +44,14 @@ __device__ __forceinline__ int wave_scan(int v, int lane) {
   return v;
 }
 
+// floor(num / den) for 0 <= num < 2^53, 0 < den: the double quotient of two
+// exactly represented integers is either that integer or at least 1/den
+// away from it, far more than its rounding error, so the floor is exact
+// (and avoids the GPU's software 64-bit integer division).
+__device__ __forceinline__ long long floor_div(long long num, long long den) {
+  return (long long)__builtin_floor((double)num / (double)den);
+}
+
 // A row of the work list and what the waves need to know about it.
 struct RowCtx {
   int hg, s;      // head group, sequence
@@ -111,8 +119,9 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
   }
 
   const long long W = (long long)gridDim.x * kWaves;
-  const long long widx = (long long)xcd_major_index(blockIdx.x, gridDim.x) * kWaves + wave;
-  const long long t_begin = widx * T / W, t_end = (widx + 1) * T / W;
+  const long long widx =
+      (long long)(P.stream_order ? (int)blockIdx.x : xcd_major_index(blockIdx.x, gridDim.x)) * kWaves + wave;
+  const long long t_begin = floor_div(widx * T, W), t_end = floor_div((widx + 1) * T, W);
   const int n_tiles = (int)(t_end - t_begin);
   if (n_tiles <= 0) return;
 
@@ -305,7 +314,7 @@ __global__ __launch_bounds__(256) void decode_stream_reduce_kernel(const DecodeP
   const long long T = (long long)per_row * P.num_kv_heads * P.qgroups;
   const long long W = (long long)P.stream_wgs * kWaves;
   const long long a = (long long)hg * per_row + pre_s, b = a + nb;
-  const long long w_first = ((a + 1) * W - 1) / T, w_last = (b * W - 1) / T;
+  const long long w_first = floor_div((a + 1) * W - 1, T), w_last = floor_div(b * W - 1, T);
   if (w_first == w_last) return;
 
   constexpr int PER = D / 64;
@@ -318,7 +327,7 @@ __global__ __launch_bounds__(256) void decode_stream_reduce_kernel(const DecodeP
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
       const long long w = w0 + u <= w_last ? w0 + u : w_last;
-      const long long start = w * T / W, stop = (w + 1) * T / W;
+      const long long start = floor_div(w * T, W), stop = floor_div((w + 1) * T, W);
       const bool use = w0 + u <= w_last && start < stop;  // empty ranges leave no partial
       const size_t pb = (size_t)(w * 2 + (start >= a ? 0 : 1)) * P.heads_per_wg + hh;
       m[u] = use ? P.part_ml[pb * 2] : -INFINITY;

@@ -226,6 +226,11 @@ static int32_t plan(kvp_pool pool, int32_t num_seqs, int32_t num_q_heads, int32_
   p->num_parts = (max_blocks + pb - 1) / pb;
   p->depth = decode_depth(pth != PATH_VALU);
   if (pth == PATH_STREAM) {
+    static const int order = [] {
+      const char* e = getenv("KVP_STREAM_ORDER");
+      return e ? atoi(e) : 0;
+    }();
+    p->stream_order = order == 1;
     p->stream_wgs = stream_workgroups(d.head_dim, p->depth);
     if (p->stream_wgs <= 0) return fail(KVP_ERR_HIP, "cannot size the streaming grid (no device?)");
   }
