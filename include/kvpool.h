@@ -206,8 +206,9 @@ size_t paged_decode_workspace_bytes(kvp_pool pool, int32_t num_seqs, int32_t num
  *   bytes, contents need no initialisation) and a second kernel on the same
  *   stream merges them.  Calls that share one workspace must not overlap.
  *
- *   Environment: KVP_DECODE_DEPTH (1..3) overrides how many blocks each
- *   wave keeps in flight ahead of the one it computes (a tuning knob).
+ *   Environment: KVP_DECODE_DEPTH (1..3 for the MFMA variant, 1..2 for
+ *   the others) overrides how many blocks each wave keeps in flight ahead
+ *   of the one it computes (a tuning knob, read once per process).
  *
  *   Errors: KVP_ERR_INVALID_ARG (nulls, layer, heads, partition size),
  *   KVP_ERR_UNSUPPORTED (variant/dtype/head group combination),

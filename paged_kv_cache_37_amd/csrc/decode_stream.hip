@@ -119,8 +119,7 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
   }
 
   const long long W = (long long)gridDim.x * kWaves;
-  const long long widx =
-      (long long)(P.stream_order ? (int)blockIdx.x : xcd_major_index(blockIdx.x, gridDim.x)) * kWaves + wave;
+  const long long widx = (long long)xcd_major_index(blockIdx.x, gridDim.x) * kWaves + wave;
   const long long t_begin = floor_div(widx * T, W), t_end = floor_div((widx + 1) * T, W);
   const int n_tiles = (int)(t_end - t_begin);
   if (n_tiles <= 0) return;
@@ -373,7 +372,6 @@ hipError_t launch_s(const DecodeParams& p, hipStream_t stream) {
   switch (p.depth) {
     case 1: return launch_sd<D, 1>(p, stream);
     case 2: return launch_sd<D, 2>(p, stream);
-    case 3: return launch_sd<D, 3>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -381,11 +379,8 @@ hipError_t launch_s(const DecodeParams& p, hipStream_t stream) {
 }  // namespace
 
 const void* stream_kernel_symbol(int head_dim, int depth) {
-  if (head_dim == 128)
-    return depth == 1 ? (const void*)decode_stream_kernel<128, 1>
-                      : depth == 2 ? (const void*)decode_stream_kernel<128, 2> : (const void*)decode_stream_kernel<128, 3>;
-  return depth == 1 ? (const void*)decode_stream_kernel<64, 1>
-                    : depth == 2 ? (const void*)decode_stream_kernel<64, 2> : (const void*)decode_stream_kernel<64, 3>;
+  if (head_dim == 128) return depth == 1 ? (const void*)decode_stream_kernel<128, 1> : (const void*)decode_stream_kernel<128, 2>;
+  return depth == 1 ? (const void*)decode_stream_kernel<64, 1> : (const void*)decode_stream_kernel<64, 2>;
 }
 
 hipError_t launch_decode_stream(const DecodeParams& p, int head_dim, hipStream_t stream) {

@@ -291,7 +291,9 @@ hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
     case 1: return launch_g<T, D, 1>(p, grid, stream);
     case 2: return launch_g<T, D, 2>(p, grid, stream);
     case 4: return launch_g<T, D, 4>(p, grid, stream);
-    case 8: return launch_g<T, D, 8>(p, grid, stream);
+    case 8:
+      if constexpr (sizeof(T) == 4 && D == 128) return hipErrorInvalidValue;  // would spill; never planned
+      else return launch_g<T, D, 8>(p, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

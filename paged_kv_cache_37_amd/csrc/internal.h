@@ -36,7 +36,6 @@ struct DecodeParams {
   int32_t depth;                // blocks of K/V a wave keeps in flight ahead of the one it computes
   int32_t* prefix;              // [S + 1] table entries before each sequence   (streaming only)
   int32_t stream_wgs;           // persistent workgroups of a streaming launch   (streaming only)
-  int32_t stream_order;         // 0: ranges contiguous per XCD; 1: interleaved over XCDs
 };
 
 // Span of one block-table row: leading slots of the first block that are

@@ -133,16 +133,6 @@ int32_t cache_write(kvp_pool pool, int32_t layer, const void* k_new, const void*
   return ok();
 }
 
-static int32_t decode_depth(int32_t mfma) {
-  // Blocks of K/V each wave keeps in flight ahead of the one it computes.
-  static const int env = [] {
-    const char* e = getenv("KVP_DECODE_DEPTH");
-    return e ? atoi(e) : 0;
-  }();
-  if (env >= 1 && env <= (mfma ? 3 : 2)) return env;
-  return mfma ? 2 : 1;
-}
-
 // Resident workgroups of the streaming kernel on the current device:
 // compute units x workgroups per compute unit at the kernel's occupancy.
 // 0 if there is no device to ask.
@@ -164,7 +154,30 @@ static int32_t stream_workgroups(int32_t head_dim, int32_t depth) {
   return cached_wgs;
 }
 
+// The streaming kernel keeps its tile counts in 32-bit prefix sums and its
+// split (tile * waves / tiles) exact in double arithmetic: both hold when
+// these bounds do.
+static bool stream_fits(int32_t num_seqs, int32_t max_blocks, int32_t head_groups, int32_t wgs) {
+  const double entries = (double)num_seqs * max_blocks;
+  const double waves = (double)wgs * kvp::kWaves;
+  return num_seqs <= kvp::kMaxStreamSeqs && entries < 2147483647.0 &&
+         entries * head_groups * (waves + 1.0) < 4503599627370496.0;  // 2^52
+}
+
 enum { PATH_VALU = 0, PATH_MFMA = 1, PATH_STREAM = 2 };
+
+// Blocks of K/V each wave keeps in flight ahead of the one it computes:
+// KVP_DECODE_DEPTH if set and valid for the path, else the measured best
+// (the streaming kernel keeps every wave busy across rows, so one suffices).
+static int32_t decode_depth(int32_t path) {
+  static const int env = [] {
+    const char* e = getenv("KVP_DECODE_DEPTH");
+    return e ? atoi(e) : 0;
+  }();
+  const int max_depth = path == PATH_MFMA ? 3 : 2;
+  if (env >= 1 && env <= max_depth) return env;
+  return path == PATH_MFMA ? 2 : 1;
+}
 
 static int32_t plan(kvp_pool pool, int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks, int32_t partition_tokens,
                     int32_t variant, kvp::DecodeParams* p, int32_t* path) {
@@ -179,14 +192,16 @@ static int32_t plan(kvp_pool pool, int32_t num_seqs, int32_t num_q_heads, int32_
     return fail(KVP_ERR_INVALID_ARG, "partition_tokens must be 0 or a multiple of 16 in [16, 1024]");
   const int32_t G = num_q_heads / d.num_kv_heads;
   const bool bf16 = d.dtype == KVP_BF16;
+  const int32_t mfma_groups = d.num_kv_heads * ((G + 15) / 16);  // head groups of the MFMA kernels
   int32_t pth;
   switch (variant) {
     case KVP_VARIANT_AUTO:
-      pth = !bf16 ? PATH_VALU
-                  : (partition_tokens == 0 && num_seqs <= kvp::kMaxStreamSeqs &&
-                     stream_workgroups(d.head_dim, decode_depth(1)) > 0)
-                        ? PATH_STREAM
-                        : PATH_MFMA;
+      if (!bf16) {
+        pth = PATH_VALU;
+      } else {
+        const int32_t wgs = partition_tokens == 0 ? stream_workgroups(d.head_dim, decode_depth(PATH_STREAM)) : 0;
+        pth = wgs > 0 && stream_fits(num_seqs, max_blocks, mfma_groups, wgs) ? PATH_STREAM : PATH_MFMA;
+      }
       break;
     case KVP_VARIANT_VALU: pth = PATH_VALU; break;
     case KVP_VARIANT_MFMA:
@@ -205,8 +220,10 @@ static int32_t plan(kvp_pool pool, int32_t num_seqs, int32_t num_q_heads, int32_
   if (pth != PATH_VALU) {
     hpw = G < 16 ? G : 16;
   } else {
+    // fp32 at head_dim 128 holds 8 heads' accumulators only by spilling
+    const int32_t cap = d.dtype == KVP_F32 && d.head_dim == 128 ? 4 : 8;
     hpw = 1;
-    while (hpw < G && hpw < 8) hpw *= 2;
+    while (hpw < G && hpw < cap) hpw *= 2;
   }
   const int32_t qgroups = (G + hpw - 1) / hpw;
   if ((long)d.num_kv_heads * qgroups > 65535) return fail(KVP_ERR_UNSUPPORTED, "too many head groups");
@@ -224,15 +241,12 @@ static int32_t plan(kvp_pool pool, int32_t num_seqs, int32_t num_q_heads, int32_
   p->qgroups = qgroups;
   p->part_blocks = pb;
   p->num_parts = (max_blocks + pb - 1) / pb;
-  p->depth = decode_depth(pth != PATH_VALU);
+  p->depth = decode_depth(pth);
   if (pth == PATH_STREAM) {
-    static const int order = [] {
-      const char* e = getenv("KVP_STREAM_ORDER");
-      return e ? atoi(e) : 0;
-    }();
-    p->stream_order = order == 1;
     p->stream_wgs = stream_workgroups(d.head_dim, p->depth);
     if (p->stream_wgs <= 0) return fail(KVP_ERR_HIP, "cannot size the streaming grid (no device?)");
+    if (!stream_fits(num_seqs, max_blocks, d.num_kv_heads * qgroups, p->stream_wgs))
+      return fail(KVP_ERR_UNSUPPORTED, "num_seqs * max_blocks_per_seq too large for the STREAM variant");
   }
   *path = pth;
   return KVP_OK;
