@@ -9,7 +9,8 @@ served from the 256 MB last-level cache.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
 
 Prints one JSON line.  `value` is the step's algorithmic bytes (K/V of the
-attended tokens, queries, outputs, tables, the written K/V) per second;
+attended slots, each physical slot once, queries, outputs, tables, the
+written K/V) per second;
 `roofline` relates the attention call's algorithmic bytes to its average
 duration (HIP events on the launch stream) and the 8 TB/s HBM peak;
 `cpu_baseline` times the CPU oracle on a bounded sample of the same batch.
@@ -77,6 +78,22 @@ def copy_probe(mib: int) -> None:
     log(f"copied {mib} MiB x3")
 
 
+def attended_slots(w) -> int:
+    """Distinct physical slots the step's attention reads (after the
+    next-token write): each sequence's attended positions mapped through
+    its table, union over sequences."""
+    import numpy as np
+
+    slots = []
+    for s in range(w.num_seqs):
+        ctx = int(w.seq_lens_after[s])
+        first = max(0, ctx - w.window) if w.window else 0
+        so = first % 16
+        idx = np.arange(so, so + ctx - first)
+        slots.append(w.block_tables_after[s][idx // 16].astype(np.int64) * 16 + idx % 16)
+    return int(np.unique(np.concatenate(slots)).size) if slots else 0
+
+
 def cpu_baseline(w, budget_s: float = 10.0) -> dict:
     """Time the CPU oracle (as it is, one thread) on whole sequences of the
     batch, pass after pass, until about `budget_s` seconds are spent."""
@@ -126,8 +143,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (see the sharding notes "
-              "in DESIGN.md); run it with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (each GPU would run "
+              "the same kernels on its own sequences or KV heads); run it with --gpus 1", file=sys.stderr)
         return 2
 
     import numpy as np
@@ -204,11 +221,16 @@ def main() -> int:
     ms_per_step = total_ms / K
     log(f"step {ms_per_step * 1e3:.1f} us (write {write_ms * 1e3:.1f} us, attention {attn_ms * 1e3:.1f} us)")
 
-    # algorithmic bytes
+    # algorithmic bytes: K/V of every attended slot counted once (a prefix
+    # block shared by many sequences is one physical block: HBM serves it
+    # once), plus queries, outputs, table rows and lengths
     S, Hq, D, Hkv, eb = w.num_seqs, w.num_q_heads, w.head_dim, w.num_kv_heads, w.elt_bytes
     valid_after = np.minimum(w.seq_lens_after, w.window) if w.window else w.seq_lens_after
-    kv_read = int(valid_after.astype(np.int64).sum()) * 2 * Hkv * D * eb
-    attn_bytes = kv_read + 2 * S * Hq * D * eb + int(np.asarray(w.row_blocks_after).sum()) * 4 + S * 4
+    per_token = 2 * Hkv * D * eb
+    kv_logical = int(valid_after.astype(np.int64).sum()) * per_token
+    kv_read = attended_slots(w) * per_token
+    other = 2 * S * Hq * D * eb + int(np.asarray(w.row_blocks_after).sum()) * 4 + S * 4
+    attn_bytes = kv_read + other
     write_bytes = 2 * 2 * S * Hkv * D * eb + S * 4
     step_bytes = attn_bytes + write_bytes
     achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
@@ -247,6 +269,9 @@ def main() -> int:
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seq_layer_steps_per_s": round(S / (ms_per_step * 1e-3), 1),
         "attention_us": round(attn_ms * 1e3, 2),
+        "kv_bytes_logical": kv_logical,
+        "kv_bytes_unique": kv_read,
+        "logical_kv_gbs": round(kv_logical / (attn_ms * 1e-3) / 1e9, 2),
         "cache_write_us": round(write_ms * 1e3, 2),
         "roofline": {
             "bound": "hbm",

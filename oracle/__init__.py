@@ -42,8 +42,7 @@ Sources (the pages this follows; titles as printed on them):
 The pages never write the attention formula; the one used is the standard
 scaled dot-product attention of one decode query over all cached keys,
 softmax(q . K^T * scale) . V, with query head h reading KV head h // G
-(G = query heads per KV head).  Every reading taken where the pages are
-silent is listed in the repository's design notes.
+(G = query heads per KV head).
 
 Each function is pinned by ``tests/test_oracle.py`` against the pages'
 worked values, closed forms, invariants and an independent library routine.
