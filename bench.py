@@ -1,8 +1,10 @@
 """Benchmark of the paged decode hot path on one MI355X.
 
-A step is one decode step of one layer for the whole batch: cache_write of
+A step is one decode step of one layer for the whole batch: the write of
 every sequence's new token into its slot, then paged decode attention of
-every sequence over its context (new token included).  Steps rotate over
+every sequence over its context (new token included): one
+paged_decode_step call (the streaming kernel fuses the write), or with
+--unfused a cache_write call and a paged_decode_attention call.  Steps rotate over
 `--layers` layer slices of one pool so that the KV read each step is not
 served from the 256 MB last-level cache.
 
@@ -11,8 +13,10 @@ served from the 256 MB last-level cache.
 Prints one JSON line.  `value` is the step's algorithmic bytes (K/V of the
 attended slots, each physical slot once, queries, outputs, tables, the
 written K/V) per second;
-`roofline` relates the attention call's algorithmic bytes to its average
-duration (HIP events on the launch stream) and the 8 TB/s HBM peak;
+`roofline` relates the timed call's algorithmic bytes (the step's, or the
+attention's with --unfused) to its average duration, from HIP events on the
+launch stream around each call in a second pass of the same K steps (the
+first pass, timed as a whole, gives `value`), and the 8 TB/s HBM peak;
 `cpu_baseline` times the CPU oracle on a bounded sample of the same batch.
 """
 from __future__ import annotations
@@ -51,15 +55,16 @@ def profile_slug(workload_name: str) -> str:
     return workload_name.replace("/", "-").replace("..", "-")
 
 
-def traffic_from_profiles(workload_name: str, variant: str):
-    """Counter-measured HBM bytes per attention call, if the profiles were
-    taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"decode_{variant}.{profile_slug(workload_name)}.traffic.json")
+def traffic_from_profiles(workload_name: str, label: str):
+    """Counter-measured HBM bytes per timed call, if the profiles were taken
+    on the current kernel sources (`label` names the call: decode_<variant>
+    for the attention call, decode_<variant>_step for the fused step)."""
+    path = os.path.join(ROOT, "profiles", f"{label}.{profile_slug(workload_name)}.traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_hash") != kernel_hash() or rec.get("variant") != variant:
+    if rec.get("kernel_hash") != kernel_hash() or rec.get("label", rec.get("variant")) != label:
         return None
     return rec.get("hbm_bytes_per_call")
 
@@ -137,6 +142,8 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=None, help="layer slices to rotate over")
     ap.add_argument("--variant", default="auto", choices=["auto", "stream", "mfma", "valu"])
     ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--unfused", action="store_true",
+                    help="time cache_write and paged_decode_attention as two calls instead of paged_decode_step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a device copy of MIB MiB (counter calibration) and exit")
@@ -186,40 +193,63 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
 
-    def step(i):
-        layer = i % L
+    def write(layer):
         ops.cache_write(pool, layer, k_new, v_new, slots, stream=stream)
+
+    def attend(layer):
         ops.paged_decode_attention(pool, layer, q, tables, lens, w.scale, out=out, sliding_window=w.window,
                                    partition_tokens=args.partition_tokens, variant=args.variant, workspace=ws,
                                    stream=stream)
+
+    def fused(layer):
+        ops.paged_decode_step(pool, layer, q, tables, lens, w.scale, k_new, v_new, slots, out=out,
+                              sliding_window=w.window, partition_tokens=args.partition_tokens, variant=args.variant,
+                              workspace=ws, stream=stream)
+
+    def step(i):
+        if args.unfused:
+            write(i % L)
+            attend(i % L)
+        else:
+            fused(i % L)
 
     log(f"warmup {args.warmup} steps")
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
+    # Pass 1 (the bench value): K steps back to back, timed as a whole.
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     log(f"timing {K} steps")
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(K):
-        layer = i % L
-        ev[i][0].record(stream)
-        ops.cache_write(pool, layer, k_new, v_new, slots, stream=stream)
-        ev[i][1].record(stream)
-        ops.paged_decode_attention(pool, layer, q, tables, lens, w.scale, out=out, sliding_window=w.window,
-                                   partition_tokens=args.partition_tokens, variant=args.variant, workspace=ws,
-                                   stream=stream)
-        ev[i][2].record(stream)
+        step(i)
     end.record(stream)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
+    ms_per_step = start.elapsed_time(end) / K
+
+    # Pass 2 (the roofline): the same K steps with events around each call.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        layer = i % L
+        ev[i][0].record(stream)
+        if args.unfused:
+            write(layer)
+            ev[i][1].record(stream)
+            attend(layer)
+        else:
+            ev[i][1].record(stream)
+            fused(layer)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
     write_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    attn_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
-    ms_per_step = total_ms / K
-    log(f"step {ms_per_step * 1e3:.1f} us (write {write_ms * 1e3:.1f} us, attention {attn_ms * 1e3:.1f} us)")
+    call_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K  # the attention call, or the fused step call
+    log(f"step {ms_per_step * 1e3:.1f} us; per call ("
+        + (f"write {write_ms * 1e3:.1f} us, attention {call_ms * 1e3:.1f} us)" if args.unfused
+           else f"fused write + attention {call_ms * 1e3:.1f} us)"))
 
     # algorithmic bytes: K/V of every attended slot counted once (a prefix
     # block shared by many sequences is one physical block: HBM serves it
@@ -233,11 +263,16 @@ def main() -> int:
     attn_bytes = kv_read + other
     write_bytes = 2 * 2 * S * Hkv * D * eb + S * 4
     step_bytes = attn_bytes + write_bytes
-    achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
+    call_bytes = attn_bytes if args.unfused else step_bytes
+    achieved = call_bytes / (call_ms * 1e-3) / 1e9
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     variant = args.variant
     if variant == "auto":
         variant = "valu" if w.dtype == "f32" else ("mfma" if args.partition_tokens else "stream")
+    label = f"decode_{variant}" if args.unfused else f"decode_{variant}_step"
+    kernel = ("paged_decode_attention (decode + merge launches)" if args.unfused else
+              "paged_decode_step (" + ("fused write + decode, merge launches)" if variant == "stream"
+                                       else "cache_write, decode, merge launches)"))
 
     result = {
         "metric": METRIC,
@@ -264,24 +299,26 @@ def main() -> int:
             "layer_slices": L,
             "variant": variant,
             "partition_tokens": args.partition_tokens,
+            "fused_step": not args.unfused,
             "seed": w.seed,
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seq_layer_steps_per_s": round(S / (ms_per_step * 1e-3), 1),
-        "attention_us": round(attn_ms * 1e3, 2),
+        "call_us": round(call_ms * 1e3, 2),
+        "attention_us": round(call_ms * 1e3, 2) if args.unfused else None,
+        "cache_write_us": round(write_ms * 1e3, 2) if args.unfused else None,
         "kv_bytes_logical": kv_logical,
         "kv_bytes_unique": kv_read,
-        "logical_kv_gbs": round(kv_logical / (attn_ms * 1e-3) / 1e9, 2),
-        "cache_write_us": round(write_ms * 1e3, 2),
+        "logical_kv_gbs": round(kv_logical / (call_ms * 1e-3) / 1e9, 2),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic_from_profiles(w.name, variant),
-            "kernel": "paged_decode_attention (decode + merge launches)",
-            "bytes_per_call": attn_bytes,
+            "traffic": traffic_from_profiles(w.name, label),
+            "kernel": kernel,
+            "bytes_per_call": call_bytes,
         },
         "cpu_baseline": None,
     }

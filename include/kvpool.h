@@ -216,6 +216,57 @@ size_t paged_decode_workspace_bytes(kvp_pool pool, int32_t num_seqs, int32_t num
  */
 int32_t paged_decode_attention(kvp_pool pool, const kvp_decode_args* args, hipStream_t stream);
 
+/*
+ * paged_decode_step -- one decode step of one layer: store each sequence's
+ * new token, then attend with it.
+ *   [Optimizing] "The Block Manager and Dynamic Allocation Lifecycle" (The
+ *   Decode Phase): the new token's K/V go into the next free slot of the
+ *   sequence's last block, and decode attention runs over the context that
+ *   now includes it.
+ *
+ *   args         : as for paged_decode_attention; seq_lens[s] counts the
+ *                  new token.
+ *   k_new, v_new : device, [num_seqs][num_kv_heads][head_dim], pool dtype,
+ *                  one token per sequence, 16-byte aligned.
+ *   slot_mapping : device int32 [num_seqs]: slot of sequence s's new token,
+ *                  which must be the slot of position seq_lens[s]-1 of row s
+ *                  (in the row's last block, a block no other sequence
+ *                  uses: copy-on-write happens first).  Negative: s has no
+ *                  new token (attention only); >= num_blocks*16: nothing
+ *                  is written.
+ *
+ *   Result: the pool and out are bit-identical to cache_write(num_seqs
+ *   tokens) followed by paged_decode_attention.  The STREAM variant does
+ *   both in one pass (the wave that computes a row's last block takes the
+ *   new K/V from registers and stores them to the pool); other variants
+ *   launch the write first.  If a slot breaks the rule above, the values
+ *   written and the outputs are unspecified, but nothing outside the pool,
+ *   the table rows and the outputs is accessed.  Errors as for
+ *   paged_decode_attention, plus KVP_ERR_INVALID_ARG for NULL or misaligned
+ *   k_new, v_new or slot_mapping.
+ */
+int32_t paged_decode_step(kvp_pool pool, const kvp_decode_args* args, const void* k_new,
+                          const void* v_new, const int32_t* slot_mapping, hipStream_t stream);
+
+/*
+ * kv_pool_copy_blocks -- the device side of copy-on-write, every layer.
+ *   [Optimizing] "Copy-on-Write (CoW) for Parallel Sampling and Prefix
+ *   Caching": before a sequence writes into a block it shares, it is given a
+ *   new physical block holding a copy of the shared one (the host
+ *   bookkeeping allocates it, moves the reference and repoints the table).
+ *
+ *   src, dst  : device int32 [num_pairs] physical block ids; every layer's
+ *               K and V of block src[i] are copied into block dst[i].  A
+ *               pair with an id outside [0, num_blocks) or src == dst is
+ *               skipped.  No dst may repeat or appear as a src in the same
+ *               call (the copies of one call run in no particular order).
+ *   Bit-exact.  num_pairs == 0 launches nothing.  Errors:
+ *   KVP_ERR_INVALID_ARG (NULL or misaligned ids, num_pairs < 0),
+ *   KVP_ERR_HIP.
+ */
+int32_t kv_pool_copy_blocks(kvp_pool pool, const int32_t* src, const int32_t* dst,
+                            int32_t num_pairs, hipStream_t stream);
+
 /* Static text of a status code. */
 const char* kvp_status_str(int32_t status);
 

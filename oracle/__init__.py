@@ -9,6 +9,8 @@ paged KV cache computes, in float64:
 
 * ``cache_write``  -- scatter each new token's K and V into the slot a slot
   mapping names (slot = physical block * block_size + offset);
+* ``copy_blocks`` -- the copy-on-write block copy: every layer's K and V of
+  one physical block into another;
 * ``decode_attention`` -- for every sequence, walk its block table, gather
   its keys and values into contiguous arrays, and run softmax(q K^T scale) V
   for every query head;
@@ -27,7 +29,8 @@ Sources (the pages this follows; titles as printed on them):
   Block Manager and Dynamic Allocation Lifecycle (prefill and decode writes
   into physical blocks; decode appends into the last block while it has
   room), §The Math of the KV Cache Bottleneck (GQA: fewer KV heads than
-  query heads).
+  query heads), §Copy-on-Write (CoW) for Parallel Sampling and Prefix
+  Caching (a writer of a shared block gets a private copy first).
 * [Paged] the paged-attention post on zhangchitc.github.io -- §What a
   physical block looks like (a block is [2, block_size, num_kv_heads,
   head_dim] per layer), §Two lookup structures (req_to_blocks is the
@@ -49,6 +52,7 @@ worked values, closed forms, invariants and an independent library routine.
 """
 from .paged import (  # noqa: F401
     cache_write,
+    copy_blocks,
     check_tables,
     decode_attention,
     decode_attention_bruteforce,

@@ -115,6 +115,20 @@ def cache_write(pool: np.ndarray, layer: int, k_new: np.ndarray, v_new: np.ndarr
     return out
 
 
+def copy_blocks(pool: np.ndarray, src, dst) -> np.ndarray:
+    """Return a copy of `pool` in which every layer's K and V of physical
+    block dst[i] equal those of block src[i] before the call ([Optimizing]
+    §Copy-on-Write (CoW) for Parallel Sampling and Prefix Caching: a writer
+    of a shared block gets a new physical block holding a copy of it).
+    Pairs naming a block outside the pool, or src == dst, are skipped."""
+    out = pool.copy()
+    nb = pool.shape[1]
+    for a, b in zip(np.asarray(src).tolist(), np.asarray(dst).tolist()):
+        if 0 <= a < nb and 0 <= b < nb and a != b:
+            out[:, b] = pool[:, a]
+    return out
+
+
 # ---------------------------------------------------------------------------
 # decode attention
 

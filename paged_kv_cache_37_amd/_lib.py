@@ -37,6 +37,8 @@ EXPORTS = (
     "cache_write",
     "paged_decode_workspace_bytes",
     "paged_decode_attention",
+    "paged_decode_step",
+    "kv_pool_copy_blocks",
     "kvp_status_str",
     "kvp_last_error",
 )
@@ -88,6 +90,8 @@ def _load() -> ctypes.CDLL:
         "cache_write": (i32, [P, i32, P, P, P, i32, P]),
         "paged_decode_workspace_bytes": (ctypes.c_size_t, [P, i32, i32, i32, i32]),
         "paged_decode_attention": (i32, [P, ctypes.POINTER(DecodeArgs), P]),
+        "paged_decode_step": (i32, [P, ctypes.POINTER(DecodeArgs), P, P, P, P]),
+        "kv_pool_copy_blocks": (i32, [P, P, P, i32, P]),
         "kvp_status_str": (ctypes.c_char_p, [i32]),
         "kvp_last_error": (ctypes.c_char_p, []),
     }

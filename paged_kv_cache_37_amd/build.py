@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvpool.so")
 
-SOURCES = ["kvpool_api.cpp", "cache_write.hip", "decode_mfma.hip", "decode_valu.hip", "decode_reduce.hip",
+SOURCES = ["kvpool_api.cpp", "cache_write.hip", "copy_blocks.hip", "decode_mfma.hip", "decode_valu.hip", "decode_reduce.hip",
            "decode_stream.hip"]
 
 ARCH = "gfx950"

@@ -67,7 +67,15 @@ struct StreamTile {
   int row_id;  // rows of this wave counted from 0
 };
 
-template <int D, int DEPTH>
+// FUSED: the step also stores each sequence's new token (k_new/v_new at
+// slot_mapping[s], the decode-phase append of [Optimizing] The Block Manager
+// and Dynamic Allocation Lifecycle) and attends with it at position
+// seq_lens[s] - 1: the wave that computes a row's last block takes the new
+// key/value from registers instead of the pool, and the wave of the KV
+// head's first head group writes them to the pool.  No wave reads a slot
+// another wave writes in the same launch (the slot lies in the sequence's
+// own last block), so no ordering between waves is needed.
+template <int D, int DEPTH, bool FUSED>
 __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stream_kernel(const DecodeParams P) {
   constexpr int NBUF = DEPTH + 1;
   __shared__ int pre[kMaxStreamSeqs + 1];  // pre[s] = table entries of sequences < s
@@ -254,10 +262,77 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
     }
   };
 
+  // The new token of the current and of the next row (FUSED only): lanes
+  // 0..D/8-1 hold its key (8 dims each), lanes 0..D/2-1 its value (2 dims
+  // each); slot < 0 when the row has no token to write.
+  uint4_v kn = {0, 0, 0, 0}, kn_next = {0, 0, 0, 0};
+  unsigned vn = 0, vn_next = 0;
+  int slot_c = -1, slot_next = -1;
+  auto load_new = [&](const RowCtx& r, uint4_v& kd, unsigned& vd, int& sd) {
+    if constexpr (FUSED) {
+      const int sl = __builtin_amdgcn_readfirstlane(P.slot_mapping[r.s]);
+      sd = sl >= 0 && sl < P.num_blocks * kBlock ? sl : -1;
+      const size_t tok = ((size_t)r.s * P.num_kv_heads + r.hg / P.qgroups) * D;
+      kd = lane < D / 8 ? ((const uint4_v*)((const uint16_t*)P.k_new + tok))[lane] : uint4_v{0, 0, 0, 0};
+      vd = lane < D / 2 ? ((const unsigned*)((const uint16_t*)P.v_new + tok))[lane] : 0u;
+    }
+  };
+  load_new(cr, kn, vn, slot_c);
+  load_new(qn, kn_next, vn_next, slot_next);
+
+  // The row's last block holds the new token at table slot send - 1: put
+  // its key and value into this wave's operands (layouts of mfma_tile.h),
+  // and store them into the pool once per KV head.
+  auto put_new = [&](MfmaTiles<D>& t) {
+    const int o = (crs.start_off + crs.n - 1) & (kBlock - 1);
+    const int q4 = lane >> 4, j = lane & 15;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      const int src = 4 * kk + q4;  // lane holding dims 32 kk + 8 q4 .. +7
+      const uint4_v v = {(unsigned)__shfl((int)kn.x, src), (unsigned)__shfl((int)kn.y, src),
+                         (unsigned)__shfl((int)kn.z, src), (unsigned)__shfl((int)kn.w, src)};
+      if (j == o) t.k[kk] = v;
+    }
+    const bool hi = (o & 1) != 0;
+    const unsigned keep = hi ? 0x0000ffffu : 0xffff0000u;
+    const int sh = hi ? 16 : 0;
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) {
+      const unsigned nv = (unsigned)__shfl((int)vn, 16 * m + j);  // dims 32 m + 2 j (low half), +1
+      if (q4 == (o >> 2)) {
+        const unsigned d0 = (nv & 0xffffu) << sh, d1 = (nv >> 16) << sh;
+        if ((o & 2) == 0) {
+          t.v[m].x = (t.v[m].x & keep) | d0;
+          t.v[m].z = (t.v[m].z & keep) | d1;
+        } else {
+          t.v[m].y = (t.v[m].y & keep) | d0;
+          t.v[m].w = (t.v[m].w & keep) | d1;
+        }
+      }
+    }
+    if (cr.hg % P.qgroups == 0) {
+      const int kvh = cr.hg / P.qgroups, b = slot_c >> 4, off = slot_c & (kBlock - 1);
+      uint16_t* blk = (uint16_t*)P.pool_layer + (size_t)b * 2 * P.num_kv_heads * kBlock * D;
+      uint16_t* kt = blk + (size_t)kvh * kBlock * D;
+      uint16_t* vt = blk + (size_t)(P.num_kv_heads + kvh) * kBlock * D;
+      if (lane < D / 8) *(uint4_v*)(kt + off * D + 8 * lane) = kn;
+      if (lane < D / 2) {
+        const int e = ((off >> 2) * D + 2 * lane) * 4 + (off & 3);
+        vt[e] = (uint16_t)(vn & 0xffffu);
+        vt[e + 4] = (uint16_t)(vn >> 16);
+      }
+    }
+  };
+
   auto compute = [&](StreamTile<D>& x) {
     if (x.row_id != crow_id) {  // first tile of the next row
       finish_row();
       cr = qn;
+      if constexpr (FUSED) {
+        kn = kn_next;
+        vn = vn_next;
+        slot_c = slot_next;
+      }
       ++crow_id;
       c_h0 = head0(cr.hg);
       c_nh = heads(cr.hg);
@@ -271,6 +346,10 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
       const uint16_t* qp = q + ((size_t)qn.s * P.num_q_heads + head0(qn.hg) + g) * D + 8 * (lane >> 4);
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) q_next[kk] = g < nh_n ? *(const uint4_v*)(qp + 32 * kk) : uint4_v{0, 0, 0, 0};
+      load_new(qn, kn_next, vn_next, slot_next);
+    }
+    if constexpr (FUSED) {
+      if (slot_c >= 0 && x.j == crs.nblocks - 1) put_new(x.t);
     }
     st.step(x.t, x.j, crs.start_off, crs.start_off + crs.n, crs.nblocks, P.scale_log2, lane);
   };
@@ -359,7 +438,10 @@ __global__ __launch_bounds__(256) void decode_stream_reduce_kernel(const DecodeP
 
 template <int D, int DEPTH>
 hipError_t launch_sd(const DecodeParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_stream_kernel<D, DEPTH>), dim3(p.stream_wgs), dim3(kThreads), 0, stream, p);
+  if (p.slot_mapping)
+    hipLaunchKernelGGL((decode_stream_kernel<D, DEPTH, true>), dim3(p.stream_wgs), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_stream_kernel<D, DEPTH, false>), dim3(p.stream_wgs), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid((p.num_q_heads + 3) / 4, p.num_seqs);
@@ -378,9 +460,13 @@ hipError_t launch_s(const DecodeParams& p, hipStream_t stream) {
 
 }  // namespace
 
-const void* stream_kernel_symbol(int head_dim, int depth) {
-  if (head_dim == 128) return depth == 1 ? (const void*)decode_stream_kernel<128, 1> : (const void*)decode_stream_kernel<128, 2>;
-  return depth == 1 ? (const void*)decode_stream_kernel<64, 1> : (const void*)decode_stream_kernel<64, 2>;
+const void* stream_kernel_symbol(int head_dim, int depth, bool fused) {
+  if (head_dim == 128) {
+    if (fused) return depth == 1 ? (const void*)decode_stream_kernel<128, 1, true> : (const void*)decode_stream_kernel<128, 2, true>;
+    return depth == 1 ? (const void*)decode_stream_kernel<128, 1, false> : (const void*)decode_stream_kernel<128, 2, false>;
+  }
+  if (fused) return depth == 1 ? (const void*)decode_stream_kernel<64, 1, true> : (const void*)decode_stream_kernel<64, 2, true>;
+  return depth == 1 ? (const void*)decode_stream_kernel<64, 1, false> : (const void*)decode_stream_kernel<64, 2, false>;
 }
 
 hipError_t launch_decode_stream(const DecodeParams& p, int head_dim, hipStream_t stream) {

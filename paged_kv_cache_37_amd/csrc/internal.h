@@ -36,6 +36,9 @@ struct DecodeParams {
   int32_t depth;                // blocks of K/V a wave keeps in flight ahead of the one it computes
   int32_t* prefix;              // [S + 1] table entries before each sequence   (streaming only)
   int32_t stream_wgs;           // persistent workgroups of a streaming launch   (streaming only)
+  const void* k_new;            // [S][Hkv][D] new token per sequence        (fused write only)
+  const void* v_new;            // [S][Hkv][D]                               (fused write only)
+  const int32_t* slot_mapping;  // [S]; NULL: attention only                 (fused write only)
 };
 
 // Span of one block-table row: leading slots of the first block that are
@@ -64,10 +67,12 @@ __device__ __forceinline__ RowSpan row_span(int ctx, int window, int max_blocks)
 hipError_t launch_cache_write(void* pool_layer, int dtype, int num_blocks, int num_kv_heads,
                               int head_dim, const void* k_new, const void* v_new,
                               const int32_t* slots, int num_tokens, hipStream_t stream);
+hipError_t launch_copy_blocks(void* pool_base, int num_layers, int num_blocks, size_t block_bytes, const int32_t* src,
+                              const int32_t* dst, int num_pairs, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeParams& p, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_decode_stream(const DecodeParams& p, int head_dim, hipStream_t stream);
-const void* stream_kernel_symbol(int head_dim, int depth);
+const void* stream_kernel_symbol(int head_dim, int depth, bool fused);
 
 }  // namespace kvp

@@ -136,20 +136,22 @@ int32_t cache_write(kvp_pool pool, int32_t layer, const void* k_new, const void*
 // Resident workgroups of the streaming kernel on the current device:
 // compute units x workgroups per compute unit at the kernel's occupancy.
 // 0 if there is no device to ask.
-static int32_t stream_workgroups(int32_t head_dim, int32_t depth) {
+static int32_t stream_workgroups(int32_t head_dim, int32_t depth, bool fused = false) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   static thread_local int cached_dev = -1, cached_d = 0, cached_depth = 0, cached_wgs = 0;
-  if (dev == cached_dev && head_dim == cached_d && depth == cached_depth) return cached_wgs;
+  static thread_local bool cached_fused = false;
+  if (dev == cached_dev && head_dim == cached_d && depth == cached_depth && fused == cached_fused) return cached_wgs;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kvp::stream_kernel_symbol(head_dim, depth), kvp::kThreads,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kvp::stream_kernel_symbol(head_dim, depth, fused), kvp::kThreads,
                                                    0) != hipSuccess ||
       per_cu <= 0)
     return 0;
   cached_dev = dev;
   cached_d = head_dim;
   cached_depth = depth;
+  cached_fused = fused;
   cached_wgs = cus * per_cu;
   return cached_wgs;
 }
@@ -293,7 +295,11 @@ size_t paged_decode_workspace_bytes(kvp_pool pool, int32_t num_seqs, int32_t num
   return need;
 }
 
-int32_t paged_decode_attention(kvp_pool pool, const kvp_decode_args* a, hipStream_t stream) {
+// Decode attention, optionally preceded by each sequence's new-token write
+// (slots != NULL): fused into the streaming kernel, else a cache_write launch
+// first.
+static int32_t decode(kvp_pool pool, const kvp_decode_args* a, const void* k_new, const void* v_new,
+                      const int32_t* slots, hipStream_t stream) {
   if (!pool || !a) return fail(KVP_ERR_INVALID_ARG, "NULL pool or args");
   const kvp_pool_desc& d = pool->desc;
   if (a->layer < 0 || a->layer >= d.num_layers) return fail(KVP_ERR_INVALID_ARG, "layer %d out of range", a->layer);
@@ -308,6 +314,21 @@ int32_t paged_decode_attention(kvp_pool pool, const kvp_decode_args* a, hipStrea
     return fail(KVP_ERR_INVALID_ARG, "NULL q, out, block_tables or seq_lens");
   if (!aligned(a->q, 16) || !aligned(a->out, 16) || !aligned(a->block_tables, 4) || !aligned(a->seq_lens, 4))
     return fail(KVP_ERR_INVALID_ARG, "q/out must be 16-byte aligned, tables and lengths 4-byte aligned");
+  const bool write = slots != nullptr || k_new != nullptr || v_new != nullptr;
+  if (write) {
+    if (!k_new || !v_new || !slots) return fail(KVP_ERR_INVALID_ARG, "NULL k_new, v_new or slot_mapping");
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(slots, 4))
+      return fail(KVP_ERR_INVALID_ARG, "k_new/v_new must be 16-byte aligned, slot_mapping 4-byte aligned");
+  }
+  if (write && path == PATH_STREAM) {
+    // the fused kernel holds the new token in registers: ring depth 1
+    p.depth = 1;
+    p.stream_wgs = stream_workgroups(d.head_dim, 1, true);
+    if (p.stream_wgs <= 0) return fail(KVP_ERR_HIP, "cannot size the streaming grid (no device?)");
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.slot_mapping = slots;
+  }
   size_t ml_off = 0, o_off = 0;
   const size_t ws = path == PATH_STREAM ? stream_workspace(p, d.head_dim, &ml_off, &o_off)
                                         : grid_workspace(p, d.head_dim, &ml_off);
@@ -334,6 +355,11 @@ int32_t paged_decode_attention(kvp_pool pool, const kvp_decode_args* a, hipStrea
   p.window = a->sliding_window;
   p.scale_log2 = a->scale * 1.4426950408889634f;
   hipError_t e;
+  if (write && path != PATH_STREAM) {
+    e = kvp::launch_cache_write(const_cast<void*>(p.pool_layer), d.dtype, d.num_blocks, d.num_kv_heads, d.head_dim,
+                                k_new, v_new, slots, a->num_seqs, stream);
+    if (e != hipSuccess) return fail(KVP_ERR_HIP, "cache_write launch: %s", hipGetErrorString(e));
+  }
   if (path == PATH_STREAM) {
     e = kvp::launch_decode_stream(p, d.head_dim, stream);
     if (e != hipSuccess) return fail(KVP_ERR_HIP, "stream decode launch: %s", hipGetErrorString(e));
@@ -346,6 +372,31 @@ int32_t paged_decode_attention(kvp_pool pool, const kvp_decode_args* a, hipStrea
     e = kvp::launch_decode_reduce(p, d.dtype, d.head_dim, stream);
     if (e != hipSuccess) return fail(KVP_ERR_HIP, "reduce launch: %s", hipGetErrorString(e));
   }
+  return ok();
+}
+
+int32_t paged_decode_attention(kvp_pool pool, const kvp_decode_args* a, hipStream_t stream) {
+  return decode(pool, a, nullptr, nullptr, nullptr, stream);
+}
+
+int32_t paged_decode_step(kvp_pool pool, const kvp_decode_args* a, const void* k_new, const void* v_new,
+                          const int32_t* slot_mapping, hipStream_t stream) {
+  if (!k_new || !v_new || !slot_mapping) return fail(KVP_ERR_INVALID_ARG, "NULL k_new, v_new or slot_mapping");
+  return decode(pool, a, k_new, v_new, slot_mapping, stream);
+}
+
+int32_t kv_pool_copy_blocks(kvp_pool pool, const int32_t* src, const int32_t* dst, int32_t num_pairs,
+                            hipStream_t stream) {
+  if (!pool) return fail(KVP_ERR_INVALID_ARG, "pool is NULL");
+  if (num_pairs < 0) return fail(KVP_ERR_INVALID_ARG, "num_pairs < 0");
+  if (num_pairs == 0) return ok();
+  if (!src || !dst) return fail(KVP_ERR_INVALID_ARG, "NULL src or dst");
+  if (!aligned(src, 4) || !aligned(dst, 4)) return fail(KVP_ERR_INVALID_ARG, "src/dst must be 4-byte aligned");
+  const kvp_pool_desc& d = pool->desc;
+  const size_t block_bytes = 2 * (size_t)d.num_kv_heads * kvp::kBlock * d.head_dim * elt_bytes(d.dtype);
+  const hipError_t e = kvp::launch_copy_blocks(pool->base, d.num_layers, d.num_blocks, block_bytes, src, dst,
+                                               num_pairs, stream);
+  if (e != hipSuccess) return fail(KVP_ERR_HIP, "copy_blocks launch: %s", hipGetErrorString(e));
   return ok();
 }
 

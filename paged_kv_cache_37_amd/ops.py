@@ -143,13 +143,9 @@ def make_workspace(pool: KVPool, num_seqs: int, num_q_heads: int, max_blocks_per
     return torch.empty(n, dtype=torch.uint8, device=pool.device) if n else None
 
 
-def paged_decode_attention(pool: KVPool, layer: int, q: torch.Tensor, block_tables: torch.Tensor,
-                           seq_lens: torch.Tensor, scale: float, out: Optional[torch.Tensor] = None,
-                           sliding_window: int = 0, partition_tokens: int = 0, variant: str = "auto",
-                           workspace: Optional[torch.Tensor] = None,
-                           stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
-    """Decode attention of q [S, Hq, D] over the pool through block_tables
-    [S, max_blocks] and seq_lens [S]; returns out [S, Hq, D]."""
+def _decode_args(pool: KVPool, layer: int, q: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                 scale: float, out: Optional[torch.Tensor], sliding_window: int, partition_tokens: int, variant: str,
+                 workspace: Optional[torch.Tensor]):
     if q.dim() != 3:
         raise ValueError("q must be [num_seqs, num_q_heads, head_dim]")
     S, Hq, D = q.shape
@@ -178,10 +174,54 @@ def paged_decode_attention(pool: KVPool, layer: int, q: torch.Tensor, block_tabl
         workspace=workspace.data_ptr() if workspace is not None else None,
         workspace_bytes=workspace.numel() * workspace.element_size() if workspace is not None else 0,
     )
+    return args, out
+
+
+def paged_decode_attention(pool: KVPool, layer: int, q: torch.Tensor, block_tables: torch.Tensor,
+                           seq_lens: torch.Tensor, scale: float, out: Optional[torch.Tensor] = None,
+                           sliding_window: int = 0, partition_tokens: int = 0, variant: str = "auto",
+                           workspace: Optional[torch.Tensor] = None,
+                           stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Decode attention of q [S, Hq, D] over the pool through block_tables
+    [S, max_blocks] and seq_lens [S]; returns out [S, Hq, D]."""
+    args, out = _decode_args(pool, layer, q, block_tables, seq_lens, scale, out, sliding_window, partition_tokens,
+                             variant, workspace)
     check(lib.paged_decode_attention(pool.handle, ctypes.byref(args), _stream(pool.device, stream)),
           "paged_decode_attention")
     return out
 
 
+def paged_decode_step(pool: KVPool, layer: int, q: torch.Tensor, block_tables: torch.Tensor,
+                      seq_lens: torch.Tensor, scale: float, k_new: torch.Tensor, v_new: torch.Tensor,
+                      slot_mapping: torch.Tensor, out: Optional[torch.Tensor] = None, sliding_window: int = 0,
+                      partition_tokens: int = 0, variant: str = "auto", workspace: Optional[torch.Tensor] = None,
+                      stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Store each sequence's new token (k_new/v_new [S, Hkv, D] at
+    slot_mapping [S], the slot of position seq_lens[s]-1) and attend with it;
+    the same result as cache_write followed by paged_decode_attention."""
+    args, out = _decode_args(pool, layer, q, block_tables, seq_lens, scale, out, sliding_window, partition_tokens,
+                             variant, workspace)
+    shape = (q.shape[0], pool.num_kv_heads, pool.head_dim)
+    _need(k_new, "k_new", pool.dtype, pool.device, shape)
+    _need(v_new, "v_new", pool.dtype, pool.device, shape)
+    _need(slot_mapping, "slot_mapping", torch.int32, pool.device, (q.shape[0],))
+    check(lib.paged_decode_step(pool.handle, ctypes.byref(args), ctypes.c_void_p(k_new.data_ptr()),
+                                ctypes.c_void_p(v_new.data_ptr()), ctypes.c_void_p(slot_mapping.data_ptr()),
+                                _stream(pool.device, stream)), "paged_decode_step")
+    return out
+
+
+def copy_blocks(pool: KVPool, src: torch.Tensor, dst: torch.Tensor,
+                stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Copy every layer's K/V of physical block src[i] into dst[i] (int32
+    device tensors of equal length): the device side of copy-on-write."""
+    if src.dim() != 1 or dst.shape != src.shape:
+        raise ValueError("src and dst must be 1-D of equal length")
+    _need(src, "src", torch.int32, pool.device)
+    _need(dst, "dst", torch.int32, pool.device)
+    check(lib.kv_pool_copy_blocks(pool.handle, ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                  int(src.shape[0]), _stream(pool.device, stream)), "kv_pool_copy_blocks")
+
+
 __all__ = ["KVPool", "KVPoolError", "kv_pool_create", "cache_write", "paged_decode_workspace_bytes",
-           "make_workspace", "paged_decode_attention", "BLOCK_SIZE"]
+           "make_workspace", "paged_decode_attention", "paged_decode_step", "copy_blocks", "BLOCK_SIZE"]

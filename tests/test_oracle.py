@@ -390,6 +390,62 @@ def test_cache_write_then_attend_matches_contiguous():
         np.testing.assert_allclose(out[s], ref.reshape(Hq, D).numpy(), rtol=0, atol=1e-12)
 
 
+def test_copy_blocks_hand_values():
+    """Each value names its own (layer, block, kv) place, so after the copy
+    block 5 must read as block 2 and block 3 as block 0 in every layer; the
+    out-of-range pair and the src == dst pair change nothing."""
+    L, NB, B, Hkv, D = 2, 8, 16, 2, 4
+    pool = np.zeros((L, NB, 2, B, Hkv, D), dtype=np.float32)
+    for l in range(L):
+        for b in range(NB):
+            for kv in range(2):
+                pool[l, b, kv] = 1000 * l + 10 * b + kv
+    out = oracle.copy_blocks(pool, [2, 0, 9, 4], [5, 3, 1, 4])
+    src_of = {5: 2, 3: 0}
+    for l in range(L):
+        for b in range(NB):
+            for kv in range(2):
+                assert np.all(out[l, b, kv] == 1000 * l + 10 * src_of.get(b, b) + kv)
+    assert pool[0, 5, 0, 0, 0, 0] == 50  # the input is not modified
+
+
+def test_copy_on_write_then_append_matches_private_history():
+    """Two sequences share a partially filled last block ([Optimizing]
+    Copy-on-Write: parallel samples share blocks until one writes).  The
+    writer gets a copy of the shared block, its table is repointed, and its
+    new token goes into the copy: its attention then equals attention over
+    its own contiguous history, and the other sequence's is unchanged."""
+    rng = np.random.default_rng(7)
+    B, Hkv, D, Hq = 16, 2, 8, 4
+    NB = 6
+    pool = np.full((1, NB, 2, B, Hkv, D), np.nan, dtype=np.float32)
+    ctx = 20  # blocks [1, 4]; block 4 holds 4 tokens, shared by both sequences
+    hist = rng.standard_normal((2, ctx, Hkv, D)).astype(np.float32)
+    for i in range(ctx):
+        blk = [1, 4][i // B]
+        pool[0, blk, :, i % B] = hist[:, i]
+    k_new = rng.standard_normal((1, Hkv, D)).astype(np.float32)
+    v_new = rng.standard_normal((1, Hkv, D)).astype(np.float32)
+    q = rng.standard_normal((2, Hq, D)).astype(np.float32)
+    # copy-on-write: sequence 0 gets block 2, a copy of block 4, then appends
+    pool2 = oracle.copy_blocks(pool, [4], [2])
+    pool2 = oracle.cache_write(pool2, 0, k_new, v_new, np.array([2 * B + ctx % B], dtype=np.int32))
+    tables = np.array([[1, 2], [1, 4]], dtype=np.int32)
+    lens = np.array([ctx + 1, ctx], dtype=np.int32)
+    out = oracle.decode_attention(pool2, 0, q, tables, lens, 0, 0.5)
+    G = Hq // Hkv
+    for s, (K, V) in enumerate([
+            (np.concatenate([hist[0], k_new]), np.concatenate([hist[1], v_new])),
+            (hist[0], hist[1])]):
+        qt = torch.from_numpy(op.to_f64(q[s])).reshape(1, Hq, 1, D)
+        kt = torch.from_numpy(op.to_f64(K)).permute(1, 0, 2).repeat_interleave(G, 0).unsqueeze(0).contiguous()
+        vt = torch.from_numpy(op.to_f64(V)).permute(1, 0, 2).repeat_interleave(G, 0).unsqueeze(0).contiguous()
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=0.5)
+        np.testing.assert_allclose(out[s], ref.reshape(Hq, D).numpy(), rtol=0, atol=1e-12)
+    # the shared block itself is untouched
+    assert pool2[0, 4].tobytes() == pool[0, 4].tobytes()
+
+
 # ---------------------------------------------------------------------------
 # planted mistakes: each must fail a pin that does not use the oracle's own code
 
