@@ -34,8 +34,9 @@ sys.path.insert(0, ROOT)
 METRIC = "paged decode attention: achieved HBM GB/s (% of peak) + seq·layer steps/s"
 HBM_PEAK_GBS = 8000.0
 DEFAULT_LAYERS = {1: 1, 2: 2, 3: 1, 4: 4, 5: 2}  # layer slices so that each step reads >= ~1 GB
-KERNEL_SOURCES = ("decode_stream.hip", "decode_mfma.hip", "decode_valu.hip", "decode_reduce.hip", "cache_write.hip",
-                  "mfma_tile.h", "decode_common.h", "internal.h", "kvpool_api.cpp")
+KERNEL_SOURCES = ("decode_stream.hip", "decode_prefix.hip", "copy_blocks.hip", "decode_mfma.hip", "decode_valu.hip",
+                  "decode_reduce.hip", "cache_write.hip", "mfma_tile.h", "decode_common.h", "internal.h",
+                  "kvpool_api.cpp")
 
 
 def log(*a):
@@ -142,6 +143,8 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=None, help="layer slices to rotate over")
     ap.add_argument("--variant", default="auto", choices=["auto", "stream", "mfma", "valu"])
     ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--no-shared-prefix", action="store_true",
+                    help="do not pass the batch's shared prefix (cascade) to the library")
     ap.add_argument("--unfused", action="store_true",
                     help="time cache_write and paged_decode_attention as two calls instead of paged_decode_step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -163,6 +166,7 @@ def main() -> int:
 
     import workloads as W
     from paged_kv_cache_37_amd import ops
+    from paged_kv_cache_37_amd.blockpool import shared_prefix_blocks
 
     dev = torch.device("cuda:0")
     L = args.layers or DEFAULT_LAYERS[args.config]
@@ -190,6 +194,9 @@ def main() -> int:
     lens = torch.from_numpy(w.seq_lens_after).to(dev)
     out = torch.empty_like(q)
     ws = ops.make_workspace(pool, w.num_seqs, w.num_q_heads, tables.shape[1], args.partition_tokens)
+    # blocks every row shares (a cached prompt prefix): attended once for the batch
+    shared = 0 if args.no_shared_prefix else shared_prefix_blocks(np.asarray(w.block_tables_after), w.seq_lens_after)
+    log(f"shared prefix: {shared} blocks")
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
 
@@ -199,12 +206,12 @@ def main() -> int:
     def attend(layer):
         ops.paged_decode_attention(pool, layer, q, tables, lens, w.scale, out=out, sliding_window=w.window,
                                    partition_tokens=args.partition_tokens, variant=args.variant, workspace=ws,
-                                   stream=stream)
+                                   stream=stream, shared_prefix_blocks=shared)
 
     def fused(layer):
         ops.paged_decode_step(pool, layer, q, tables, lens, w.scale, k_new, v_new, slots, out=out,
                               sliding_window=w.window, partition_tokens=args.partition_tokens, variant=args.variant,
-                              workspace=ws, stream=stream)
+                              workspace=ws, stream=stream, shared_prefix_blocks=shared)
 
     def step(i):
         if args.unfused:
@@ -300,6 +307,7 @@ def main() -> int:
             "variant": variant,
             "partition_tokens": args.partition_tokens,
             "fused_step": not args.unfused,
+            "shared_prefix_blocks": shared,
             "seed": w.seed,
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),

@@ -171,6 +171,9 @@ typedef struct {
   int32_t variant;              /* kvp_variant                                  */
   void* workspace;              /* device scratch, may be NULL if not needed    */
   size_t workspace_bytes;
+  int32_t shared_prefix_blocks; /* 0, or: the first this-many entries of every
+                                   row are the same full blocks (a shared
+                                   prompt prefix); see paged_decode_attention */
 } kvp_decode_args;
 
 /*
@@ -215,6 +218,21 @@ size_t paged_decode_workspace_bytes(kvp_pool pool, int32_t num_seqs, int32_t num
  *   KVP_ERR_WORKSPACE_TOO_SMALL, KVP_ERR_HIP.
  */
 int32_t paged_decode_attention(kvp_pool pool, const kvp_decode_args* args, hipStream_t stream);
+/*
+ *   Shared prefix (cascade).  shared_prefix_blocks = P > 0 promises that the
+ *   first P entries of every row are the same physical blocks, all full and
+ *   all attended (seq_lens[s] >= 16 P): a prompt prefix that every sequence
+ *   of the batch reuses ([Pool] "Finding a prefix again"; [Memory] "How
+ *   vLLM recognizes a reusable prefix": only full blocks are shared).  The
+ *   STREAM variant then attends the prefix once per KV head for all
+ *   sequences (a dense pass whose MFMA columns are 16 query rows of any
+ *   sequences), streams only the private tails, and merges the two; the
+ *   result is the same attention up to fp32 rounding.  Other variants, and
+ *   rows with a sliding window, ignore the hint.  P must be <=
+ *   max_blocks_per_seq (KVP_ERR_INVALID_ARG otherwise); if the promise does
+ *   not hold the outputs are unspecified (memory is still only read inside
+ *   the pool and the table rows).
+ */
 
 /*
  * paged_decode_step -- one decode step of one layer: store each sequence's

@@ -71,6 +71,7 @@ class DecodeArgs(ctypes.Structure):
         ("variant", ctypes.c_int32),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
+        ("shared_prefix_blocks", ctypes.c_int32),
     ]
 
 

@@ -409,3 +409,21 @@ def reservation_waste(used_tokens: int, reserved_tokens: int) -> float:
 def paging_waste_slots(num_tokens: int, block_size: int = 16) -> int:
     """Slots left empty in a request's last block."""
     return (-num_tokens) % block_size
+
+
+def shared_prefix_blocks(rows: Sequence[Sequence[int]], seq_lens: Sequence[int], block_size: int = 16) -> int:
+    """Leading table entries that name the same physical block in every row
+    and are full, attended blocks in every sequence: the part of a batch's
+    context that decode attention can read once for all of its sequences
+    (paged_decode_attention's shared_prefix_blocks).  Requests that found a
+    cached prefix share its blocks ([Pool] "Finding a prefix again"), and
+    only full blocks are shared ([Memory] "How vLLM recognizes a reusable
+    prefix")."""
+    if len(rows) == 0:
+        return 0
+    n = min(min(len(r) for r in rows), min(int(c) // block_size for c in seq_lens))
+    first = rows[0]
+    k = 0
+    while k < n and all(int(r[k]) == int(first[k]) for r in rows):
+        k += 1
+    return k

@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
     for (int i = 0; i < per; ++i) {
       const int s = s0 + i;
       if (s < S) {
-        const int nb = row_span(P.seq_lens[s], P.window, P.max_blocks).nblocks;
+        const int nb = max(row_span(P.seq_lens[s], P.window, P.max_blocks).nblocks - P.prefix_blocks, 0);
         pre[s + 1] = nb;
         local += nb;
       }
@@ -118,9 +118,10 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
   const long long T = (long long)per_row * HG;
 
   if (blockIdx.x == 0) {
-    // publish the prefix sums for the merge pass; zero the rows of empty sequences
+    // publish the prefix sums for the merge pass; zero the rows of empty
+    // sequences (with a shared prefix the merge pass writes every row)
     for (int i = threadIdx.x; i <= S; i += kThreads) P.prefix[i] = pre[i];
-    for (int s = 0; s < S; ++s)
+    for (int s = 0; s < S && P.prefix_blocks == 0; ++s)
       if (pre[s + 1] == pre[s])
         for (int i = threadIdx.x; i < P.num_q_heads * D; i += kThreads)
           ((uint16_t*)P.out)[(size_t)s * P.num_q_heads * D + i] = 0;
@@ -165,12 +166,12 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
   RowCtx ir = row_at(t_begin);  // row of the next tile to issue
   int ij = (int)(t_begin - ir.a);
   int irow_id = 0;
-  const int32_t* irow = P.block_tables + (size_t)ir.s * P.max_blocks;
+  const int32_t* irow = P.block_tables + (size_t)ir.s * P.max_blocks + P.prefix_blocks;
   int ids_a = ij + lane < ir.nb ? irow[ij + lane] : 0;            // entries ij .. ij+63
   int ids_b = ij + 64 + lane < ir.nb ? irow[ij + 64 + lane] : 0;  // entries ij+64 .. ij+127
   int ids_base = ij;                                               // entry held by lane 0 of ids_a
   RowCtx nr = row_after(ir);                                       // the row after, prefetched
-  int ids_n = lane < nr.nb ? P.block_tables[(size_t)nr.s * P.max_blocks + lane] : 0;
+  int ids_n = lane < nr.nb ? P.block_tables[(size_t)nr.s * P.max_blocks + P.prefix_blocks + lane] : 0;
   MfmaLanes ila = mfma_lanes<D>(P.num_kv_heads, ir.hg / P.qgroups, lane);
   int issued = 0;
 
@@ -186,12 +187,12 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
       ir = nr;
       ij = 0;
       ++irow_id;
-      irow = P.block_tables + (size_t)ir.s * P.max_blocks;
+      irow = P.block_tables + (size_t)ir.s * P.max_blocks + P.prefix_blocks;
       ids_a = ids_n;
       ids_b = 64 + lane < ir.nb ? irow[64 + lane] : 0;
       ids_base = 0;
       nr = row_after(ir);
-      ids_n = lane < nr.nb ? P.block_tables[(size_t)nr.s * P.max_blocks + lane] : 0;
+      ids_n = lane < nr.nb ? P.block_tables[(size_t)nr.s * P.max_blocks + P.prefix_blocks + lane] : 0;
       ila = mfma_lanes<D>(P.num_kv_heads, ir.hg / P.qgroups, lane);
     } else if (ij - ids_base == 64) {  // next chunk of 64 entries: rotate, fetch the one after
       ids_a = ids_b;
@@ -228,7 +229,25 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
     const float l_tot = rows_sum(st.l_run);
     const int q4 = lane >> 4;
     const long long ra = cr.a, rb = cr.a + cr.nb;
-    if (ra >= t_begin && rb <= t_end) {
+    if (ra >= t_begin && rb <= t_end && P.prefix_blocks > 0) {
+      // a whole tail of a row with a shared prefix: its partial goes to the
+      // row's own slot, for the merge with the prefix pass
+      const size_t pbase = ((size_t)cr.hg * S + cr.s) * P.heads_per_wg;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int g = 4 * q4 + r4;
+        if (g < c_nh) {
+          float2* o = (float2*)(P.row_o + (pbase + g) * D);
+#pragma unroll
+          for (int m = 0; m < D / 32; ++m)
+            o[16 * m + (lane & 15)] = make_float2(st.acc[2 * m][r4], st.acc[2 * m + 1][r4]);
+        }
+      }
+      if (lane < c_nh) {
+        P.row_ml[(pbase + lane) * 2 + 0] = st.m_run;
+        P.row_ml[(pbase + lane) * 2 + 1] = l_tot;
+      }
+    } else if (ra >= t_begin && rb <= t_end) {
       // the whole row is here: normalise and store (two bf16 per store)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
@@ -348,10 +367,11 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
       for (int kk = 0; kk < D / 32; ++kk) q_next[kk] = g < nh_n ? *(const uint4_v*)(qp + 32 * kk) : uint4_v{0, 0, 0, 0};
       load_new(qn, kn_next, vn_next, slot_next);
     }
+    const int J = P.prefix_blocks + x.j;  // table entry of the tile
     if constexpr (FUSED) {
-      if (slot_c >= 0 && x.j == crs.nblocks - 1) put_new(x.t);
+      if (slot_c >= 0 && J == crs.nblocks - 1) put_new(x.t);
     }
-    st.step(x.t, x.j, crs.start_off, crs.start_off + crs.n, crs.nblocks, P.scale_log2, lane);
+    st.step(x.t, J, crs.start_off, crs.start_off + crs.n, crs.nblocks, P.scale_log2, lane);
   };
 
   StreamTile<D> buf[NBUF];
@@ -377,6 +397,10 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
 // w_last; each left its partial in slot 0 (the row held the wave's first
 // tile) or slot 1 (the row was the wave's last).  Rows inside one wave were
 // stored by the first pass.  The partials' loads go out eight at a time.
+// With a shared prefix every row is merged here: the prefix pass's piece,
+// then either the row's own slot (a tail inside one wave) or the wave
+// slots (a tail cut by range boundaries); a row with no tail is the prefix
+// piece alone.
 template <int D>
 __global__ __launch_bounds__(256) void decode_stream_reduce_kernel(const DecodeParams P) {
   const int s = blockIdx.y;
@@ -384,51 +408,85 @@ __global__ __launch_bounds__(256) void decode_stream_reduce_kernel(const DecodeP
   if (h >= P.num_q_heads) return;
   const int lane = threadIdx.x & 63;
   const int S = P.num_seqs;
-  const int pre_s = P.prefix[s], nb = P.prefix[s + 1] - pre_s, per_row = P.prefix[S];
-  if (nb == 0) return;
+  const bool cascade = P.prefix_blocks > 0;
   const int kvh = h / P.group, g_in = h - kvh * P.group;
   const int qg = g_in / P.heads_per_wg, hh = g_in - qg * P.heads_per_wg;
   const int hg = kvh * P.qgroups + qg;
-  const long long T = (long long)per_row * P.num_kv_heads * P.qgroups;
-  const long long W = (long long)P.stream_wgs * kWaves;
-  const long long a = (long long)hg * per_row + pre_s, b = a + nb;
-  const long long w_first = floor_div((a + 1) * W - 1, T), w_last = floor_div(b * W - 1, T);
-  if (w_first == w_last) return;
 
   constexpr int PER = D / 64;
-  constexpr int CH = 8;
   float M = -INFINITY, den = 0.f, num[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) num[e] = 0.f;
-  for (long long w0 = w_first; w0 <= w_last; w0 += CH) {
-    float m[CH], l[CH], v[CH][PER];
+  // With a shared prefix, the prefix pass's piece and the row's own slot
+  // do not depend on the prefix sums: their loads go out with them.
+  float rm = -INFINITY, rl = 0.f, ro[PER];
+  if (cascade) {
+    const size_t qh = (size_t)s * P.num_q_heads + h;
+    const size_t rb = ((size_t)hg * S + s) * P.heads_per_wg + hh;
+    M = P.pre_ml[qh * 2];
+    den = P.pre_ml[qh * 2 + 1];
+    rm = P.row_ml[rb * 2];
+    rl = P.row_ml[rb * 2 + 1];
 #pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      const long long w = w0 + u <= w_last ? w0 + u : w_last;
-      const long long start = floor_div(w * T, W), stop = floor_div((w + 1) * T, W);
-      const bool use = w0 + u <= w_last && start < stop;  // empty ranges leave no partial
-      const size_t pb = (size_t)(w * 2 + (start >= a ? 0 : 1)) * P.heads_per_wg + hh;
-      m[u] = use ? P.part_ml[pb * 2] : -INFINITY;
-      l[u] = use ? P.part_ml[pb * 2 + 1] : 0.f;
-#pragma unroll
-      for (int e = 0; e < PER; ++e) v[u][e] = use ? P.part_o[pb * D + lane + 64 * e] : 0.f;
+    for (int e = 0; e < PER; ++e) {
+      num[e] = P.pre_o[qh * D + lane + 64 * e];
+      ro[e] = P.row_o[rb * D + lane + 64 * e];
     }
-    float Mc = M;
+  }
+  const int pre_s = P.prefix[s], nb = P.prefix[s + 1] - pre_s, per_row = P.prefix[S];
+  if (nb == 0 && !cascade) return;
+  // merge one more piece (max m, sum l, unnormalised o)
+  auto add = [&](float m, float l, const float* o) {
+    const float Mc = fmaxf(M, m);
+    if (Mc == -INFINITY) return;
+    const float a = __builtin_amdgcn_exp2f(M - Mc), b = __builtin_amdgcn_exp2f(m - Mc);
+    den = den * a + l * b;
 #pragma unroll
-    for (int u = 0; u < CH; ++u) Mc = fmaxf(Mc, m[u]);
-    if (Mc == -INFINITY) continue;
-    const float ao = __builtin_amdgcn_exp2f(M - Mc);
-    den *= ao;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) num[e] *= ao;
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      const float f = __builtin_amdgcn_exp2f(m[u] - Mc);
-      den += f * l[u];
-#pragma unroll
-      for (int e = 0; e < PER; ++e) num[e] += f * v[u][e];
-    }
+    for (int e = 0; e < PER; ++e) num[e] = num[e] * a + o[e] * b;
     M = Mc;
+  };
+
+  if (nb > 0) {
+    const long long T = (long long)per_row * P.num_kv_heads * P.qgroups;
+    const long long W = (long long)P.stream_wgs * kWaves;
+    const long long a = (long long)hg * per_row + pre_s, b = a + nb;
+    const long long w_first = floor_div((a + 1) * W - 1, T), w_last = floor_div(b * W - 1, T);
+    if (w_first == w_last) {
+      if (!cascade) return;  // stored by the first pass
+      add(rm, rl, ro);       // the tail one wave held whole
+    } else {
+      constexpr int CH = 8;
+      for (long long w0 = w_first; w0 <= w_last; w0 += CH) {
+        float m[CH], l[CH], v[CH][PER];
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+          const long long w = w0 + u <= w_last ? w0 + u : w_last;
+          const long long start = floor_div(w * T, W), stop = floor_div((w + 1) * T, W);
+          const bool use = w0 + u <= w_last && start < stop;  // empty ranges leave no partial
+          const size_t pb = (size_t)(w * 2 + (start >= a ? 0 : 1)) * P.heads_per_wg + hh;
+          m[u] = use ? P.part_ml[pb * 2] : -INFINITY;
+          l[u] = use ? P.part_ml[pb * 2 + 1] : 0.f;
+#pragma unroll
+          for (int e = 0; e < PER; ++e) v[u][e] = use ? P.part_o[pb * D + lane + 64 * e] : 0.f;
+        }
+        float Mc = M;
+#pragma unroll
+        for (int u = 0; u < CH; ++u) Mc = fmaxf(Mc, m[u]);
+        if (Mc == -INFINITY) continue;
+        const float ao = __builtin_amdgcn_exp2f(M - Mc);
+        den *= ao;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) num[e] *= ao;
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+          const float f = __builtin_amdgcn_exp2f(m[u] - Mc);
+          den += f * l[u];
+#pragma unroll
+          for (int e = 0; e < PER; ++e) num[e] += f * v[u][e];
+        }
+        M = Mc;
+      }
+    }
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
   uint16_t* out = (uint16_t*)P.out + ((size_t)s * P.num_q_heads + h) * D;
@@ -438,6 +496,10 @@ __global__ __launch_bounds__(256) void decode_stream_reduce_kernel(const DecodeP
 
 template <int D, int DEPTH>
 hipError_t launch_sd(const DecodeParams& p, hipStream_t stream) {
+  if (p.prefix_blocks > 0) {
+    const hipError_t e = launch_decode_prefix(p, D, stream);
+    if (e != hipSuccess) return e;
+  }
   if (p.slot_mapping)
     hipLaunchKernelGGL((decode_stream_kernel<D, DEPTH, true>), dim3(p.stream_wgs), dim3(kThreads), 0, stream, p);
   else

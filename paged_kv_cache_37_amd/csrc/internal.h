@@ -11,6 +11,7 @@ constexpr int kBlock = 16;      // tokens per block (the pages' default block si
 constexpr int kWaves = 4;       // waves per decode workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxStreamSeqs = 4096;  // sequences one streaming launch can take (LDS prefix sums)
+constexpr int kMaxPrefixBlocks = 4096;  // shared-prefix blocks one prefix pass takes (LDS block ids)
 
 // Geometry and arguments of one decode launch, resolved on the host.
 struct DecodeParams {
@@ -39,6 +40,11 @@ struct DecodeParams {
   const void* k_new;            // [S][Hkv][D] new token per sequence        (fused write only)
   const void* v_new;            // [S][Hkv][D]                               (fused write only)
   const int32_t* slot_mapping;  // [S]; NULL: attention only                 (fused write only)
+  int32_t prefix_blocks;        // table entries every row shares (cascade); 0: none   (streaming only)
+  float* pre_o;                 // [S][Hq][D] prefix pass: unnormalised output         (cascade only)
+  float* pre_ml;                // [S][Hq][2] prefix pass: (max, sum)                  (cascade only)
+  float* row_o;                 // [rows][heads_per_wg][D] tails held whole by a wave  (cascade only)
+  float* row_ml;                // [rows][heads_per_wg][2]                             (cascade only)
 };
 
 // Span of one block-table row: leading slots of the first block that are
@@ -73,6 +79,7 @@ hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int head_dim, hi
 hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeParams& p, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_decode_stream(const DecodeParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_decode_prefix(const DecodeParams& p, int head_dim, hipStream_t stream);
 const void* stream_kernel_symbol(int head_dim, int depth, bool fused);
 
 }  // namespace kvp

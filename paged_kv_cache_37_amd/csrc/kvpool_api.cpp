@@ -270,24 +270,38 @@ static size_t grid_workspace(const kvp::DecodeParams& p, int32_t head_dim, size_
 }
 
 // Workspace of the streaming kernel: prefix sums, then two partial slots per
-// wave for up to heads_per_wg heads: (max, sum) pairs and outputs.
-static size_t stream_workspace(const kvp::DecodeParams& p, int32_t head_dim, size_t* ml_off, size_t* o_off) {
+// wave for up to heads_per_wg heads ((max, sum) pairs and outputs), then the
+// shared-prefix pieces: one per (sequence, query head) from the prefix pass
+// and one per (row, head) for tails a single wave holds.
+struct StreamLayout {
+  size_t ml, o, pre_ml, pre_o, row_ml, row_o, total;
+};
+
+static StreamLayout stream_workspace(const kvp::DecodeParams& p, int32_t head_dim) {
+  StreamLayout L;
   const size_t slots = (size_t)p.stream_wgs * kvp::kWaves * 2 * p.heads_per_wg;
-  *ml_off = align256((size_t)(p.num_seqs + 1) * sizeof(int32_t));
-  *o_off = *ml_off + align256(slots * 2 * sizeof(float));
-  return *o_off + slots * head_dim * sizeof(float);
+  const size_t qh = (size_t)p.num_seqs * p.num_q_heads;
+  const size_t rows = (size_t)p.num_kv_heads * p.qgroups * p.num_seqs * p.heads_per_wg;
+  L.ml = align256((size_t)(p.num_seqs + 1) * sizeof(int32_t));
+  L.o = L.ml + align256(slots * 2 * sizeof(float));
+  L.pre_ml = L.o + align256(slots * head_dim * sizeof(float));
+  L.pre_o = L.pre_ml + align256(qh * 2 * sizeof(float));
+  L.row_ml = L.pre_o + align256(qh * head_dim * sizeof(float));
+  L.row_o = L.row_ml + align256(rows * 2 * sizeof(float));
+  L.total = L.row_o + rows * head_dim * sizeof(float);
+  return L;
 }
 
 size_t paged_decode_workspace_bytes(kvp_pool pool, int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
                                     int32_t partition_tokens) {
   if (!pool) return 0;
   // enough for every variant that could run with these sizes
-  size_t need = 0, a, b;
+  size_t need = 0, a;
   for (int32_t v : {KVP_VARIANT_VALU, KVP_VARIANT_MFMA, KVP_VARIANT_STREAM}) {
     kvp::DecodeParams p;
     int32_t path;
     if (plan(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, v, &p, &path) != KVP_OK) continue;
-    const size_t n = path == PATH_STREAM ? stream_workspace(p, pool->desc.head_dim, &a, &b)
+    const size_t n = path == PATH_STREAM ? stream_workspace(p, pool->desc.head_dim).total
                                          : grid_workspace(p, pool->desc.head_dim, &a);
     if (n > need) need = n;
   }
@@ -329,9 +343,15 @@ static int32_t decode(kvp_pool pool, const kvp_decode_args* a, const void* k_new
     p.v_new = v_new;
     p.slot_mapping = slots;
   }
-  size_t ml_off = 0, o_off = 0;
-  const size_t ws = path == PATH_STREAM ? stream_workspace(p, d.head_dim, &ml_off, &o_off)
-                                        : grid_workspace(p, d.head_dim, &ml_off);
+  if (a->shared_prefix_blocks < 0 || a->shared_prefix_blocks > a->max_blocks_per_seq)
+    return fail(KVP_ERR_INVALID_ARG, "shared_prefix_blocks must be in [0, max_blocks_per_seq]");
+  // the shared-prefix pass is a STREAM feature for full-context rows; elsewhere the hint is ignored
+  // (a shorter hint is as valid as the full one: longer prefixes use the first kMaxPrefixBlocks)
+  if (path == PATH_STREAM && a->sliding_window == 0)
+    p.prefix_blocks = a->shared_prefix_blocks < kvp::kMaxPrefixBlocks ? a->shared_prefix_blocks : kvp::kMaxPrefixBlocks;
+  size_t ml_off = 0;
+  const StreamLayout SL = path == PATH_STREAM ? stream_workspace(p, d.head_dim) : StreamLayout{};
+  const size_t ws = path == PATH_STREAM ? SL.total : grid_workspace(p, d.head_dim, &ml_off);
   if (ws > 0) {
     if (!a->workspace || a->workspace_bytes < ws)
       return fail(KVP_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes needed (%zu given)", ws,
@@ -340,8 +360,12 @@ static int32_t decode(kvp_pool pool, const kvp_decode_args* a, const void* k_new
     char* w = (char*)a->workspace;
     if (path == PATH_STREAM) {
       p.prefix = (int32_t*)w;
-      p.part_ml = (float*)(w + ml_off);
-      p.part_o = (float*)(w + o_off);
+      p.part_ml = (float*)(w + SL.ml);
+      p.part_o = (float*)(w + SL.o);
+      p.pre_ml = (float*)(w + SL.pre_ml);
+      p.pre_o = (float*)(w + SL.pre_o);
+      p.row_ml = (float*)(w + SL.row_ml);
+      p.row_o = (float*)(w + SL.row_o);
     } else {
       p.part_o = (float*)w;
       p.part_ml = (float*)(w + ml_off);

@@ -292,13 +292,17 @@ def _scattered(config, seed, rng, ctx, Hq, Hkv, D, window, L) -> Workload:
     return w
 
 
-def config4(seed: int = 4, num_layers: int = 1, num_seqs: int = 256) -> Workload:
-    """Shared 2048-token prefix (128 blocks, same physical ids in every row)
-    plus a private tail per sequence whose last block is partial."""
-    rng = np.random.default_rng(seed)
-    tails_allowed = np.array([t for t in range(1, 513) if t % BLOCK_SIZE != 0])
-    tails = rng.choice(tails_allowed, size=num_seqs)
-    prefix_blocks = 2048 // BLOCK_SIZE
+def shared_prefix(seed: int, prefix_tokens: int, tails, num_q_heads: int = 32, num_kv_heads: int = 8,
+                  head_dim: int = 128, num_layers: int = 1, config: int = 0, rng=None) -> Workload:
+    """bf16 batch whose rows all start with the same prefix_tokens / 16 full
+    blocks (the same physical ids in every row) followed by a private tail
+    of tails[s] tokens (0 = the prefix alone); physical ids are a seeded
+    permutation of a pool 1.25x the unique blocks."""
+    if prefix_tokens % BLOCK_SIZE:
+        raise ValueError("the shared prefix is a whole number of blocks")
+    rng = np.random.default_rng(seed) if rng is None else rng
+    tails = np.asarray(tails, dtype=np.int64)
+    prefix_blocks = prefix_tokens // BLOCK_SIZE
     tail_blocks = [(int(t) + BLOCK_SIZE - 1) // BLOCK_SIZE for t in tails]
     unique = prefix_blocks + sum(tail_blocks)
     NB = math.ceil(1.25 * unique)
@@ -308,12 +312,21 @@ def config4(seed: int = 4, num_layers: int = 1, num_seqs: int = 256) -> Workload
     for nb in tail_blocks:
         rows.append(prefix + list(perm[k:k + nb]))
         k += nb
-    ctx = 2048 + tails
-    w = _base(4, seed, "bf16", num_layers, NB, 32, 8, 128, 0, ctx)
-    w.pool = _draw_pool(seed, w.dtype, num_layers, NB, 8, 128, BLOCK_SIZE)
+    ctx = prefix_tokens + tails
+    w = _base(config, seed, "bf16", num_layers, NB, num_q_heads, num_kv_heads, head_dim, 0, ctx)
+    w.pool = _draw_pool(seed, w.dtype, num_layers, NB, num_kv_heads, head_dim, BLOCK_SIZE)
     _finish(w, rows)
     _draw_q(w)
     return w
+
+
+def config4(seed: int = 4, num_layers: int = 1, num_seqs: int = 256) -> Workload:
+    """Shared 2048-token prefix (128 blocks, same physical ids in every row)
+    plus a private tail per sequence whose last block is partial."""
+    rng = np.random.default_rng(seed)
+    tails_allowed = np.array([t for t in range(1, 513) if t % BLOCK_SIZE != 0])
+    tails = rng.choice(tails_allowed, size=num_seqs)
+    return shared_prefix(seed, 2048, tails, 32, 8, 128, num_layers, config=4, rng=rng)
 
 
 def make(config: int, seed: Optional[int] = None, num_layers: int = 1) -> Workload:
