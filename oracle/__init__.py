@@ -11,6 +11,8 @@ paged KV cache computes, in float64:
   mapping names (slot = physical block * block_size + offset);
 * ``copy_blocks`` -- the copy-on-write block copy: every layer's K and V of
   one physical block into another;
+* ``fp8`` -- the E4M3 codes of an FP8 KV cache: decode, encode (nearest,
+  ties to even, saturating) and the scaled quantization a write applies;
 * ``decode_attention`` -- for every sequence, walk its block table, gather
   its keys and values into contiguous arrays, and run softmax(q K^T scale) V
   for every query head;
@@ -50,6 +52,7 @@ softmax(q . K^T * scale) . V, with query head h reading KV head h // G
 Each function is pinned by ``tests/test_oracle.py`` against the pages'
 worked values, closed forms, invariants and an independent library routine.
 """
+from .fp8 import e4m3_decode, e4m3_encode, quantize  # noqa: F401
 from .paged import (  # noqa: F401
     cache_write,
     copy_blocks,

@@ -8,13 +8,17 @@ Pool layout consumed here is the block shape the pages print ([Paged]
 
     pool[layer, block, kv, slot, kv_head, dim]     kv: 0 = K, 1 = V
 
-bf16 pools arrive as uint16 bit patterns, fp32 pools as float32.
+bf16 pools arrive as uint16 bit patterns, fp32 pools as float32, FP8 pools
+as uint8 E4M3 codes with one (k_scale, v_scale) pair for the layer
+(``oracle.fp8``).
 """
 from __future__ import annotations
 
 import math
 
 import numpy as np
+
+from .fp8 import e4m3_decode, quantize
 
 
 # ---------------------------------------------------------------------------
@@ -23,9 +27,11 @@ import numpy as np
 
 def to_f64(x: np.ndarray) -> np.ndarray:
     """Exact widening to float64: uint16 arrays are bf16 bit patterns (a bf16
-    value is the upper half of the float32 with the same bits), float32 is
-    widened directly."""
+    value is the upper half of the float32 with the same bits), uint8 arrays
+    E4M3 codes (unscaled), float32 is widened directly."""
     x = np.asarray(x)
+    if x.dtype == np.uint8:
+        return e4m3_decode(x)
     if x.dtype == np.uint16:
         return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     if x.dtype in (np.float32, np.float64):
@@ -95,14 +101,18 @@ def check_tables(block_tables, seq_lens, window: int, block_size: int, num_block
 
 
 def cache_write(pool: np.ndarray, layer: int, k_new: np.ndarray, v_new: np.ndarray,
-                slot_mapping: np.ndarray) -> np.ndarray:
+                slot_mapping: np.ndarray, k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
     """Return a copy of `pool` with token t's K and V stored at slot
     slot_mapping[t] of `layer`: physical block slot // B, offset slot % B
     ([Optimizing] §The Block Manager and Dynamic Allocation Lifecycle: the
     kernel writes each token's key and value vectors into the physical
     block's free slot).  A negative slot is skipped (padding).  The copy is
-    bit for bit: no arithmetic touches the values."""
+    bit for bit: no arithmetic touches the values, except for an FP8 pool,
+    whose codes are the new values quantized with the layer's scales
+    (``oracle.fp8.quantize``)."""
     out = pool.copy()
+    if pool.dtype == np.uint8:
+        k_new, v_new = quantize(k_new, k_scale), quantize(v_new, v_scale)
     B = pool.shape[3]
     for t, slot in enumerate(np.asarray(slot_mapping)):
         slot = int(slot)
@@ -159,10 +169,12 @@ def softmax_weights(q_head: np.ndarray, K_head: np.ndarray, scale: float) -> np.
 
 
 def decode_attention_seq(pool: np.ndarray, layer: int, q_seq: np.ndarray, table_row,
-                         ctx: int, window: int, scale: float, heads=None) -> np.ndarray:
+                         ctx: int, window: int, scale: float, heads=None,
+                         k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
     """Output [Hq, D] (float64) of one sequence: gather its K/V by walking its
     table, then for each query head h, with G = Hq / Hkv and KV head h // G,
-    out_h = softmax(K q_h * scale) V."""
+    out_h = softmax(K q_h * scale) V.  The stored K and V are multiplied by
+    k_scale and v_scale first (FP8 pools; 1 otherwise)."""
     q = to_f64(q_seq)
     Hq, D = q.shape
     Hkv = pool.shape[4]
@@ -173,6 +185,7 @@ def decode_attention_seq(pool: np.ndarray, layer: int, q_seq: np.ndarray, table_
     if n == 0:
         return out
     K, V = gather_kv(pool, layer, table_row, start_off, n)
+    K, V = K * k_scale, V * v_scale
     for h in (range(Hq) if heads is None else heads):
         kv = h // G
         p = softmax_weights(q[h], K[:, kv, :], scale)
@@ -181,13 +194,13 @@ def decode_attention_seq(pool: np.ndarray, layer: int, q_seq: np.ndarray, table_
 
 
 def decode_attention(pool: np.ndarray, layer: int, q: np.ndarray, block_tables, seq_lens,
-                     window: int, scale: float) -> np.ndarray:
+                     window: int, scale: float, k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
     """Decode attention for every sequence: float64 [S, Hq, D]."""
     S = q.shape[0]
     out = np.zeros(q.shape, dtype=np.float64)
     for s in range(S):
         out[s] = decode_attention_seq(pool, layer, q[s], block_tables[s], int(seq_lens[s]),
-                                      window, scale)
+                                      window, scale, k_scale=k_scale, v_scale=v_scale)
     return out
 
 

@@ -511,3 +511,108 @@ def test_pins_pass_for_the_oracle():
                                   "head_modulo", "no_scale", "flip_sign", "no_normalise"])
 def test_planted_mistake_is_caught(kind):
     assert not _independent_pins_pass(_mutant(kind))
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) codes: pinned to the format's definition by worked values, not
+# by re-running the oracle's own formula
+
+
+def test_e4m3_known_codes():
+    """Values of E4M3 codes worked out by hand from the field layout (sign,
+    exponent bias 7, 3 mantissa bits, subnormals at exponent field 0)."""
+    known = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x0F: 1.875 * 2.0 ** -6,
+             0x30: 0.5, 0x38: 1.0, 0x39: 1.125, 0x3F: 1.875, 0x40: 2.0, 0x48: 4.0, 0x7E: 448.0,
+             0xB8: -1.0, 0xC0: -2.0, 0xFE: -448.0}
+    vals = oracle.e4m3_decode(np.array(list(known), dtype=np.uint8))
+    assert list(vals) == list(known.values())
+    neg_zero = oracle.e4m3_decode(np.array([0x80], np.uint8))[0]
+    assert neg_zero == 0.0 and np.signbit(neg_zero)
+    assert np.all(np.isnan(oracle.e4m3_decode(np.array([0x7F, 0xFF], np.uint8))))
+    pos = oracle.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0)  # codes 0..0x7E are the positive values in order
+
+
+def test_e4m3_encode_rounding_and_saturation():
+    codes = np.arange(256, dtype=np.uint8)
+    vals = oracle.e4m3_decode(codes)
+    finite = ~np.isnan(vals)
+    assert np.all(oracle.e4m3_encode(vals[finite]) == codes[finite])  # every code is its own nearest
+    # midpoints of consecutive positive codes go to the code with the even mantissa;
+    # a hair either side goes to the nearer one
+    for c in range(0, 0x7E):
+        lo, hi = vals[c], vals[c + 1]
+        mid = (lo + hi) / 2
+        even = c if c % 2 == 0 else c + 1
+        assert oracle.e4m3_encode(mid) == even, hex(c)
+        assert oracle.e4m3_encode(np.nextafter(mid, 0)) == c
+        assert oracle.e4m3_encode(np.nextafter(mid, np.inf)) == c + 1
+        assert oracle.e4m3_encode(-mid) == (even | 0x80)
+    # beyond the largest code: saturate
+    for x, c in ((448.0, 0x7E), (460.0, 0x7E), (464.0, 0x7E), (1e6, 0x7E), (np.inf, 0x7E), (-1e9, 0xFE)):
+        assert oracle.e4m3_encode(x) == c, x
+    assert oracle.e4m3_encode(2.0 ** -10) == 0x00       # tie between 0 and 2^-9: even
+    assert oracle.e4m3_encode(0.75 * 2.0 ** -9) == 0x01
+    assert oracle.e4m3_encode(-2.0 ** -12) == 0x80      # rounds to -0
+
+
+def test_fp8_quantize_uses_float32_product():
+    """quantize(x, s) encodes the float32 product x * float32(1/s): for s = 3,
+    1/s is not exact in float32 and 3 * fl(1/3) rounds to exactly 1."""
+    bits = W.f32_to_bf16_bits(np.array([3.0, 6.0, -0.75], dtype=np.float32))
+    assert list(oracle.quantize(bits, 3.0)) == [0x38, 0x40, 0xA8]   # 1.0, 2.0, -0.25
+    assert list(oracle.quantize(np.array([896.0], np.float32), 1.0)) == [0x7E]
+
+
+def test_fp8_cache_write_then_attend():
+    """An FP8 pool: the write stores quantized codes, attention reads codes
+    times the layer's scales; equals SDPA over the dequantized history."""
+    rng = np.random.default_rng(11)
+    B, Hkv, D, Hq = 16, 2, 16, 4
+    pool = np.full((1, 4, 2, B, Hkv, D), 0x7F, dtype=np.uint8)
+    codes = rng.integers(0, 0x7E, size=(2, 20, Hkv, D), dtype=np.uint8) | (rng.integers(0, 2, (2, 20, Hkv, D), dtype=np.uint8) << 7)
+    for i in range(20):
+        pool[0, [2, 0][i // B], :, i % B] = codes[:, i]
+    k_new = W.f32_to_bf16_bits(rng.standard_normal((1, Hkv, D)).astype(np.float32))
+    v_new = W.f32_to_bf16_bits(rng.standard_normal((1, Hkv, D)).astype(np.float32))
+    ks, vs = 0.37, 1.9
+    pool2 = oracle.cache_write(pool, 0, k_new, v_new, np.array([0 * B + 20 % B], np.int32), ks, vs)
+    assert np.all(pool2[0, 0, 0, 4] == oracle.quantize(k_new[0], ks))
+    assert np.all(pool2[0, 0, 1, 4] == oracle.quantize(v_new[0], vs))
+    q = rng.standard_normal((1, Hq, D)).astype(np.float32)
+    out = oracle.decode_attention(pool2, 0, q, np.array([[2, 0]], np.int32), np.array([21], np.int32), 0, 0.25,
+                                  k_scale=ks, v_scale=vs)
+    K = np.concatenate([oracle.e4m3_decode(codes[0]), oracle.e4m3_decode(oracle.quantize(k_new, ks))]) * ks
+    V = np.concatenate([oracle.e4m3_decode(codes[1]), oracle.e4m3_decode(oracle.quantize(v_new, vs))]) * vs
+    G = Hq // Hkv
+    qt = torch.from_numpy(q[0].astype(np.float64)).reshape(1, Hq, 1, D)
+    kt = torch.from_numpy(K).permute(1, 0, 2).repeat_interleave(G, 0).unsqueeze(0).contiguous()
+    vt = torch.from_numpy(V).permute(1, 0, 2).repeat_interleave(G, 0).unsqueeze(0).contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=0.25)
+    np.testing.assert_allclose(out[0], ref.reshape(Hq, D).numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("kind", ["ties_away", "truncate", "bias8", "no_saturation"])
+def test_planted_fp8_mistake_is_caught(kind):
+    """Plausible mistakes in an E4M3 encoder each break a worked value."""
+    def mutant(x):
+        x = np.asarray(x, dtype=np.float64)
+        if kind == "bias8":  # the variant with exponent bias 8 halves every value
+            return oracle.e4m3_encode(x * 2.0)
+        if kind == "no_saturation":
+            c = oracle.e4m3_encode(x)
+            return np.where(np.abs(x) > 448, 0x7F, c).astype(np.uint8)
+        a = np.abs(x)
+        _, E = np.frexp(a)
+        e = np.maximum(E - 1, -6)
+        q = np.ldexp(1.0, e - 3)
+        m = np.floor(a / q + 0.5) if kind == "ties_away" else np.floor(a / q)
+        return oracle.e4m3_encode(np.copysign(m * q, x))
+    vals = oracle.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))
+    mids = (vals[:-1] + vals[1:]) / 2
+    even = np.array([c if c % 2 == 0 else c + 1 for c in range(0x7E)], dtype=np.uint8)
+    ok_ties = np.all(mutant(mids) == even)
+    ok_sat = mutant(1e6) == 0x7E
+    ok_known = mutant(1.0) == 0x38
+    ok_above = np.all(mutant(np.nextafter(mids, np.inf)) == np.arange(1, 0x7F, dtype=np.uint8))
+    assert not (ok_ties and ok_sat and ok_known and ok_above)

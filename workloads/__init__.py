@@ -13,6 +13,10 @@ num_kv_heads, head_dim]`` with index 0 = K and 1 = V)::
 
 bf16 data is held as its raw 16-bit patterns (``np.uint16``) so that the
 oracle and the device see identical bytes; fp32 data is ``np.float32``.
+An "fp8" workload holds its pool as 8-bit E4M3 codes (``np.uint8``, drawn
+directly as codes: sign, exponent field 1..9 and mantissa uniform, i.e.
+magnitudes 2^-6 .. 7.5 before the per-layer scales k_scale and v_scale),
+and its queries and new tokens in bf16.
 Slots no sequence owns (unused blocks, the slots after a sequence's last
 token, and the slots before a sliding window's first position) hold NaN so
 that any read of them would show up in the results.
@@ -43,6 +47,7 @@ import numpy as np
 
 BLOCK_SIZE = 16
 BF16_NAN = np.uint16(0x7FC0)
+FP8_NAN = np.uint8(0x7F)  # the E4M3 NaN code
 
 _CONFIG_NAMES = {
     1: "tiny-fp32-S4-H8/2-D64",
@@ -57,7 +62,7 @@ _CONFIG_NAMES = {
 class Workload:
     config: int
     seed: int
-    dtype: str                 # "f32" or "bf16"
+    dtype: str                 # pool storage: "f32", "bf16" or "fp8" (E4M3 codes)
     num_layers: int
     num_blocks: int
     block_size: int
@@ -69,8 +74,8 @@ class Workload:
     seq_lens: np.ndarray       # int32 [S], absolute context length
     block_tables: np.ndarray   # int32 [S, W]; entries past row_blocks[s] are filler
     row_blocks: np.ndarray     # int32 [S], used entries of each row
-    pool: np.ndarray           # [L, NB, 2, B, Hkv, D]; uint16 (bf16 bits) or float32
-    q: np.ndarray              # [S, Hq, D]; same storage dtype as pool
+    pool: np.ndarray           # [L, NB, 2, B, Hkv, D]; uint16 (bf16 bits), float32 or uint8 (fp8 codes)
+    q: np.ndarray              # [S, Hq, D]; float32 for f32 pools, else bf16 bits
     # one next-token write per sequence (position seq_lens[s]); filled by with_next_token()
     k_new: Optional[np.ndarray] = None          # [T, Hkv, D]
     v_new: Optional[np.ndarray] = None          # [T, Hkv, D]
@@ -81,6 +86,8 @@ class Workload:
     unused_blocks: np.ndarray = field(default_factory=lambda: np.zeros(0, np.int32))
     owned_slots: int = 0       # distinct physical slots some sequence attends to
     name: str = ""
+    k_scale: float = 1.0       # fp8 pools: stored K code c means c * k_scale (float32-representable)
+    v_scale: float = 1.0       # fp8 pools: stored V code c means c * v_scale
 
     @property
     def num_seqs(self) -> int:
@@ -88,7 +95,13 @@ class Workload:
 
     @property
     def elt_bytes(self) -> int:
-        return 4 if self.dtype == "f32" else 2
+        """Bytes of one pool element."""
+        return {"f32": 4, "bf16": 2, "fp8": 1}[self.dtype]
+
+    @property
+    def act_dtype(self) -> str:
+        """Storage of queries, outputs and new tokens: fp32 or bf16."""
+        return "f32" if self.dtype == "f32" else "bf16"
 
     def valid_tokens(self) -> np.ndarray:
         """Keys each sequence attends to (the whole context, or the window)."""
@@ -141,7 +154,16 @@ def _store(x: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def _nan(dtype: str):
-    return np.float32("nan") if dtype == "f32" else BF16_NAN
+    return {"f32": np.float32("nan"), "bf16": BF16_NAN, "fp8": FP8_NAN}[dtype]
+
+
+def _draw_codes(seed: int, tag: int, shape) -> np.ndarray:
+    """E4M3 codes: sign, exponent field 1..9 and mantissa drawn uniformly."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, tag]))
+    sign = rng.integers(0, 2, size=shape, dtype=np.uint8)
+    expo = rng.integers(1, 10, size=shape, dtype=np.uint8)
+    mant = rng.integers(0, 8, size=shape, dtype=np.uint8)
+    return (sign << 7) | (expo << 3) | mant
 
 
 _POOL_CHUNK = 64  # physical blocks drawn per independent random stream
@@ -150,7 +172,7 @@ _POOL_CHUNK = 64  # physical blocks drawn per independent random stream
 def _draw_pool(seed: int, dtype: str, L: int, NB: int, Hkv: int, D: int, B: int) -> np.ndarray:
     """N(0,1) values for every slot of the pool, drawn in fixed chunks of
     physical blocks so the result does not depend on the thread count."""
-    storage = np.float32 if dtype == "f32" else np.uint16
+    storage = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[dtype]
     pool = np.empty((L, NB, 2, B, Hkv, D), dtype=storage)
     nchunks = (NB + _POOL_CHUNK - 1) // _POOL_CHUNK
 
@@ -158,8 +180,8 @@ def _draw_pool(seed: int, dtype: str, L: int, NB: int, Hkv: int, D: int, B: int)
         layer, c = job
         b0 = c * _POOL_CHUNK
         b1 = min(NB, b0 + _POOL_CHUNK)
-        vals = _normal_f32(seed, 1_000_003 * (layer + 1) + c, (b1 - b0, 2, B, Hkv, D))
-        pool[layer, b0:b1] = _store(vals, dtype)
+        tag, shape = 1_000_003 * (layer + 1) + c, (b1 - b0, 2, B, Hkv, D)
+        pool[layer, b0:b1] = _draw_codes(seed, tag, shape) if dtype == "fp8" else _store(_normal_f32(seed, tag, shape), dtype)
 
     jobs = [(layer, c) for layer in range(L) for c in range(nchunks)]
     with ThreadPoolExecutor(_threads()) as ex:
@@ -223,7 +245,7 @@ def _finish(w: Workload, rows, extra_cols: int = 1) -> Workload:
 
 
 def _base(config, seed, dtype, L, NB, Hq, Hkv, D, window, seq_lens) -> Workload:
-    return Workload(
+    w = Workload(
         config=config, seed=seed, dtype=dtype, num_layers=L, num_blocks=NB,
         block_size=BLOCK_SIZE, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
         window=window, scale=float(np.float32(1.0 / math.sqrt(D))),
@@ -231,10 +253,14 @@ def _base(config, seed, dtype, L, NB, Hq, Hkv, D, window, seq_lens) -> Workload:
         block_tables=np.zeros((0, 0), np.int32), row_blocks=np.zeros(0, np.int32),
         pool=np.zeros(0), q=np.zeros(0), name=_CONFIG_NAMES.get(config, f"custom-{config}"),
     )
+    if dtype == "fp8":
+        w.name += "-fp8"
+        w.k_scale, w.v_scale = float(np.float32(0.37)), float(np.float32(0.61))
+    return w
 
 
 def _draw_q(w: Workload) -> None:
-    w.q = _store(_normal_f32(w.seed, 7, (w.num_seqs, w.num_q_heads, w.head_dim)), w.dtype)
+    w.q = _store(_normal_f32(w.seed, 7, (w.num_seqs, w.num_q_heads, w.head_dim)), w.act_dtype)
 
 
 # ---------------------------------------------------------------------------
@@ -258,25 +284,25 @@ def config1(seed: int = 1) -> Workload:
     return with_next_token(w, list(perm[k:]))
 
 
-def config2(seed: int = 2, num_layers: int = 1) -> Workload:
+def config2(seed: int = 2, num_layers: int = 1, dtype: str = "bf16") -> Workload:
     rng = np.random.default_rng(seed)
     ctx = rng.integers(512, 4096, size=64, endpoint=True)
-    return _scattered(2, seed, rng, ctx, 32, 8, 128, 0, num_layers)
+    return _scattered(2, seed, rng, ctx, 32, 8, 128, 0, num_layers, dtype)
 
 
-def config3(seed: int = 3, num_layers: int = 1) -> Workload:
+def config3(seed: int = 3, num_layers: int = 1, dtype: str = "bf16") -> Workload:
     rng = np.random.default_rng(seed)
     ctx = np.full(128, 8192)
-    return _scattered(3, seed, rng, ctx, 64, 8, 128, 0, num_layers)
+    return _scattered(3, seed, rng, ctx, 64, 8, 128, 0, num_layers, dtype)
 
 
-def config5(seed: int = 5, num_layers: int = 1) -> Workload:
+def config5(seed: int = 5, num_layers: int = 1, dtype: str = "bf16") -> Workload:
     rng = np.random.default_rng(seed)
     ctx = rng.integers(4096, 32768, size=32, endpoint=True)
-    return _scattered(5, seed, rng, ctx, 32, 8, 128, 4096, num_layers)
+    return _scattered(5, seed, rng, ctx, 32, 8, 128, 4096, num_layers, dtype)
 
 
-def _scattered(config, seed, rng, ctx, Hq, Hkv, D, window, L) -> Workload:
+def _scattered(config, seed, rng, ctx, Hq, Hkv, D, window, L, dtype="bf16") -> Workload:
     spans = [_row_span(int(c), window, BLOCK_SIZE) for c in ctx]
     need = sum(nrow for _, nrow, _ in spans)
     NB = math.ceil(1.25 * need)
@@ -285,7 +311,7 @@ def _scattered(config, seed, rng, ctx, Hq, Hkv, D, window, L) -> Workload:
     for _, nrow, _ in spans:
         rows.append(list(perm[k:k + nrow]))
         k += nrow
-    w = _base(config, seed, "bf16", L, NB, Hq, Hkv, D, window, ctx)
+    w = _base(config, seed, dtype, L, NB, Hq, Hkv, D, window, ctx)
     w.pool = _draw_pool(seed, w.dtype, L, NB, Hkv, D, BLOCK_SIZE)
     _finish(w, rows)
     _draw_q(w)
@@ -293,7 +319,8 @@ def _scattered(config, seed, rng, ctx, Hq, Hkv, D, window, L) -> Workload:
 
 
 def shared_prefix(seed: int, prefix_tokens: int, tails, num_q_heads: int = 32, num_kv_heads: int = 8,
-                  head_dim: int = 128, num_layers: int = 1, config: int = 0, rng=None) -> Workload:
+                  head_dim: int = 128, num_layers: int = 1, config: int = 0, rng=None,
+                  dtype: str = "bf16") -> Workload:
     """bf16 batch whose rows all start with the same prefix_tokens / 16 full
     blocks (the same physical ids in every row) followed by a private tail
     of tails[s] tokens (0 = the prefix alone); physical ids are a seeded
@@ -313,29 +340,31 @@ def shared_prefix(seed: int, prefix_tokens: int, tails, num_q_heads: int = 32, n
         rows.append(prefix + list(perm[k:k + nb]))
         k += nb
     ctx = prefix_tokens + tails
-    w = _base(config, seed, "bf16", num_layers, NB, num_q_heads, num_kv_heads, head_dim, 0, ctx)
+    w = _base(config, seed, dtype, num_layers, NB, num_q_heads, num_kv_heads, head_dim, 0, ctx)
     w.pool = _draw_pool(seed, w.dtype, num_layers, NB, num_kv_heads, head_dim, BLOCK_SIZE)
     _finish(w, rows)
     _draw_q(w)
     return w
 
 
-def config4(seed: int = 4, num_layers: int = 1, num_seqs: int = 256) -> Workload:
+def config4(seed: int = 4, num_layers: int = 1, num_seqs: int = 256, dtype: str = "bf16") -> Workload:
     """Shared 2048-token prefix (128 blocks, same physical ids in every row)
     plus a private tail per sequence whose last block is partial."""
     rng = np.random.default_rng(seed)
     tails_allowed = np.array([t for t in range(1, 513) if t % BLOCK_SIZE != 0])
     tails = rng.choice(tails_allowed, size=num_seqs)
-    return shared_prefix(seed, 2048, tails, 32, 8, 128, num_layers, config=4, rng=rng)
+    return shared_prefix(seed, 2048, tails, 32, 8, 128, num_layers, config=4, rng=rng, dtype=dtype)
 
 
-def make(config: int, seed: Optional[int] = None, num_layers: int = 1) -> Workload:
+def make(config: int, seed: Optional[int] = None, num_layers: int = 1, dtype: str = "bf16") -> Workload:
+    """Workload `config` (1..5); configs 2..5 can hold their pool as fp8
+    codes instead of bf16 (dtype="fp8"), with the same shapes and tables."""
     seed = config if seed is None else seed
     if config == 1:
-        if num_layers != 1:
-            raise ValueError("config 1 has one layer")
+        if num_layers != 1 or dtype != "bf16":
+            raise ValueError("config 1 is one fp32 layer")
         return config1(seed)
-    return {2: config2, 3: config3, 4: config4, 5: config5}[config](seed, num_layers=num_layers)
+    return {2: config2, 3: config3, 4: config4, 5: config5}[config](seed, num_layers=num_layers, dtype=dtype)
 
 
 def custom(seed: int, ctx, num_q_heads: int, num_kv_heads: int, head_dim: int,
@@ -390,8 +419,8 @@ def with_next_token(w: Workload, fresh_blocks) -> Workload:
         slots[s] = row[lb] * B + pos % B
         new_first = _row_span(pos + 1, w.window, B)[0]
         rows.append(row[new_first - first_block:])
-    w.k_new = _store(_normal_f32(w.seed, 11, (T, w.num_kv_heads, w.head_dim)), w.dtype)
-    w.v_new = _store(_normal_f32(w.seed, 12, (T, w.num_kv_heads, w.head_dim)), w.dtype)
+    w.k_new = _store(_normal_f32(w.seed, 11, (T, w.num_kv_heads, w.head_dim)), w.act_dtype)
+    w.v_new = _store(_normal_f32(w.seed, 12, (T, w.num_kv_heads, w.head_dim)), w.act_dtype)
     w.slot_mapping = slots
     width = max(w.block_tables.shape[1], max(len(r) for r in rows))
     bt = np.full((T, width), w.block_tables[0, -1], dtype=np.int32)
