@@ -8,7 +8,7 @@ paged_decode_step call (the streaming kernel fuses the write), or with
 `--layers` layer slices of one pool so that the KV read each step is not
 served from the 256 MB last-level cache.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--kv-dtype bf16|fp8]
 
 Prints one JSON line.  `value` is the step's algorithmic bytes (K/V of the
 attended slots, each physical slot once, queries, outputs, tables, the
@@ -36,7 +36,7 @@ HBM_PEAK_GBS = 8000.0
 DEFAULT_LAYERS = {1: 1, 2: 2, 3: 1, 4: 4, 5: 2}  # layer slices so that each step reads >= ~1 GB
 KERNEL_SOURCES = ("decode_stream.hip", "decode_prefix.hip", "copy_blocks.hip", "decode_mfma.hip", "decode_valu.hip",
                   "decode_reduce.hip", "cache_write.hip", "mfma_tile.h", "decode_common.h", "internal.h",
-                  "kvpool_api.cpp")
+                  "fp8.h", "kvpool_api.cpp")
 
 
 def log(*a):
@@ -115,7 +115,7 @@ def cpu_baseline(w, budget_s: float = 10.0) -> dict:
         while time.perf_counter() - t0 < budget_s:
             for s in range(w.num_seqs):
                 oracle.decode_attention_seq(w.pool, 0, w.q[s], w.block_tables[s], int(w.seq_lens[s]), w.window,
-                                            w.scale)
+                                            w.scale, k_scale=w.k_scale, v_scale=w.v_scale)
                 done += 1
                 kv_bytes += int(valid[s]) * per_token
                 if time.perf_counter() - t0 > budget_s:
@@ -139,6 +139,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
+                    help="pool storage: bf16, or FP8 E4M3 codes with per-layer scales")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None, help="layer slices to rotate over")
     ap.add_argument("--variant", default="auto", choices=["auto", "stream", "mfma", "valu"])
@@ -169,14 +171,16 @@ def main() -> int:
     from paged_kv_cache_37_amd.blockpool import shared_prefix_blocks
 
     dev = torch.device("cuda:0")
-    L = args.layers or DEFAULT_LAYERS[args.config]
+    # an FP8 pool holds half the bytes per layer: twice the slices for the same footprint
+    L = args.layers or DEFAULT_LAYERS[args.config] * (2 if args.kv_dtype == "fp8" else 1)
     log(f"generating config {args.config} with {L} layer slice(s)")
     t0 = time.time()
-    w = W.make(args.config, args.seed, num_layers=L)
+    w = W.make(args.config, args.seed, num_layers=L, dtype=args.kv_dtype)
     W.with_next_token(w, w.unused_blocks)
     log(f"generated in {time.time() - t0:.1f}s: {w.name}, {w.num_blocks} blocks/layer")
 
-    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dt = torch.float32 if w.dtype == "f32" else torch.bfloat16  # queries, outputs, new tokens
+    pool_dt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[w.dtype]
 
     def up(a):
         a = np.ascontiguousarray(a)
@@ -184,9 +188,14 @@ def main() -> int:
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
 
-    pool = ops.KVPool(L, w.num_blocks, w.num_kv_heads, w.head_dim, dt, dev)
-    pool.load_logical(torch.from_numpy(w.pool.view(np.int16)).view(torch.bfloat16) if dt == torch.bfloat16
-                      else torch.from_numpy(w.pool))
+    pool = ops.KVPool(L, w.num_blocks, w.num_kv_heads, w.head_dim, pool_dt, dev)
+    if w.dtype == "bf16":
+        pool.load_logical(torch.from_numpy(w.pool.view(np.int16)).view(torch.bfloat16))
+    else:
+        pool.load_logical(torch.from_numpy(w.pool))  # float32 values or uint8 codes
+    if w.dtype == "fp8":
+        for layer in range(L):
+            pool.set_fp8_scales(layer, w.k_scale, w.v_scale)
     q = up(w.q)
     k_new, v_new = up(w.k_new), up(w.v_new)
     slots = torch.from_numpy(w.slot_mapping).to(dev)
@@ -262,13 +271,14 @@ def main() -> int:
     # block shared by many sequences is one physical block: HBM serves it
     # once), plus queries, outputs, table rows and lengths
     S, Hq, D, Hkv, eb = w.num_seqs, w.num_q_heads, w.head_dim, w.num_kv_heads, w.elt_bytes
+    ab = 4 if w.dtype == "f32" else 2  # bytes of a query, output or new-token element
     valid_after = np.minimum(w.seq_lens_after, w.window) if w.window else w.seq_lens_after
     per_token = 2 * Hkv * D * eb
     kv_logical = int(valid_after.astype(np.int64).sum()) * per_token
     kv_read = attended_slots(w) * per_token
-    other = 2 * S * Hq * D * eb + int(np.asarray(w.row_blocks_after).sum()) * 4 + S * 4
+    other = 2 * S * Hq * D * ab + int(np.asarray(w.row_blocks_after).sum()) * 4 + S * 4
     attn_bytes = kv_read + other
-    write_bytes = 2 * 2 * S * Hkv * D * eb + S * 4
+    write_bytes = 2 * S * Hkv * D * (ab + eb) + S * 4  # new K/V read, stored into the pool
     step_bytes = attn_bytes + write_bytes
     call_bytes = attn_bytes if args.unfused else step_bytes
     achieved = call_bytes / (call_ms * 1e-3) / 1e9
@@ -296,6 +306,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {
             "workload": w.name,
+            "kv_dtype": w.dtype,
             "num_seqs": S,
             "num_q_heads": Hq,
             "num_kv_heads": Hkv,

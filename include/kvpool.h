@@ -64,22 +64,33 @@ typedef enum {
   KVP_ERR_HIP = -4               /* the HIP runtime refused a launch */
 } kvp_status;
 
-typedef enum { KVP_F32 = 0, KVP_BF16 = 1 } kvp_dtype;
+/*
+ * Pool element types.  KVP_FP8_E4M3 stores each K/V value as one byte in
+ * the E4M3 format (sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+ * infinities, S.1111.111 = NaN, largest magnitude 448); a stored K code c
+ * means c * k_scale and a V code c means c * v_scale, one (k_scale,
+ * v_scale) per layer (kv_pool_set_fp8_scales).  [Optimizing] "The Math of
+ * the KV Cache Bottleneck": FP8 halves the bytes per element of BF16.
+ * Queries, outputs and new tokens stay BF16 with an FP8 pool.
+ */
+typedef enum { KVP_F32 = 0, KVP_BF16 = 1, KVP_FP8_E4M3 = 2 } kvp_dtype;
 
 /* Kernel variant for paged_decode_attention. */
 typedef enum {
-  KVP_VARIANT_AUTO = 0,   /* bf16: STREAM (MFMA with partition_tokens > 0 or
-                             more than 4096 sequences); fp32: VALU            */
-  KVP_VARIANT_VALU = 1,   /* vector ALU dot products, partitioned rows        */
+  KVP_VARIANT_AUTO = 0,   /* bf16/fp8: STREAM (MFMA with partition_tokens > 0
+                             or more than 4096 sequences); fp32: VALU         */
+  KVP_VARIANT_VALU = 1,   /* vector ALU dot products, partitioned rows
+                             (fp32 and bf16 pools)                            */
   KVP_VARIANT_MFMA = 2,   /* matrix cores for QK^T and PV, partitioned rows
-                             (bf16 only)                                      */
+                             (bf16 and fp8 pools)                             */
   KVP_VARIANT_STREAM = 3  /* matrix cores, persistent waves that split the
-                             batch's blocks evenly (bf16, <= 4096 sequences)  */
+                             batch's blocks evenly (bf16 and fp8 pools, <=
+                             4096 sequences)                                  */
 } kvp_variant;
 
 /*
  * Pool geometry.  block_size must be 16 (the pages' default block).
- * head_dim 64 or 128.  dtype KVP_F32 or KVP_BF16.
+ * head_dim 64 or 128.  dtype a kvp_dtype.
  */
 typedef struct {
   int32_t num_layers;
@@ -130,6 +141,16 @@ int32_t kv_pool_destroy(kvp_pool pool);
 int32_t kv_pool_describe(kvp_pool pool, kvp_pool_desc* desc);
 
 /*
+ * Scales of one layer of an FP8 pool: a K code c stands for c * k_scale, a
+ * V code for c * v_scale (both finite and > 0; 1.0 until set).  Writes
+ * quantize with them (cache_write, paged_decode_step), attention
+ * dequantizes with them; they apply to calls enqueued after this one.
+ * Errors: KVP_ERR_INVALID_ARG (layer, non-positive or non-finite scale),
+ * KVP_ERR_UNSUPPORTED (the pool is not FP8).
+ */
+int32_t kv_pool_set_fp8_scales(kvp_pool pool, int32_t layer, float k_scale, float v_scale);
+
+/*
  * Element offset (from dev_base) of K (kv = 0) or V (kv = 1) of
  * (layer, block, head, slot, dim), per the layout above; -1 if any index is
  * out of range.  Host-side helper for loaders and tests.
@@ -143,14 +164,18 @@ int64_t kv_pool_offset(kvp_pool pool, int32_t layer, int32_t block, int32_t kv, 
  *   prefill the kernel writes the prompt's K/V into the allocated blocks; in
  *   decode the new token's K/V go to the free slot of the last block.
  *
- *   k_new, v_new : device, [num_tokens][num_kv_heads][head_dim], pool dtype,
- *                  contiguous.
+ *   k_new, v_new : device, [num_tokens][num_kv_heads][head_dim], pool dtype
+ *                  (BF16 for an FP8 pool), contiguous.
  *   slot_mapping : device int32 [num_tokens]; slot = block * 16 + offset
  *                  ([Optimizing] "PagedAttention": floor(i/B), i mod B).
  *                  A negative slot (padding) writes nothing; a slot
  *                  >= num_blocks*16 writes nothing.  Two tokens naming the
  *                  same slot in one call leave that slot undefined.
- *   The copy is bit-exact.  num_tokens == 0 launches nothing.
+ *   The copy is bit-exact.  An FP8 pool stores codes instead: each value x
+ *   becomes the E4M3 code nearest to x * (1 / scale) (reciprocal and product
+ *   in float32, ties to the even code, magnitudes above 448 saturate to
+ *   448), with the layer's k_scale / v_scale.  num_tokens == 0 launches
+ *   nothing.
  */
 int32_t cache_write(kvp_pool pool, int32_t layer, const void* k_new, const void* v_new,
                     const int32_t* slot_mapping, int32_t num_tokens, hipStream_t stream);
@@ -158,7 +183,8 @@ int32_t cache_write(kvp_pool pool, int32_t layer, const void* k_new, const void*
 /* Arguments of paged_decode_attention (all device pointers caller-owned). */
 typedef struct {
   int32_t layer;
-  const void* q;                /* [num_seqs][num_q_heads][head_dim], pool dtype */
+  const void* q;                /* [num_seqs][num_q_heads][head_dim], pool dtype
+                                   (BF16 for an FP8 pool)                       */
   void* out;                    /* same shape and dtype as q                    */
   const int32_t* block_tables;  /* [num_seqs][max_blocks_per_seq]               */
   int32_t max_blocks_per_seq;   /* row stride of block_tables (>= 1)            */
@@ -201,7 +227,9 @@ size_t paged_decode_workspace_bytes(kvp_pool pool, int32_t num_seqs, int32_t num
  *
  *   out[s][h] = sum_i p_i V_i with p = softmax(K q[s][h] * scale) over the
  *   attended keys of KV head h / G; fp32 accumulation, output rounded to
- *   the pool dtype (round to nearest even for bf16).
+ *   the query dtype (round to nearest even for bf16).  With an FP8 pool,
+ *   K and V are the stored codes times the layer's k_scale and v_scale
+ *   (variants STREAM and MFMA).
  *
  *   Long rows are split into partitions of partition_tokens table slots;
  *   each partition leaves its partial result (running max, sum and

@@ -66,4 +66,6 @@ def quantize(x, scale: float) -> np.ndarray:
     if x.dtype == np.uint16:
         x = (x.astype(np.uint32) << 16).view(np.float32)
     inv = np.float32(1.0) / np.float32(scale)
-    return e4m3_encode((x.astype(np.float32) * inv).astype(np.float32))
+    with np.errstate(over="ignore"):  # a product past float32's range is inf and saturates
+        y = (x.astype(np.float32) * inv).astype(np.float32)
+    return e4m3_encode(y)

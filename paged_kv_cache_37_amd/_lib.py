@@ -22,6 +22,7 @@ KVP_ERR_HIP = -4
 
 KVP_F32 = 0
 KVP_BF16 = 1
+KVP_FP8_E4M3 = 2
 
 KVP_VARIANT_AUTO = 0
 KVP_VARIANT_VALU = 1
@@ -33,6 +34,7 @@ EXPORTS = (
     "kv_pool_create",
     "kv_pool_destroy",
     "kv_pool_describe",
+    "kv_pool_set_fp8_scales",
     "kv_pool_offset",
     "cache_write",
     "paged_decode_workspace_bytes",
@@ -87,6 +89,7 @@ def _load() -> ctypes.CDLL:
         "kv_pool_create": (i32, [ctypes.POINTER(PoolDesc), P, ctypes.c_size_t, ctypes.POINTER(P)]),
         "kv_pool_destroy": (i32, [P]),
         "kv_pool_describe": (i32, [P, ctypes.POINTER(PoolDesc)]),
+        "kv_pool_set_fp8_scales": (i32, [P, i32, ctypes.c_float, ctypes.c_float]),
         "kv_pool_offset": (ctypes.c_int64, [P, i32, i32, i32, i32, i32, i32]),
         "cache_write": (i32, [P, i32, P, P, P, i32, P]),
         "paged_decode_workspace_bytes": (ctypes.c_size_t, [P, i32, i32, i32, i32]),

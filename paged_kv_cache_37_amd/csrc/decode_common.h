@@ -59,8 +59,9 @@ __device__ __forceinline__ void store_out(void* out, size_t idx, float v) {
 // m_s[w][h] (base 2), weight sum l_s[w][h] and unnormalised output
 // o_s[w][h][d] in LDS (synchronised by the caller).  With M = max_w m_w,
 //   num = sum_w 2^(m_w - M) o_w,   den = sum_w 2^(m_w - M) l_w.
-// A row held by one partition stores num/den; otherwise the partition's
-// (M, den, num) go to the workspace for decode_reduce.
+// A row held by one partition stores num/den (times the V scale of an FP8
+// pool, 1 otherwise); otherwise the partition's (M, den, num) go to the
+// workspace for decode_reduce.
 template <typename OutT, int D, int ROWS>
 __device__ __forceinline__ void finish_partition(const DecodeParams& P, float (*o_s)[ROWS][D + 1],
                                                  float (*m_s)[ROWS], float (*l_s)[ROWS], int s, int h0, int nh,
@@ -81,7 +82,7 @@ __device__ __forceinline__ void finish_partition(const DecodeParams& P, float (*
     }
     const size_t row_h = (size_t)s * P.num_q_heads + h0 + hh;
     if (nparts == 1) {
-      store_out<OutT>(P.out, row_h * D + d, den > 0.f ? num / den : 0.f);
+      store_out<OutT>(P.out, row_h * D + d, den > 0.f ? num / den * P.v_scale : 0.f);
     } else {
       P.part_o[(row_h * P.num_parts + part) * D + d] = num;
       if (d == 0) {

@@ -1,4 +1,4 @@
-// Paged decode attention on the CDNA4 matrix cores (bf16 pools),
+// Paged decode attention on the CDNA4 matrix cores (bf16 or FP8 pools),
 // partitioned form: one workgroup per (partition of a block-table row, KV
 // head [, chunk of 16 query heads], sequence).
 //
@@ -22,7 +22,7 @@ namespace {
 #define KVP_MFMA_WAVES_PER_EU 2
 #endif
 
-template <int D, int DEPTH>
+template <int D, int DEPTH, bool FP8>
 __global__ __launch_bounds__(kThreads, KVP_MFMA_WAVES_PER_EU) void decode_mfma_kernel(const DecodeParams P) {
   constexpr int NBUF = DEPTH + 1;
   __shared__ float o_s[kWaves][16][D + 1];
@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kThreads, KVP_MFMA_WAVES_PER_EU) void decode_mfma_k
   const int jb = part * P.part_blocks;
   const int nbp = min(P.part_blocks, rs.nblocks - jb);
 
-  const uint16_t* pool = (const uint16_t*)P.pool_layer;
+  const void* pool = P.pool_layer;
   const MfmaLanes la = mfma_lanes<D>(P.num_kv_heads, kvh, lane);
   st.reset();
   const int so = rs.start_off;
@@ -69,16 +69,16 @@ __global__ __launch_bounds__(kThreads, KVP_MFMA_WAVES_PER_EU) void decode_mfma_k
 
   // Table entries of this wave: wave, wave + 4, ...; `cnt` of them.
   const int cnt = nbp > wave ? (nbp - wave + kWaves - 1) / kWaves : 0;
-  auto issue = [&](int k, MfmaTiles<D>& t) {
+  auto issue = [&](int k, MfmaTiles<D, FP8>& t) {
     const int kc = k < cnt ? k : cnt - 1;  // past the end: re-read the last block (a cache hit)
-    mfma_issue<D>(t, pool, la, __builtin_amdgcn_readlane(my_id, wave + kc * kWaves), P.num_blocks);
+    mfma_issue(t, pool, la, __builtin_amdgcn_readlane(my_id, wave + kc * kWaves), P.num_blocks);
   };
 
   // Software pipeline: the loads of block k + DEPTH are issued before block k
   // is computed; the scheduling barrier keeps the compiler from sinking them
   // below the compute, so DEPTH blocks stay in flight while one is consumed.
   if (cnt > 0) {
-    MfmaTiles<D> buf[NBUF];
+    MfmaTiles<D, FP8> buf[NBUF];
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       issue(d, buf[d]);
@@ -110,14 +110,14 @@ __global__ __launch_bounds__(kThreads, KVP_MFMA_WAVES_PER_EU) void decode_mfma_k
   finish_partition<uint16_t, D, 16>(P, o_s, m_s, l_s, s, h0, nh, part, nparts);
 }
 
-template <int D>
+template <int D, bool FP8>
 hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid(p.num_kv_heads * p.qgroups, p.num_seqs, p.num_parts);
   const dim3 block(kThreads);
   switch (p.depth) {
-    case 1: hipLaunchKernelGGL((decode_mfma_kernel<D, 1>), grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((decode_mfma_kernel<D, 2>), grid, block, 0, stream, p); break;
-    case 3: hipLaunchKernelGGL((decode_mfma_kernel<D, 3>), grid, block, 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((decode_mfma_kernel<D, 1, FP8>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((decode_mfma_kernel<D, 2, FP8>), grid, block, 0, stream, p); break;
+    case 3: hipLaunchKernelGGL((decode_mfma_kernel<D, 3, FP8>), grid, block, 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -126,8 +126,8 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t stream) {
-  if (head_dim == 128) return launch_d<128>(p, stream);
-  if (head_dim == 64) return launch_d<64>(p, stream);
+  if (head_dim == 128) return p.kv_fp8 ? launch_d<128, true>(p, stream) : launch_d<128, false>(p, stream);
+  if (head_dim == 64) return p.kv_fp8 ? launch_d<64, true>(p, stream) : launch_d<64, false>(p, stream);
   return hipErrorInvalidValue;
 }
 

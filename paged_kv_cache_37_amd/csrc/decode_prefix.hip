@@ -1,5 +1,5 @@
 // Shared-prefix (cascade) pass of paged decode attention on the CDNA4 matrix
-// cores (bf16 pools).
+// cores (bf16 or FP8 pools).
 //
 // When every sequence of a batch starts with the same physical blocks (a
 // cached prefix that all of them reference: [Pool] "Finding a prefix again"
@@ -22,7 +22,7 @@
 namespace kvp {
 namespace {
 
-template <int D, int DEPTH>
+template <int D, int DEPTH, bool FP8>
 __global__ __launch_bounds__(kThreads, 2) void decode_prefix_kernel(const DecodeParams P) {
   constexpr int NBUF = DEPTH + 1;
   __shared__ float o_s[kWaves][16][D + 1];
@@ -64,18 +64,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode_prefix_kernel(const Decode
   // that concurrent waves spread over the L2 channels.
   for (int i = lane; i < cnt; i += 64) ids_s[wave][i] = P.block_tables[j0 + i];
   const int rot = cnt > 0 ? (int)(((long long)tile * 37) % cnt) : 0;
-  const uint16_t* pool = (const uint16_t*)P.pool_layer;
+  const void* pool = P.pool_layer;
   const MfmaLanes la = mfma_lanes<D>(P.num_kv_heads, kvh, lane);
   int issued = 0;
-  auto issue = [&](MfmaTiles<D>& t) {
+  auto issue = [&](MfmaTiles<D, FP8>& t) {
     const int k = issued < cnt ? issued : cnt - 1;  // past the end: re-read the last block (a cache hit)
     const int kr = k + rot < cnt ? k + rot : k + rot - cnt;
-    mfma_issue<D>(t, pool, la, __builtin_amdgcn_readfirstlane(ids_s[wave][kr]), P.num_blocks);
+    mfma_issue(t, pool, la, __builtin_amdgcn_readfirstlane(ids_s[wave][kr]), P.num_blocks);
     ++issued;
   };
 
   if (cnt > 0) {
-    MfmaTiles<D> buf[NBUF];
+    MfmaTiles<D, FP8> buf[NBUF];
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       issue(buf[d]);
@@ -138,10 +138,15 @@ hipError_t launch_decode_prefix(const DecodeParams& p, int head_dim, hipStream_t
   const long long tiles = ((long long)p.num_seqs * p.group + 15) / 16;
   const long long grid = tiles * p.num_kv_heads;
   if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidValue;
-  if (head_dim == 128)
-    hipLaunchKernelGGL((decode_prefix_kernel<128, 2>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  const dim3 g((unsigned)grid), b(kThreads);
+  if (head_dim == 128 && p.kv_fp8)
+    hipLaunchKernelGGL((decode_prefix_kernel<128, 2, true>), g, b, 0, stream, p);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL((decode_prefix_kernel<128, 2, false>), g, b, 0, stream, p);
+  else if (head_dim == 64 && p.kv_fp8)
+    hipLaunchKernelGGL((decode_prefix_kernel<64, 2, true>), g, b, 0, stream, p);
   else if (head_dim == 64)
-    hipLaunchKernelGGL((decode_prefix_kernel<64, 2>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((decode_prefix_kernel<64, 2, false>), g, b, 0, stream, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

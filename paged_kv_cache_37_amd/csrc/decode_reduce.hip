@@ -63,7 +63,7 @@ __global__ __launch_bounds__(64 * kRowsPerWg) void decode_reduce_kernel(const De
     }
     M = Mc;
   }
-  const float inv = den > 0.f ? 1.f / den : 0.f;
+  const float inv = den > 0.f ? P.v_scale / den : 0.f;
 #pragma unroll
   for (int e = 0; e < PER; ++e) store_out<OutT>(P.out, row_h * D + lane + 64 * e, num[e] * inv);
 }
@@ -78,8 +78,9 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode_reduce(const DecodeParams& p, int dtype, int head_dim, hipStream_t stream) {
-  if (head_dim == 128) return dtype == 1 ? launch_t<128, uint16_t>(p, stream) : launch_t<128, float>(p, stream);
-  return dtype == 1 ? launch_t<64, uint16_t>(p, stream) : launch_t<64, float>(p, stream);
+  // bf16 and FP8 pools produce bf16 outputs, fp32 pools fp32
+  if (head_dim == 128) return dtype != 0 ? launch_t<128, uint16_t>(p, stream) : launch_t<128, float>(p, stream);
+  return dtype != 0 ? launch_t<64, uint16_t>(p, stream) : launch_t<64, float>(p, stream);
 }
 
 }  // namespace kvp

@@ -1,4 +1,4 @@
-// Paged decode attention on the CDNA4 matrix cores (bf16 pools), streaming
+// Paged decode attention on the CDNA4 matrix cores (bf16 or FP8 pools), streaming
 // form: a persistent grid of exactly the resident waves splits the batch's
 // work evenly, whatever the mix of sequence lengths.
 //
@@ -60,9 +60,9 @@ struct RowCtx {
 };
 
 // Tile ring entry: loads in flight plus the tile's place in its row.
-template <int D>
+template <int D, bool FP8>
 struct StreamTile {
-  MfmaTiles<D> t;
+  MfmaTiles<D, FP8> t;
   int j;       // table entry within the row
   int row_id;  // rows of this wave counted from 0
 };
@@ -74,8 +74,10 @@ struct StreamTile {
 // key/value from registers instead of the pool, and the wave of the KV
 // head's first head group writes them to the pool.  No wave reads a slot
 // another wave writes in the same launch (the slot lies in the sequence's
-// own last block), so no ordering between waves is needed.
-template <int D, int DEPTH, bool FUSED>
+// own last block), so no ordering between waves is needed.  Into an FP8
+// pool the new token goes as its codes (the same rounding as cache_write),
+// and the attention uses those codes.
+template <int D, int DEPTH, bool FUSED, bool FP8>
 __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stream_kernel(const DecodeParams P) {
   constexpr int NBUF = DEPTH + 1;
   __shared__ int pre[kMaxStreamSeqs + 1];  // pre[s] = table entries of sequences < s
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
   const int n_tiles = (int)(t_end - t_begin);
   if (n_tiles <= 0) return;
 
-  const uint16_t* pool = (const uint16_t*)P.pool_layer;
+  const void* pool = P.pool_layer;
   const uint16_t* q = (const uint16_t*)P.q;
 
   auto row_at = [&](long long t) {  // row holding tile t
@@ -175,9 +177,9 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
   MfmaLanes ila = mfma_lanes<D>(P.num_kv_heads, ir.hg / P.qgroups, lane);
   int issued = 0;
 
-  auto issue = [&](StreamTile<D>& x) {
+  auto issue = [&](StreamTile<D, FP8>& x) {
     if (issued >= n_tiles) {  // past the range: re-issue the last tile (a cache hit), same context
-      mfma_issue<D>(x.t, pool, ila, __builtin_amdgcn_readlane(ij - 1 - ids_base < 64 ? ids_a : ids_b,
+      mfma_issue(x.t, pool, ila, __builtin_amdgcn_readlane(ij - 1 - ids_base < 64 ? ids_a : ids_b,
                                                                (ij - 1 - ids_base) & 63),
                     P.num_blocks);
       x.j = -1;
@@ -199,7 +201,7 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
       ids_base += 64;
       ids_b = ids_base + 64 + lane < ir.nb ? irow[ids_base + 64 + lane] : 0;
     }
-    mfma_issue<D>(x.t, pool, ila, __builtin_amdgcn_readlane(ids_a, ij - ids_base), P.num_blocks);
+    mfma_issue(x.t, pool, ila, __builtin_amdgcn_readlane(ids_a, ij - ids_base), P.num_blocks);
     x.j = ij;
     x.row_id = irow_id;
     ++ij;
@@ -253,7 +255,7 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
       for (int r4 = 0; r4 < 4; ++r4) {
         const int g = 4 * q4 + r4;
         const float lg = __shfl(l_tot, g);
-        const float inv = lg > 0.f ? 1.f / lg : 0.f;
+        const float inv = lg > 0.f ? P.v_scale / lg : 0.f;
         if (g < c_nh) {
           unsigned* o = (unsigned*)((uint16_t*)P.out + ((size_t)cr.s * P.num_q_heads + c_h0 + g) * D);
 #pragma unroll
@@ -302,48 +304,78 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
   // The row's last block holds the new token at table slot send - 1: put
   // its key and value into this wave's operands (layouts of mfma_tile.h),
   // and store them into the pool once per KV head.
-  auto put_new = [&](MfmaTiles<D>& t) {
+  auto put_new = [&](MfmaTiles<D, FP8>& t) {
     const int o = (crs.start_off + crs.n - 1) & (kBlock - 1);
     const int q4 = lane >> 4, j = lane & 15;
+    const int kvh = cr.hg / P.qgroups, b = slot_c >> 4, off = slot_c & (kBlock - 1);
+    const bool writer = cr.hg % P.qgroups == 0;
+    const size_t blk = (size_t)b * 2 * P.num_kv_heads * kBlock * D;
+    const size_t kt = blk + (size_t)kvh * kBlock * D, vt = blk + (size_t)(P.num_kv_heads + kvh) * kBlock * D;
+    const int e = ((off >> 2) * D + 2 * lane) * 4 + (off & 3);  // this lane's first V element
+    if constexpr (FP8) {
+      const uint2_v kc = fp8_quant8(kn, P.inv_k_scale);  // codes of dims 8 lane .. +7
+      const unsigned vc = fp8_quant2(vn, P.inv_v_scale);  // codes of dims 2 lane, +1
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
-      const int src = 4 * kk + q4;  // lane holding dims 32 kk + 8 q4 .. +7
-      const uint4_v v = {(unsigned)__shfl((int)kn.x, src), (unsigned)__shfl((int)kn.y, src),
-                         (unsigned)__shfl((int)kn.z, src), (unsigned)__shfl((int)kn.w, src)};
-      if (j == o) t.k[kk] = v;
-    }
-    const bool hi = (o & 1) != 0;
-    const unsigned keep = hi ? 0x0000ffffu : 0xffff0000u;
-    const int sh = hi ? 16 : 0;
+      for (int kk = 0; kk < D / 32; ++kk) {
+        const int src = 4 * kk + q4;
+        const uint2_v v = {(unsigned)__shfl((int)kc.x, src), (unsigned)__shfl((int)kc.y, src)};
+        if (j == o) t.k[kk] = v;
+      }
+      const int sh = 8 * (o & 3);
+      const unsigned keep = ~(0xffu << sh);
 #pragma unroll
-    for (int m = 0; m < D / 32; ++m) {
-      const unsigned nv = (unsigned)__shfl((int)vn, 16 * m + j);  // dims 32 m + 2 j (low half), +1
-      if (q4 == (o >> 2)) {
-        const unsigned d0 = (nv & 0xffffu) << sh, d1 = (nv >> 16) << sh;
-        if ((o & 2) == 0) {
-          t.v[m].x = (t.v[m].x & keep) | d0;
-          t.v[m].z = (t.v[m].z & keep) | d1;
-        } else {
-          t.v[m].y = (t.v[m].y & keep) | d0;
-          t.v[m].w = (t.v[m].w & keep) | d1;
+      for (int m = 0; m < D / 32; ++m) {
+        const unsigned nv = (unsigned)__shfl((int)vc, 16 * m + j);  // dims 32 m + 2 j (byte 0), +1 (byte 1)
+        if (q4 == (o >> 2)) {
+          t.v[m].x = (t.v[m].x & keep) | ((nv & 0xffu) << sh);
+          t.v[m].y = (t.v[m].y & keep) | (((nv >> 8) & 0xffu) << sh);
         }
       }
-    }
-    if (cr.hg % P.qgroups == 0) {
-      const int kvh = cr.hg / P.qgroups, b = slot_c >> 4, off = slot_c & (kBlock - 1);
-      uint16_t* blk = (uint16_t*)P.pool_layer + (size_t)b * 2 * P.num_kv_heads * kBlock * D;
-      uint16_t* kt = blk + (size_t)kvh * kBlock * D;
-      uint16_t* vt = blk + (size_t)(P.num_kv_heads + kvh) * kBlock * D;
-      if (lane < D / 8) *(uint4_v*)(kt + off * D + 8 * lane) = kn;
-      if (lane < D / 2) {
-        const int e = ((off >> 2) * D + 2 * lane) * 4 + (off & 3);
-        vt[e] = (uint16_t)(vn & 0xffffu);
-        vt[e + 4] = (uint16_t)(vn >> 16);
+      if (writer) {
+        uint8_t* pl = (uint8_t*)P.pool_layer;
+        if (lane < D / 8) *(uint2_v*)(pl + kt + off * D + 8 * lane) = kc;
+        if (lane < D / 2) {
+          pl[vt + e] = (uint8_t)(vc & 0xffu);
+          pl[vt + e + 4] = (uint8_t)((vc >> 8) & 0xffu);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) {
+        const int src = 4 * kk + q4;  // lane holding dims 32 kk + 8 q4 .. +7
+        const uint4_v v = {(unsigned)__shfl((int)kn.x, src), (unsigned)__shfl((int)kn.y, src),
+                           (unsigned)__shfl((int)kn.z, src), (unsigned)__shfl((int)kn.w, src)};
+        if (j == o) t.k[kk] = v;
+      }
+      const bool hi = (o & 1) != 0;
+      const unsigned keep = hi ? 0x0000ffffu : 0xffff0000u;
+      const int sh = hi ? 16 : 0;
+#pragma unroll
+      for (int m = 0; m < D / 32; ++m) {
+        const unsigned nv = (unsigned)__shfl((int)vn, 16 * m + j);  // dims 32 m + 2 j (low half), +1
+        if (q4 == (o >> 2)) {
+          const unsigned d0 = (nv & 0xffffu) << sh, d1 = (nv >> 16) << sh;
+          if ((o & 2) == 0) {
+            t.v[m].x = (t.v[m].x & keep) | d0;
+            t.v[m].z = (t.v[m].z & keep) | d1;
+          } else {
+            t.v[m].y = (t.v[m].y & keep) | d0;
+            t.v[m].w = (t.v[m].w & keep) | d1;
+          }
+        }
+      }
+      if (writer) {
+        uint16_t* pl = (uint16_t*)P.pool_layer;
+        if (lane < D / 8) *(uint4_v*)(pl + kt + off * D + 8 * lane) = kn;
+        if (lane < D / 2) {
+          pl[vt + e] = (uint16_t)(vn & 0xffffu);
+          pl[vt + e + 4] = (uint16_t)(vn >> 16);
+        }
       }
     }
   };
 
-  auto compute = [&](StreamTile<D>& x) {
+  auto compute = [&](StreamTile<D, FP8>& x) {
     if (x.row_id != crow_id) {  // first tile of the next row
       finish_row();
       cr = qn;
@@ -374,7 +406,7 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
     st.step(x.t, J, crs.start_off, crs.start_off + crs.n, crs.nblocks, P.scale_log2, lane);
   };
 
-  StreamTile<D> buf[NBUF];
+  StreamTile<D, FP8> buf[NBUF];
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) {
     issue(buf[d]);
@@ -488,22 +520,25 @@ __global__ __launch_bounds__(256) void decode_stream_reduce_kernel(const DecodeP
       }
     }
   }
-  const float inv = den > 0.f ? 1.f / den : 0.f;
+  const float inv = den > 0.f ? P.v_scale / den : 0.f;
   uint16_t* out = (uint16_t*)P.out + ((size_t)s * P.num_q_heads + h) * D;
 #pragma unroll
   for (int e = 0; e < PER; ++e) out[lane + 64 * e] = bf16_rne(num[e] * inv);
 }
 
-template <int D, int DEPTH>
+template <int D, int DEPTH, bool FP8>
 hipError_t launch_sd(const DecodeParams& p, hipStream_t stream) {
   if (p.prefix_blocks > 0) {
     const hipError_t e = launch_decode_prefix(p, D, stream);
     if (e != hipSuccess) return e;
   }
-  if (p.slot_mapping)
-    hipLaunchKernelGGL((decode_stream_kernel<D, DEPTH, true>), dim3(p.stream_wgs), dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((decode_stream_kernel<D, DEPTH, false>), dim3(p.stream_wgs), dim3(kThreads), 0, stream, p);
+  if (p.slot_mapping) {
+    // the fused step runs at ring depth 1 (the new token takes the registers of a deeper ring)
+    if constexpr (DEPTH != 1) return hipErrorInvalidValue;
+    else hipLaunchKernelGGL((decode_stream_kernel<D, 1, true, FP8>), dim3(p.stream_wgs), dim3(kThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((decode_stream_kernel<D, DEPTH, false, FP8>), dim3(p.stream_wgs), dim3(kThreads), 0, stream, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid((p.num_q_heads + 3) / 4, p.num_seqs);
@@ -511,29 +546,31 @@ hipError_t launch_sd(const DecodeParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool FP8>
 hipError_t launch_s(const DecodeParams& p, hipStream_t stream) {
   switch (p.depth) {
-    case 1: return launch_sd<D, 1>(p, stream);
-    case 2: return launch_sd<D, 2>(p, stream);
+    case 1: return launch_sd<D, 1, FP8>(p, stream);
+    case 2: return launch_sd<D, 2, FP8>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
+template <int D, bool FP8>
+const void* symbol_of(int depth, bool fused) {
+  if (fused) return depth == 1 ? (const void*)decode_stream_kernel<D, 1, true, FP8> : nullptr;
+  return depth == 1 ? (const void*)decode_stream_kernel<D, 1, false, FP8> : (const void*)decode_stream_kernel<D, 2, false, FP8>;
+}
+
 }  // namespace
 
-const void* stream_kernel_symbol(int head_dim, int depth, bool fused) {
-  if (head_dim == 128) {
-    if (fused) return depth == 1 ? (const void*)decode_stream_kernel<128, 1, true> : (const void*)decode_stream_kernel<128, 2, true>;
-    return depth == 1 ? (const void*)decode_stream_kernel<128, 1, false> : (const void*)decode_stream_kernel<128, 2, false>;
-  }
-  if (fused) return depth == 1 ? (const void*)decode_stream_kernel<64, 1, true> : (const void*)decode_stream_kernel<64, 2, true>;
-  return depth == 1 ? (const void*)decode_stream_kernel<64, 1, false> : (const void*)decode_stream_kernel<64, 2, false>;
+const void* stream_kernel_symbol(int head_dim, int depth, bool fused, bool fp8) {
+  if (head_dim == 128) return fp8 ? symbol_of<128, true>(depth, fused) : symbol_of<128, false>(depth, fused);
+  return fp8 ? symbol_of<64, true>(depth, fused) : symbol_of<64, false>(depth, fused);
 }
 
 hipError_t launch_decode_stream(const DecodeParams& p, int head_dim, hipStream_t stream) {
-  if (head_dim == 128) return launch_s<128>(p, stream);
-  if (head_dim == 64) return launch_s<64>(p, stream);
+  if (head_dim == 128) return p.kv_fp8 ? launch_s<128, true>(p, stream) : launch_s<128, false>(p, stream);
+  if (head_dim == 64) return p.kv_fp8 ? launch_s<64, true>(p, stream) : launch_s<64, false>(p, stream);
   return hipErrorInvalidValue;
 }
 

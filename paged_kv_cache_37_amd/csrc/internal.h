@@ -45,6 +45,10 @@ struct DecodeParams {
   float* pre_ml;                // [S][Hq][2] prefix pass: (max, sum)                  (cascade only)
   float* row_o;                 // [rows][heads_per_wg][D] tails held whole by a wave  (cascade only)
   float* row_ml;                // [rows][heads_per_wg][2]                             (cascade only)
+  int32_t kv_fp8;               // the pool holds E4M3 codes (K scale folded into scale_log2)
+  float v_scale;                // multiplies every output (FP8 V codes); 1 otherwise
+  float inv_k_scale;            // 1 / k_scale, 1 / v_scale: quantizing the fused write's new token
+  float inv_v_scale;
 };
 
 // Span of one block-table row: leading slots of the first block that are
@@ -72,7 +76,8 @@ __device__ __forceinline__ RowSpan row_span(int ctx, int window, int max_blocks)
 // Launchers (each defined next to its kernel).
 hipError_t launch_cache_write(void* pool_layer, int dtype, int num_blocks, int num_kv_heads,
                               int head_dim, const void* k_new, const void* v_new,
-                              const int32_t* slots, int num_tokens, hipStream_t stream);
+                              const int32_t* slots, int num_tokens, float inv_k_scale, float inv_v_scale,
+                              hipStream_t stream);
 hipError_t launch_copy_blocks(void* pool_base, int num_layers, int num_blocks, size_t block_bytes, const int32_t* src,
                               const int32_t* dst, int num_pairs, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int head_dim, hipStream_t stream);
@@ -80,6 +85,8 @@ hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t s
 hipError_t launch_decode_reduce(const DecodeParams& p, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_decode_stream(const DecodeParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_decode_prefix(const DecodeParams& p, int head_dim, hipStream_t stream);
-const void* stream_kernel_symbol(int head_dim, int depth, bool fused);
+// The streaming kernel instance a launch would use (for occupancy queries);
+// nullptr for one that is never launched (the fused step runs at depth 1).
+const void* stream_kernel_symbol(int head_dim, int depth, bool fused, bool fp8);
 
 }  // namespace kvp

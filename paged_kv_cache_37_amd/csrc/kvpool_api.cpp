@@ -8,6 +8,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <new>
+#include <vector>
 
 #include "internal.h"
 #include "kvpool.h"
@@ -16,6 +17,7 @@ struct kvp_pool_s {
   kvp_pool_desc desc;
   void* base;
   size_t bytes;
+  std::vector<float> k_scale, v_scale;  // per layer (FP8 pools)
 };
 
 namespace {
@@ -35,7 +37,7 @@ int32_t ok() {
   return KVP_OK;
 }
 
-size_t elt_bytes(int32_t dtype) { return dtype == KVP_F32 ? 4 : 2; }
+size_t elt_bytes(int32_t dtype) { return dtype == KVP_F32 ? 4 : dtype == KVP_BF16 ? 2 : 1; }
 
 // Elements of one layer: num_blocks * 2 * Hkv * 16 * D.
 size_t layer_elems(const kvp_pool_desc& d) {
@@ -49,7 +51,8 @@ int32_t check_desc(const kvp_pool_desc* d) {
   if (d->block_size != kvp::kBlock) return fail(KVP_ERR_UNSUPPORTED, "block_size must be 16 (got %d)", d->block_size);
   if (d->head_dim != 64 && d->head_dim != 128)
     return fail(KVP_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", d->head_dim);
-  if (d->dtype != KVP_F32 && d->dtype != KVP_BF16) return fail(KVP_ERR_UNSUPPORTED, "dtype must be F32 or BF16");
+  if (d->dtype != KVP_F32 && d->dtype != KVP_BF16 && d->dtype != KVP_FP8_E4M3)
+    return fail(KVP_ERR_UNSUPPORTED, "dtype must be F32, BF16 or FP8_E4M3");
   if ((size_t)d->num_blocks * kvp::kBlock > (size_t)INT32_MAX)
     return fail(KVP_ERR_INVALID_ARG, "num_blocks * 16 must fit in int32 slot numbers");
   return KVP_OK;
@@ -86,8 +89,10 @@ int32_t kv_pool_create(const kvp_pool_desc* desc, void* dev_base, size_t bytes, 
   if (!aligned(dev_base, 256)) return fail(KVP_ERR_INVALID_ARG, "dev_base must be 256-byte aligned");
   const size_t need = kv_pool_bytes(desc);
   if (bytes < need) return fail(KVP_ERR_INVALID_ARG, "pool memory too small: %zu < %zu bytes", bytes, need);
-  kvp_pool_s* p = new (std::nothrow) kvp_pool_s{*desc, dev_base, bytes};
+  kvp_pool_s* p = new (std::nothrow) kvp_pool_s{*desc, dev_base, bytes, {}, {}};
   if (!p) return fail(KVP_ERR_INVALID_ARG, "out of host memory");
+  p->k_scale.assign(desc->num_layers, 1.0f);
+  p->v_scale.assign(desc->num_layers, 1.0f);
   *out = p;
   return ok();
 }
@@ -100,6 +105,17 @@ int32_t kv_pool_destroy(kvp_pool pool) {
 int32_t kv_pool_describe(kvp_pool pool, kvp_pool_desc* desc) {
   if (!pool || !desc) return fail(KVP_ERR_INVALID_ARG, "NULL argument");
   *desc = pool->desc;
+  return ok();
+}
+
+int32_t kv_pool_set_fp8_scales(kvp_pool pool, int32_t layer, float k_scale, float v_scale) {
+  if (!pool) return fail(KVP_ERR_INVALID_ARG, "pool is NULL");
+  if (pool->desc.dtype != KVP_FP8_E4M3) return fail(KVP_ERR_UNSUPPORTED, "the pool is not FP8");
+  if (layer < 0 || layer >= pool->desc.num_layers) return fail(KVP_ERR_INVALID_ARG, "layer %d out of range", layer);
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return fail(KVP_ERR_INVALID_ARG, "scales must be finite and > 0");
+  pool->k_scale[layer] = k_scale;
+  pool->v_scale[layer] = v_scale;
   return ok();
 }
 
@@ -128,7 +144,8 @@ int32_t cache_write(kvp_pool pool, int32_t layer, const void* k_new, const void*
     return fail(KVP_ERR_INVALID_ARG, "k_new/v_new must be 16-byte aligned");
   char* base = (char*)pool->base + (size_t)layer * layer_elems(d) * elt_bytes(d.dtype);
   const hipError_t e = kvp::launch_cache_write(base, d.dtype, d.num_blocks, d.num_kv_heads, d.head_dim, k_new,
-                                               v_new, slot_mapping, num_tokens, stream);
+                                               v_new, slot_mapping, num_tokens, 1.0f / pool->k_scale[layer],
+                                               1.0f / pool->v_scale[layer], stream);
   if (e != hipSuccess) return fail(KVP_ERR_HIP, "cache_write launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -136,22 +153,25 @@ int32_t cache_write(kvp_pool pool, int32_t layer, const void* k_new, const void*
 // Resident workgroups of the streaming kernel on the current device:
 // compute units x workgroups per compute unit at the kernel's occupancy.
 // 0 if there is no device to ask.
-static int32_t stream_workgroups(int32_t head_dim, int32_t depth, bool fused = false) {
+static int32_t stream_workgroups(int32_t head_dim, int32_t depth, bool fused, bool fp8) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   static thread_local int cached_dev = -1, cached_d = 0, cached_depth = 0, cached_wgs = 0;
-  static thread_local bool cached_fused = false;
-  if (dev == cached_dev && head_dim == cached_d && depth == cached_depth && fused == cached_fused) return cached_wgs;
+  static thread_local bool cached_fused = false, cached_fp8 = false;
+  if (dev == cached_dev && head_dim == cached_d && depth == cached_depth && fused == cached_fused &&
+      fp8 == cached_fp8)
+    return cached_wgs;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kvp::stream_kernel_symbol(head_dim, depth, fused), kvp::kThreads,
-                                                   0) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kvp::stream_kernel_symbol(head_dim, depth, fused, fp8),
+                                                   kvp::kThreads, 0) != hipSuccess ||
       per_cu <= 0)
     return 0;
   cached_dev = dev;
   cached_d = head_dim;
   cached_depth = depth;
   cached_fused = fused;
+  cached_fp8 = fp8;
   cached_wgs = cus * per_cu;
   return cached_wgs;
 }
@@ -193,7 +213,8 @@ static int32_t plan(kvp_pool pool, int32_t num_seqs, int32_t num_q_heads, int32_
       (partition_tokens % kvp::kBlock != 0 || partition_tokens < kvp::kBlock || partition_tokens > 64 * kvp::kBlock))
     return fail(KVP_ERR_INVALID_ARG, "partition_tokens must be 0 or a multiple of 16 in [16, 1024]");
   const int32_t G = num_q_heads / d.num_kv_heads;
-  const bool bf16 = d.dtype == KVP_BF16;
+  const bool bf16 = d.dtype != KVP_F32;  // bf16 or fp8 storage: the matrix-core kernels
+  const bool fp8 = d.dtype == KVP_FP8_E4M3;
   const int32_t mfma_groups = d.num_kv_heads * ((G + 15) / 16);  // head groups of the MFMA kernels
   int32_t pth;
   switch (variant) {
@@ -201,17 +222,21 @@ static int32_t plan(kvp_pool pool, int32_t num_seqs, int32_t num_q_heads, int32_
       if (!bf16) {
         pth = PATH_VALU;
       } else {
-        const int32_t wgs = partition_tokens == 0 ? stream_workgroups(d.head_dim, decode_depth(PATH_STREAM)) : 0;
+        const int32_t wgs =
+            partition_tokens == 0 ? stream_workgroups(d.head_dim, decode_depth(PATH_STREAM), false, fp8) : 0;
         pth = wgs > 0 && stream_fits(num_seqs, max_blocks, mfma_groups, wgs) ? PATH_STREAM : PATH_MFMA;
       }
       break;
-    case KVP_VARIANT_VALU: pth = PATH_VALU; break;
+    case KVP_VARIANT_VALU:
+      if (d.dtype == KVP_FP8_E4M3) return fail(KVP_ERR_UNSUPPORTED, "the VALU variant takes fp32 and bf16 pools");
+      pth = PATH_VALU;
+      break;
     case KVP_VARIANT_MFMA:
-      if (!bf16) return fail(KVP_ERR_UNSUPPORTED, "the MFMA variant needs a bf16 pool");
+      if (!bf16) return fail(KVP_ERR_UNSUPPORTED, "the MFMA variant needs a bf16 or fp8 pool");
       pth = PATH_MFMA;
       break;
     case KVP_VARIANT_STREAM:
-      if (!bf16) return fail(KVP_ERR_UNSUPPORTED, "the STREAM variant needs a bf16 pool");
+      if (!bf16) return fail(KVP_ERR_UNSUPPORTED, "the STREAM variant needs a bf16 or fp8 pool");
       if (num_seqs > kvp::kMaxStreamSeqs)
         return fail(KVP_ERR_UNSUPPORTED, "the STREAM variant takes at most %d sequences", kvp::kMaxStreamSeqs);
       pth = PATH_STREAM;
@@ -245,7 +270,7 @@ static int32_t plan(kvp_pool pool, int32_t num_seqs, int32_t num_q_heads, int32_
   p->num_parts = (max_blocks + pb - 1) / pb;
   p->depth = decode_depth(pth);
   if (pth == PATH_STREAM) {
-    p->stream_wgs = stream_workgroups(d.head_dim, p->depth);
+    p->stream_wgs = stream_workgroups(d.head_dim, p->depth, false, fp8);
     if (p->stream_wgs <= 0) return fail(KVP_ERR_HIP, "cannot size the streaming grid (no device?)");
     if (!stream_fits(num_seqs, max_blocks, d.num_kv_heads * qgroups, p->stream_wgs))
       return fail(KVP_ERR_UNSUPPORTED, "num_seqs * max_blocks_per_seq too large for the STREAM variant");
@@ -301,8 +326,13 @@ size_t paged_decode_workspace_bytes(kvp_pool pool, int32_t num_seqs, int32_t num
     kvp::DecodeParams p;
     int32_t path;
     if (plan(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, v, &p, &path) != KVP_OK) continue;
-    const size_t n = path == PATH_STREAM ? stream_workspace(p, pool->desc.head_dim).total
-                                         : grid_workspace(p, pool->desc.head_dim, &a);
+    size_t n = path == PATH_STREAM ? stream_workspace(p, pool->desc.head_dim).total
+                                   : grid_workspace(p, pool->desc.head_dim, &a);
+    if (path == PATH_STREAM) {  // the fused step's grid (its own occupancy) must fit too
+      p.stream_wgs = stream_workgroups(pool->desc.head_dim, 1, true, pool->desc.dtype == KVP_FP8_E4M3);
+      const size_t nf = stream_workspace(p, pool->desc.head_dim).total;
+      if (nf > n) n = nf;
+    }
     if (n > need) need = n;
   }
   g_err[0] = '\0';
@@ -337,7 +367,7 @@ static int32_t decode(kvp_pool pool, const kvp_decode_args* a, const void* k_new
   if (write && path == PATH_STREAM) {
     // the fused kernel holds the new token in registers: ring depth 1
     p.depth = 1;
-    p.stream_wgs = stream_workgroups(d.head_dim, 1, true);
+    p.stream_wgs = stream_workgroups(d.head_dim, 1, true, d.dtype == KVP_FP8_E4M3);
     if (p.stream_wgs <= 0) return fail(KVP_ERR_HIP, "cannot size the streaming grid (no device?)");
     p.k_new = k_new;
     p.v_new = v_new;
@@ -377,11 +407,17 @@ static int32_t decode(kvp_pool pool, const kvp_decode_args* a, const void* k_new
   p.block_tables = a->block_tables;
   p.seq_lens = a->seq_lens;
   p.window = a->sliding_window;
-  p.scale_log2 = a->scale * 1.4426950408889634f;
+  // FP8 codes: K's scale joins the softmax scale, V's the final normalisation
+  const bool fp8 = d.dtype == KVP_FP8_E4M3;
+  p.kv_fp8 = fp8;
+  p.scale_log2 = a->scale * 1.4426950408889634f * (fp8 ? pool->k_scale[a->layer] : 1.0f);
+  p.v_scale = fp8 ? pool->v_scale[a->layer] : 1.0f;
+  p.inv_k_scale = 1.0f / pool->k_scale[a->layer];
+  p.inv_v_scale = 1.0f / pool->v_scale[a->layer];
   hipError_t e;
   if (write && path != PATH_STREAM) {
     e = kvp::launch_cache_write(const_cast<void*>(p.pool_layer), d.dtype, d.num_blocks, d.num_kv_heads, d.head_dim,
-                                k_new, v_new, slots, a->num_seqs, stream);
+                                k_new, v_new, slots, a->num_seqs, p.inv_k_scale, p.inv_v_scale, stream);
     if (e != hipSuccess) return fail(KVP_ERR_HIP, "cache_write launch: %s", hipGetErrorString(e));
   }
   if (path == PATH_STREAM) {

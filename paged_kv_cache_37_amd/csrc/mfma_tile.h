@@ -13,9 +13,16 @@
 // operands of two PV MFMAs (column j of MFMA 2m+e is dimension 32m+2j+e).
 // The accumulator of PV MFMA n, register r, lane l is therefore
 //   O[head 4q + r][dim 32(n/2) + 2(l%16) + n%2].
+// An FP8 pool has the same layout with one-byte E4M3 codes: a lane loads
+// 8 bytes per operand and widens them to the 8 bf16 values above (exact),
+// so the MFMAs are the same; the K scale is folded into the softmax scale
+// and the V scale into the final normalisation by the callers.
 #pragma once
 
+#include <type_traits>
+
 #include "decode_common.h"
+#include "fp8.h"
 
 namespace kvp {
 
@@ -26,12 +33,13 @@ typedef __attribute__((ext_vector_type(4))) float float4_v;
 typedef __attribute__((ext_vector_type(4))) unsigned uint4_v;
 typedef __attribute__((ext_vector_type(2))) unsigned uint2_v;
 
-// A block's K and V operands for one wave.
-template <int D>
+// A block's K and V operands for one wave (as loaded: bf16 values, or FP8 codes).
+template <int D, bool FP8 = false>
 struct MfmaTiles {
-  uint4_v k[D / 32];  // token l%16, dims 32kk + 8q .. +7
-  uint4_v v[D / 32];  // tokens 4q..4q+3 of dims 32m + 2(l%16), +1
-  bool bad;           // block id outside the pool: contributes nothing
+  using Op = std::conditional_t<FP8, uint2_v, uint4_v>;
+  Op k[D / 32];  // token l%16, dims 32kk + 8q .. +7
+  Op v[D / 32];  // tokens 4q..4q+3 of dims 32m + 2(l%16), +1
+  bool bad;      // block id outside the pool: contributes nothing
 };
 
 // Per-wave addressing of one KV head's tiles inside a block.
@@ -56,16 +64,18 @@ __device__ __forceinline__ MfmaLanes mfma_lanes(int num_kv_heads, int kvh, int l
 }
 
 // Issue the loads of physical block `id` (checked against the pool size).
-template <int D>
-__device__ __forceinline__ void mfma_issue(MfmaTiles<D>& t, const uint16_t* __restrict__ pool, const MfmaLanes& a,
+template <int D, bool FP8>
+__device__ __forceinline__ void mfma_issue(MfmaTiles<D, FP8>& t, const void* __restrict__ pool, const MfmaLanes& a,
                                            int id, int num_blocks) {
+  using E = std::conditional_t<FP8, uint8_t, uint16_t>;
+  using Op = typename MfmaTiles<D, FP8>::Op;
   t.bad = (unsigned)id >= (unsigned)num_blocks;
   if (t.bad) id = 0;
-  const uint16_t* kt = pool + (size_t)id * a.blk_stride + a.k_off;
+  const E* kt = (const E*)pool + (size_t)id * a.blk_stride + a.k_off;
 #pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk) t.k[kk] = *(const uint4_v*)(kt + a.k_lane + 32 * kk);
+  for (int kk = 0; kk < D / 32; ++kk) t.k[kk] = *(const Op*)(kt + a.k_lane + 32 * kk);
 #pragma unroll
-  for (int m = 0; m < D / 32; ++m) t.v[m] = *(const uint4_v*)(kt + a.v_rel + a.v_lane + 128 * m);
+  for (int m = 0; m < D / 32; ++m) t.v[m] = *(const Op*)(kt + a.v_rel + a.v_lane + 128 * m);
 }
 
 // Running softmax state of one wave for up to 16 query heads of a group.
@@ -93,13 +103,25 @@ struct MfmaRow {
 
   // One block: table entry J of a row whose attended table slots are
   // [so, send) and which uses `nblocks` entries.
-  __device__ __forceinline__ void step(MfmaTiles<D>& t, int J, int so, int send, int nblocks, float scale_log2,
+  template <bool FP8>
+  __device__ __forceinline__ void step(MfmaTiles<D, FP8>& t, int J, int so, int send, int nblocks, float scale_log2,
                                        int lane) {
     const int q4 = lane >> 4;
+    uint4_v kop[D / 32], vop[D / 32];
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      if constexpr (FP8) {
+        kop[kk] = fp8_widen8(t.k[kk]);
+        vop[kk] = fp8_widen8(t.v[kk]);
+      } else {
+        kop[kk] = t.k[kk];
+        vop[kk] = t.v[kk];
+      }
+    }
     float4_v sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk)
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, t.k[kk]),
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, kop[kk]),
                                                      __builtin_bit_cast(bf16x8_v, qop[kk]), sacc, 0, 0, 0);
     float sv[4];
 #pragma unroll
@@ -118,10 +140,10 @@ struct MfmaRow {
       }
 #pragma unroll
       for (int m = 0; m < D / 32; ++m) {
-        t.v[m].x &= vm[0];
-        t.v[m].y &= vm[1];
-        t.v[m].z &= vm[0];
-        t.v[m].w &= vm[1];
+        vop[m].x &= vm[0];
+        vop[m].y &= vm[1];
+        vop[m].z &= vm[0];
+        vop[m].w &= vm[1];
       }
     }
     // The running max is raised only when a score exceeds it by more than
@@ -154,7 +176,7 @@ struct MfmaRow {
     const short4_v pa_lo = __builtin_bit_cast(short4_v, uint2_v{l01, l23});
 #pragma unroll
     for (int m = 0; m < D / 32; ++m) {
-      const short8_v vv = __builtin_bit_cast(short8_v, t.v[m]);
+      const short8_v vv = __builtin_bit_cast(short8_v, vop[m]);
       const short4_v v0 = __builtin_shufflevector(vv, vv, 0, 1, 2, 3);
       const short4_v v1 = __builtin_shufflevector(vv, vv, 4, 5, 6, 7);
       acc[2 * m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa_hi, v0, acc[2 * m], 0, 0, 0);

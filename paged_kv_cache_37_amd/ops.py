@@ -15,7 +15,7 @@ from ._lib import DecodeArgs, KVPoolError, PoolDesc, check, lib
 
 BLOCK_SIZE = 16
 
-_DTYPES = {torch.float32: _lib.KVP_F32, torch.bfloat16: _lib.KVP_BF16}
+_DTYPES = {torch.float32: _lib.KVP_F32, torch.bfloat16: _lib.KVP_BF16, torch.float8_e4m3fn: _lib.KVP_FP8_E4M3}
 _VARIANTS = {"auto": _lib.KVP_VARIANT_AUTO, "valu": _lib.KVP_VARIANT_VALU, "mfma": _lib.KVP_VARIANT_MFMA,
              "stream": _lib.KVP_VARIANT_STREAM}
 
@@ -42,7 +42,13 @@ def _need(t: torch.Tensor, name: str, dtype=None, device=None, shape=None):
 
 class KVPool:
     """A pool of 16-token KV blocks in one torch allocation, with the
-    library handle over it.  Layout: include/kvpool.h."""
+    library handle over it.  Layout: include/kvpool.h.
+
+    dtype is the storage type: float32, bfloat16, or float8_e4m3fn (E4M3
+    codes with one K and one V scale per layer, set by set_fp8_scales).
+    act_dtype is the type of queries, outputs and new tokens: the pool's own
+    type, bfloat16 for an FP8 pool.  The host helpers (flat, load_logical,
+    to_logical) see an FP8 pool's codes as uint8."""
 
     def __init__(self, num_layers: int, num_blocks: int, num_kv_heads: int, head_dim: int,
                  dtype: torch.dtype = torch.bfloat16, device="cuda"):
@@ -57,6 +63,8 @@ class KVPool:
         if self.device.type == "cuda" and self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())
         self.dtype = dtype
+        self.act_dtype = torch.bfloat16 if dtype == torch.float8_e4m3fn else dtype
+        self.elem_dtype = torch.uint8 if dtype == torch.float8_e4m3fn else dtype
         self.num_layers, self.num_blocks = num_layers, num_blocks
         self.num_kv_heads, self.head_dim = num_kv_heads, head_dim
         self.nbytes = int(nbytes)
@@ -74,9 +82,15 @@ class KVPool:
 
     # -- layout helpers (host side; loading and inspecting pools) --------
 
+    def set_fp8_scales(self, layer: int, k_scale: float, v_scale: float) -> None:
+        """An FP8 pool's scales for `layer`: a stored code c stands for
+        c * k_scale (K) or c * v_scale (V).  Both default to 1."""
+        check(lib.kv_pool_set_fp8_scales(self.handle, layer, float(k_scale), float(v_scale)),
+              "kv_pool_set_fp8_scales")
+
     def flat(self) -> torch.Tensor:
-        """The pool as a flat tensor of its dtype."""
-        return self.storage.view(self.dtype)
+        """The pool as a flat tensor of its elements (uint8 codes for FP8)."""
+        return self.storage.view(self.elem_dtype)
 
     def offset(self, layer: int, block: int, kv: int, head: int, slot: int, dim: int) -> int:
         return int(lib.kv_pool_offset(self.handle, layer, block, kv, head, slot, dim))
@@ -92,8 +106,10 @@ class KVPool:
         if tuple(logical.shape) != (L, NB, 2, BLOCK_SIZE, H, D):
             raise ValueError(f"logical pool must be {(L, NB, 2, BLOCK_SIZE, H, D)}, got {tuple(logical.shape)}")
         src = logical.to(device=self.device)
-        if src.dtype != self.dtype:
-            raise ValueError(f"logical pool dtype {src.dtype} != pool dtype {self.dtype}")
+        if src.dtype == torch.float8_e4m3fn:
+            src = src.view(torch.uint8)
+        if src.dtype != self.elem_dtype:
+            raise ValueError(f"logical pool dtype {src.dtype} != pool elements {self.elem_dtype}")
         tiles = self._tiles()
         # K tile [16][D] per (block, head); V tile [4][D][4] (slot t -> (t//4, d, t%4))
         tiles[:, :, 0].view(L, NB, H, BLOCK_SIZE, D).copy_(src[:, :, 0].permute(0, 1, 3, 2, 4))
@@ -121,8 +137,8 @@ def cache_write(pool: KVPool, layer: int, k_new: torch.Tensor, v_new: torch.Tens
     if T < 0:
         raise ValueError("slot_mapping must be 1-D")
     shape = (T, pool.num_kv_heads, pool.head_dim)
-    _need(k_new, "k_new", pool.dtype, pool.device, shape)
-    _need(v_new, "v_new", pool.dtype, pool.device, shape)
+    _need(k_new, "k_new", pool.act_dtype, pool.device, shape)
+    _need(v_new, "v_new", pool.act_dtype, pool.device, shape)
     _need(slot_mapping, "slot_mapping", torch.int32, pool.device)
     check(lib.cache_write(pool.handle, layer, ctypes.c_void_p(k_new.data_ptr()),
                           ctypes.c_void_p(v_new.data_ptr()), ctypes.c_void_p(slot_mapping.data_ptr()), T,
@@ -149,7 +165,7 @@ def _decode_args(pool: KVPool, layer: int, q: torch.Tensor, block_tables: torch.
     if q.dim() != 3:
         raise ValueError("q must be [num_seqs, num_q_heads, head_dim]")
     S, Hq, D = q.shape
-    _need(q, "q", pool.dtype, pool.device)
+    _need(q, "q", pool.act_dtype, pool.device)
     if D != pool.head_dim:
         raise ValueError(f"q head_dim {D} != pool head_dim {pool.head_dim}")
     if block_tables.dim() != 2 or block_tables.shape[0] != S:
@@ -158,7 +174,7 @@ def _decode_args(pool: KVPool, layer: int, q: torch.Tensor, block_tables: torch.
     _need(seq_lens, "seq_lens", torch.int32, pool.device, (S,))
     if out is None:
         out = torch.empty_like(q)
-    _need(out, "out", pool.dtype, pool.device, tuple(q.shape))
+    _need(out, "out", pool.act_dtype, pool.device, tuple(q.shape))
     if variant not in _VARIANTS:
         raise ValueError(f"variant must be one of {sorted(_VARIANTS)}")
     mb = int(block_tables.shape[1])
@@ -206,8 +222,8 @@ def paged_decode_step(pool: KVPool, layer: int, q: torch.Tensor, block_tables: t
     args, out = _decode_args(pool, layer, q, block_tables, seq_lens, scale, out, sliding_window, partition_tokens,
                              variant, workspace, shared_prefix_blocks)
     shape = (q.shape[0], pool.num_kv_heads, pool.head_dim)
-    _need(k_new, "k_new", pool.dtype, pool.device, shape)
-    _need(v_new, "v_new", pool.dtype, pool.device, shape)
+    _need(k_new, "k_new", pool.act_dtype, pool.device, shape)
+    _need(v_new, "v_new", pool.act_dtype, pool.device, shape)
     _need(slot_mapping, "slot_mapping", torch.int32, pool.device, (q.shape[0],))
     check(lib.paged_decode_step(pool.handle, ctypes.byref(args), ctypes.c_void_p(k_new.data_ptr()),
                                 ctypes.c_void_p(v_new.data_ptr()), ctypes.c_void_p(slot_mapping.data_ptr()),

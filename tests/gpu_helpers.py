@@ -20,10 +20,19 @@ def say(*a):
 
 
 def torch_dtype(w):
+    """Type of the workload's queries, outputs and new tokens."""
     return torch.float32 if w.dtype == "f32" else torch.bfloat16
 
 
+def pool_dtype(w):
+    """Storage type of the workload's pool."""
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[w.dtype]
+
+
 def host_to_torch(arr: np.ndarray, dtype: torch.dtype) -> torch.Tensor:
+    """Host bits (uint16 for bf16, uint8 codes for FP8, float32) as a tensor."""
+    if dtype == torch.float8_e4m3fn:
+        return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.uint8))
     if dtype == torch.bfloat16:
         return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
     return torch.from_numpy(np.ascontiguousarray(arr))
@@ -49,8 +58,11 @@ class Dev:
         self.w = w
         self.dt = torch_dtype(w)
         self.ops = ops
-        self.pool = pool or ops.KVPool(w.num_layers, w.num_blocks, w.num_kv_heads, w.head_dim, self.dt, device)
-        self.pool.load_logical(host_to_torch(w.pool, self.dt))
+        self.pool = pool or ops.KVPool(w.num_layers, w.num_blocks, w.num_kv_heads, w.head_dim, pool_dtype(w), device)
+        self.pool.load_logical(host_to_torch(w.pool, pool_dtype(w)))
+        if w.dtype == "fp8":
+            for layer in range(w.num_layers):
+                self.pool.set_fp8_scales(layer, w.k_scale, w.v_scale)
         self.q = host_to_torch(w.q, self.dt).to(device)
         self.tables = torch.from_numpy(np.ascontiguousarray(w.block_tables)).to(device)
         self.lens = torch.from_numpy(np.ascontiguousarray(w.seq_lens)).to(device)
@@ -68,9 +80,11 @@ def reference(w, layer=0, seqs=None, pool=None, q=None, tables=None, lens=None):
     q = w.q if q is None else q
     tables = w.block_tables if tables is None else tables
     lens = w.seq_lens if lens is None else lens
+    ks, vs = w.k_scale, w.v_scale
     if seqs is None:
-        return oracle.decode_attention(pool, layer, q, tables, lens, w.window, w.scale)
-    return np.stack([oracle.decode_attention_seq(pool, layer, q[s], tables[s], int(lens[s]), w.window, w.scale)
+        return oracle.decode_attention(pool, layer, q, tables, lens, w.window, w.scale, k_scale=ks, v_scale=vs)
+    return np.stack([oracle.decode_attention_seq(pool, layer, q[s], tables[s], int(lens[s]), w.window, w.scale,
+                                                 k_scale=ks, v_scale=vs)
                      for s in seqs])
 
 
@@ -81,6 +95,9 @@ def ulp_bf16(x: np.ndarray) -> np.ndarray:
 
 
 def compare(out: torch.Tensor, ref: np.ndarray, dtype: str, what: str = "") -> dict:
+    """fp32 pools: |err| <= F32_ATOL.  bf16 and FP8 pools (bf16 outputs; an
+    FP8 code widens to bf16 exactly, so the same arithmetic follows):
+    |err| <= BF16_ATOL + BF16_RTOL |ref|."""
     got = to_f64(out)
     assert got.shape == ref.shape, (got.shape, ref.shape)
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"

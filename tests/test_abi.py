@@ -152,3 +152,46 @@ def test_cache_write_rejects_bad_arguments(ops):
     assert ops.lib.cache_write(h, 0, None, None, None, 0, None) == 0
     assert ops.lib.kvp_status_str(E.KVP_ERR_WORKSPACE_TOO_SMALL) == b"workspace too small"
     ops.lib.kv_pool_destroy(h)
+
+
+def test_fp8_pool_geometry_and_scales(ops):
+    """An FP8 pool: one byte per element, the same element offsets as the
+    other dtypes, per-layer scales validated on the host."""
+    E = ops._lib
+    d = desc(ops, 3, 10, 2, 128, dtype=E.KVP_FP8_E4M3)
+    assert ops.lib.kv_pool_bytes(ctypes.byref(d)) == 3 * 10 * 2 * 16 * 2 * 128
+    st, h = _handle(ops, d)
+    assert st == 0
+    ref_st, ref = _handle(ops, desc(ops, 3, 10, 2, 128, dtype=E.KVP_BF16))
+    for args in ((0, 0, 0, 0, 0, 0), (2, 9, 1, 1, 15, 127), (1, 4, 1, 0, 6, 33)):
+        assert ops.lib.kv_pool_offset(h, *args) == ops.lib.kv_pool_offset(ref, *args)
+    assert ops.lib.kv_pool_set_fp8_scales(h, 2, 0.5, 3.0) == 0
+    assert ops.lib.kv_pool_set_fp8_scales(h, 3, 0.5, 3.0) == E.KVP_ERR_INVALID_ARG
+    assert ops.lib.kv_pool_set_fp8_scales(h, -1, 0.5, 3.0) == E.KVP_ERR_INVALID_ARG
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        assert ops.lib.kv_pool_set_fp8_scales(h, 0, bad, 1.0) == E.KVP_ERR_INVALID_ARG
+        assert ops.lib.kv_pool_set_fp8_scales(h, 0, 1.0, bad) == E.KVP_ERR_INVALID_ARG
+    assert ops.lib.kv_pool_set_fp8_scales(ref, 0, 1.0, 1.0) == E.KVP_ERR_UNSUPPORTED
+    assert ops.lib.kv_pool_set_fp8_scales(None, 0, 1.0, 1.0) == E.KVP_ERR_INVALID_ARG
+    ops.lib.kv_pool_destroy(h)
+    ops.lib.kv_pool_destroy(ref)
+
+
+def test_fp8_pool_variant_checks(ops):
+    """The VALU variant takes no FP8 pool; the matrix-core variants no fp32
+    pool.  Both are refused before any launch."""
+    E = ops._lib
+    A = ops.DecodeArgs
+    base = dict(layer=0, q=0x1000, out=0x2000, block_tables=0x3000, max_blocks_per_seq=4, seq_lens=0x4000,
+                sliding_window=0, num_seqs=2, num_q_heads=8, scale=0.125, partition_tokens=0, variant=0,
+                workspace=None, workspace_bytes=0)
+    _, h8 = _handle(ops, desc(ops, 1, 8, 2, 64, dtype=E.KVP_FP8_E4M3))
+    _, h32 = _handle(ops, desc(ops, 1, 8, 2, 64, dtype=E.KVP_F32))
+    a = A(**{**base, "variant": E.KVP_VARIANT_VALU})
+    assert ops.lib.paged_decode_attention(h8, ctypes.byref(a), None) == E.KVP_ERR_UNSUPPORTED
+    assert b"VALU" in ops.lib.kvp_last_error()
+    for v in (E.KVP_VARIANT_MFMA, E.KVP_VARIANT_STREAM):
+        a = A(**{**base, "variant": v})
+        assert ops.lib.paged_decode_attention(h32, ctypes.byref(a), None) == E.KVP_ERR_UNSUPPORTED
+    ops.lib.kv_pool_destroy(h8)
+    ops.lib.kv_pool_destroy(h32)

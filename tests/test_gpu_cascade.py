@@ -74,6 +74,37 @@ def test_cascade_shapes(gpu, prefix, Hq, Hkv, D):
     close_to_plain(out_c, out_p, ref, f"prefix {prefix}")
 
 
+@pytest.mark.parametrize("prefix,Hq,Hkv,D", [(2048, 32, 8, 128), (256, 8, 2, 64)])
+def test_cascade_fp8(gpu, prefix, Hq, Hkv, D):
+    """FP8 pools: the prefix pass widens the same codes as the tail pass."""
+    tails = [0, 1, 15, 16, 17, 100, 300, 7]
+    w = W.shared_prefix(950 + prefix + D, prefix, tails, Hq, Hkv, D, dtype="fp8")
+    dev = Dev(w)
+    out_c = dev.attend(shared_prefix_blocks=prefix // 16)
+    out_p = dev.attend()
+    ref = reference(w)
+    compare(out_c, ref, w.dtype, f"fp8 cascade prefix {prefix} D {D}")
+    close_to_plain(out_c, out_p, ref, f"fp8 prefix {prefix}")
+
+
+def test_cascade_fp8_fused_step(gpu):
+    w = W.make(4, dtype="fp8")
+    W.with_next_token(w, w.unused_blocks)
+    dev = Dev(w)
+    dt = dev.dt
+    tables = torch.from_numpy(np.ascontiguousarray(w.block_tables_after)).cuda()
+    lens = torch.from_numpy(np.ascontiguousarray(w.seq_lens_after)).cuda()
+    out = dev.ops.paged_decode_step(dev.pool, 0, dev.q, tables, lens, w.scale, host_to_torch(w.k_new, dt).cuda(),
+                                    host_to_torch(w.v_new, dt).cuda(), torch.from_numpy(w.slot_mapping).cuda(),
+                                    shared_prefix_blocks=128)
+    torch.cuda.synchronize()
+    pool_ref = oracle.cache_write(w.pool, 0, w.k_new, w.v_new, w.slot_mapping, w.k_scale, w.v_scale)
+    assert torch_to_bits(dev.pool.to_logical()).tobytes() == np.ascontiguousarray(pool_ref).tobytes()
+    seqs = list(range(3, w.num_seqs, 9))
+    ref = reference(w, pool=pool_ref, tables=w.block_tables_after, lens=w.seq_lens_after, seqs=seqs)
+    compare(out[seqs], ref, "fp8", "config4-fp8 cascade step")
+
+
 def test_cascade_partial_hint(gpu):
     """A hint shorter than the real shared prefix is still a valid promise."""
     w = W.shared_prefix(77, 160, [5, 40, 0, 33], 8, 2, 128)

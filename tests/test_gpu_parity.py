@@ -223,7 +223,7 @@ def test_needle_is_returned_exactly(gpu, variant, window):
         cands = [first, first + 1, 15, 16, 31, 32, c - 1, (first + c) // 2]
         cands = [p for p in cands if first <= p < c]
         picks.append(cands[s % len(cands)])
-    one = W.f32_to_bf16_bits(np.float32(32.0))
+    one = W.f32_to_bf16_bits(np.array([32.0], dtype=np.float32))[0]
     zero = np.uint16(0)
     for s, pstar in enumerate(picks):
         first = max(0, ctx[s] - window) if window else 0

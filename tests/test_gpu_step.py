@@ -74,7 +74,7 @@ def check_step(w, variant, what, seqs=None, partition_tokens=0, **kw):
     slots = np.asarray(kw.get("slots", w.slot_mapping))
     # the library skips a slot past the pool like a negative one; the oracle skips negatives
     slots = np.where(slots < w.num_blocks * 16, slots, -1).astype(np.int32)
-    pool_ref = oracle.cache_write(w.pool, 0, w.k_new, w.v_new, slots)
+    pool_ref = oracle.cache_write(w.pool, 0, w.k_new, w.v_new, slots, w.k_scale, w.v_scale)
     assert f_pool.tobytes() == np.ascontiguousarray(pool_ref).tobytes(), f"{what}: pool differs from the oracle"
     lens = kw.get("lens", w.seq_lens_after)
     tables = kw.get("tables", w.block_tables_after)
@@ -90,6 +90,24 @@ def test_step_matches_write_then_attend(gpu, config):
     for v in variants:
         seqs = None if config in (1, 5) else list(range(0, w.num_seqs, 7))
         check_step(w, v, f"config{config}", seqs=seqs, partition_tokens=512 if v == "mfma" else 0)
+
+
+@pytest.mark.parametrize("config", [2, 5])
+def test_step_fp8_matches_write_then_attend(gpu, config):
+    """FP8 pools: the fused step stores the new token's codes (the same
+    rounding as cache_write) and attends with them."""
+    w = W.make(config, dtype="fp8")
+    W.with_next_token(w, w.unused_blocks)
+    for v in ("stream", "mfma"):
+        check_step(w, v, f"config{config}-fp8", seqs=list(range(0, w.num_seqs, 7)),
+                   partition_tokens=512 if v == "mfma" else 0)
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,window", [(8, 2, 128, 0), (32, 1, 128, 0), (12, 4, 64, 0), (8, 2, 128, 33)])
+def test_step_fp8_head_groups(gpu, Hq, Hkv, D, window):
+    w = custom_stepped(320 + Hq + D + window, [1, 15, 16, 17, 31, 32, 200, 511], Hq, Hkv, D, window=window,
+                       dtype="fp8")
+    check_step(w, "stream", f"fp8 G{Hq // Hkv}-D{D}-W{window}")
 
 
 @pytest.mark.parametrize("Hq,Hkv,D", [(8, 2, 128), (64, 8, 128), (32, 1, 128), (12, 4, 64), (48, 2, 64)])
