@@ -286,7 +286,8 @@ def main() -> int:
     variant = args.variant
     if variant == "auto":
         variant = "valu" if w.dtype == "f32" else ("mfma" if args.partition_tokens else "stream")
-    label = f"decode_{variant}" if args.unfused else f"decode_{variant}_step"
+    path = "cascade" if shared and variant == "stream" and not w.window else variant
+    label = f"decode_{path}" if args.unfused else f"decode_{path}_step"
     kernel = ("paged_decode_attention (decode + merge launches)" if args.unfused else
               "paged_decode_step (" + ("fused write + decode, merge launches)" if variant == "stream"
                                        else "cache_write, decode, merge launches)"))

@@ -533,9 +533,9 @@ hipError_t launch_sd(const DecodeParams& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if (p.slot_mapping) {
-    // the fused step runs at ring depth 1 (the new token takes the registers of a deeper ring)
-    if constexpr (DEPTH != 1) return hipErrorInvalidValue;
-    else hipLaunchKernelGGL((decode_stream_kernel<D, 1, true, FP8>), dim3(p.stream_wgs), dim3(kThreads), 0, stream, p);
+    // a deeper ring fits beside the new token's registers only with FP8 operands
+    if constexpr (DEPTH != 1 && !FP8) return hipErrorInvalidValue;
+    else hipLaunchKernelGGL((decode_stream_kernel<D, DEPTH, true, FP8>), dim3(p.stream_wgs), dim3(kThreads), 0, stream, p);
   } else {
     hipLaunchKernelGGL((decode_stream_kernel<D, DEPTH, false, FP8>), dim3(p.stream_wgs), dim3(kThreads), 0, stream, p);
   }
@@ -557,7 +557,11 @@ hipError_t launch_s(const DecodeParams& p, hipStream_t stream) {
 
 template <int D, bool FP8>
 const void* symbol_of(int depth, bool fused) {
-  if (fused) return depth == 1 ? (const void*)decode_stream_kernel<D, 1, true, FP8> : nullptr;
+  if (fused) {
+    if (depth == 1) return (const void*)decode_stream_kernel<D, 1, true, FP8>;
+    if constexpr (FP8) return (const void*)decode_stream_kernel<D, 2, true, true>;
+    return nullptr;
+  }
   return depth == 1 ? (const void*)decode_stream_kernel<D, 1, false, FP8> : (const void*)decode_stream_kernel<D, 2, false, FP8>;
 }
 

@@ -86,7 +86,7 @@ hipError_t launch_decode_reduce(const DecodeParams& p, int dtype, int head_dim, 
 hipError_t launch_decode_stream(const DecodeParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_decode_prefix(const DecodeParams& p, int head_dim, hipStream_t stream);
 // The streaming kernel instance a launch would use (for occupancy queries);
-// nullptr for one that is never launched (the fused step runs at depth 1).
+// nullptr for one that is never launched (the bf16 fused step runs at depth 1).
 const void* stream_kernel_symbol(int head_dim, int depth, bool fused, bool fp8);
 
 }  // namespace kvp

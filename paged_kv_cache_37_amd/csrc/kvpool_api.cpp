@@ -191,15 +191,20 @@ enum { PATH_VALU = 0, PATH_MFMA = 1, PATH_STREAM = 2 };
 // Blocks of K/V each wave keeps in flight ahead of the one it computes:
 // KVP_DECODE_DEPTH if set and valid for the path, else the measured best
 // (the streaming kernel keeps every wave busy across rows, so one suffices).
-static int32_t decode_depth(int32_t path) {
+static int32_t decode_depth(int32_t path, bool fp8) {
   static const int env = [] {
     const char* e = getenv("KVP_DECODE_DEPTH");
     return e ? atoi(e) : 0;
   }();
   const int max_depth = path == PATH_MFMA ? 3 : 2;
   if (env >= 1 && env <= max_depth) return env;
+  (void)fp8;  // FP8 tiles carry half the bytes, yet a second one in flight measured no faster
   return path == PATH_MFMA ? 2 : 1;
 }
+
+// Ring depth of the fused step: the new token's registers leave room for a
+// second tile in flight only with FP8 (8-byte) operands.
+static int32_t fused_depth(int32_t depth, bool fp8) { return fp8 ? depth : 1; }
 
 static int32_t plan(kvp_pool pool, int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks, int32_t partition_tokens,
                     int32_t variant, kvp::DecodeParams* p, int32_t* path) {
@@ -223,7 +228,7 @@ static int32_t plan(kvp_pool pool, int32_t num_seqs, int32_t num_q_heads, int32_
         pth = PATH_VALU;
       } else {
         const int32_t wgs =
-            partition_tokens == 0 ? stream_workgroups(d.head_dim, decode_depth(PATH_STREAM), false, fp8) : 0;
+            partition_tokens == 0 ? stream_workgroups(d.head_dim, decode_depth(PATH_STREAM, fp8), false, fp8) : 0;
         pth = wgs > 0 && stream_fits(num_seqs, max_blocks, mfma_groups, wgs) ? PATH_STREAM : PATH_MFMA;
       }
       break;
@@ -268,7 +273,7 @@ static int32_t plan(kvp_pool pool, int32_t num_seqs, int32_t num_q_heads, int32_
   p->qgroups = qgroups;
   p->part_blocks = pb;
   p->num_parts = (max_blocks + pb - 1) / pb;
-  p->depth = decode_depth(pth);
+  p->depth = decode_depth(pth, fp8);
   if (pth == PATH_STREAM) {
     p->stream_wgs = stream_workgroups(d.head_dim, p->depth, false, fp8);
     if (p->stream_wgs <= 0) return fail(KVP_ERR_HIP, "cannot size the streaming grid (no device?)");
@@ -329,7 +334,8 @@ size_t paged_decode_workspace_bytes(kvp_pool pool, int32_t num_seqs, int32_t num
     size_t n = path == PATH_STREAM ? stream_workspace(p, pool->desc.head_dim).total
                                    : grid_workspace(p, pool->desc.head_dim, &a);
     if (path == PATH_STREAM) {  // the fused step's grid (its own occupancy) must fit too
-      p.stream_wgs = stream_workgroups(pool->desc.head_dim, 1, true, pool->desc.dtype == KVP_FP8_E4M3);
+      const bool fp8 = pool->desc.dtype == KVP_FP8_E4M3;
+      p.stream_wgs = stream_workgroups(pool->desc.head_dim, fused_depth(p.depth, fp8), true, fp8);
       const size_t nf = stream_workspace(p, pool->desc.head_dim).total;
       if (nf > n) n = nf;
     }
@@ -365,9 +371,10 @@ static int32_t decode(kvp_pool pool, const kvp_decode_args* a, const void* k_new
       return fail(KVP_ERR_INVALID_ARG, "k_new/v_new must be 16-byte aligned, slot_mapping 4-byte aligned");
   }
   if (write && path == PATH_STREAM) {
-    // the fused kernel holds the new token in registers: ring depth 1
-    p.depth = 1;
-    p.stream_wgs = stream_workgroups(d.head_dim, 1, true, d.dtype == KVP_FP8_E4M3);
+    // the fused kernel holds the new token in registers
+    const bool fp8 = d.dtype == KVP_FP8_E4M3;
+    p.depth = fused_depth(p.depth, fp8);
+    p.stream_wgs = stream_workgroups(d.head_dim, p.depth, true, fp8);
     if (p.stream_wgs <= 0) return fail(KVP_ERR_HIP, "cannot size the streaming grid (no device?)");
     p.k_new = k_new;
     p.v_new = v_new;
