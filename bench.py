@@ -9,6 +9,7 @@ paged_decode_step call (the streaming kernel fuses the write), or with
 served from the 256 MB last-level cache.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--kv-dtype bf16|fp8]
+                    [--block-size 16|32]
 
 Prints one JSON line.  `value` is the step's algorithmic bytes (K/V of the
 attended slots, each physical slot once, queries, outputs, tables, the
@@ -33,7 +34,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention: achieved HBM GB/s (% of peak) + seq·layer steps/s"
 HBM_PEAK_GBS = 8000.0
-DEFAULT_LAYERS = {1: 1, 2: 2, 3: 1, 4: 4, 5: 2}  # layer slices so that each step reads >= ~1 GB
+DEFAULT_LAYERS = {1: 1, 2: 2, 3: 1, 4: 4, 5: 2, 6: 1}  # layer slices so that each step reads >= ~1 GB
 KERNEL_SOURCES = ("decode_stream.hip", "decode_prefix.hip", "copy_blocks.hip", "decode_mfma.hip", "decode_valu.hip",
                   "decode_reduce.hip", "cache_write.hip", "mfma_tile.h", "decode_common.h", "internal.h",
                   "fp8.h", "kvpool_api.cpp")
@@ -94,9 +95,10 @@ def attended_slots(w) -> int:
     for s in range(w.num_seqs):
         ctx = int(w.seq_lens_after[s])
         first = max(0, ctx - w.window) if w.window else 0
-        so = first % 16
+        B = w.block_size
+        so = first % B
         idx = np.arange(so, so + ctx - first)
-        slots.append(w.block_tables_after[s][idx // 16].astype(np.int64) * 16 + idx % 16)
+        slots.append(w.block_tables_after[s][idx // B].astype(np.int64) * B + idx % B)
     return int(np.unique(np.concatenate(slots)).size) if slots else 0
 
 
@@ -138,9 +140,11 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5, 6],
+                    help="2..5 as in the workload generator; 6 = 16 long contexts (32k..40k tokens)")
     ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
                     help="pool storage: bf16, or FP8 E4M3 codes with per-layer scales")
+    ap.add_argument("--block-size", type=int, default=16, choices=[16, 32], help="tokens per KV block")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None, help="layer slices to rotate over")
     ap.add_argument("--variant", default="auto", choices=["auto", "stream", "mfma", "valu"])
@@ -175,7 +179,7 @@ def main() -> int:
     L = args.layers or DEFAULT_LAYERS[args.config] * (2 if args.kv_dtype == "fp8" else 1)
     log(f"generating config {args.config} with {L} layer slice(s)")
     t0 = time.time()
-    w = W.make(args.config, args.seed, num_layers=L, dtype=args.kv_dtype)
+    w = W.make(args.config, args.seed, num_layers=L, dtype=args.kv_dtype, block_size=args.block_size)
     W.with_next_token(w, w.unused_blocks)
     log(f"generated in {time.time() - t0:.1f}s: {w.name}, {w.num_blocks} blocks/layer")
 
@@ -188,7 +192,7 @@ def main() -> int:
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
 
-    pool = ops.KVPool(L, w.num_blocks, w.num_kv_heads, w.head_dim, pool_dt, dev)
+    pool = ops.KVPool(L, w.num_blocks, w.num_kv_heads, w.head_dim, pool_dt, dev, block_size=w.block_size)
     if w.dtype == "bf16":
         pool.load_logical(torch.from_numpy(w.pool.view(np.int16)).view(torch.bfloat16))
     else:
@@ -204,7 +208,8 @@ def main() -> int:
     out = torch.empty_like(q)
     ws = ops.make_workspace(pool, w.num_seqs, w.num_q_heads, tables.shape[1], args.partition_tokens)
     # blocks every row shares (a cached prompt prefix): attended once for the batch
-    shared = 0 if args.no_shared_prefix else shared_prefix_blocks(np.asarray(w.block_tables_after), w.seq_lens_after)
+    shared = 0 if args.no_shared_prefix else shared_prefix_blocks(np.asarray(w.block_tables_after), w.seq_lens_after,
+                                                                  block_size=w.block_size)
     log(f"shared prefix: {shared} blocks")
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
@@ -312,7 +317,7 @@ def main() -> int:
             "num_q_heads": Hq,
             "num_kv_heads": Hkv,
             "head_dim": D,
-            "block_size": 16,
+            "block_size": w.block_size,
             "context_tokens_total": int(valid_after.sum()),
             "sliding_window": w.window,
             "layer_slices": L,

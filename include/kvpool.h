@@ -2,8 +2,8 @@
  * kvpool.h -- C ABI of the MI355X (gfx950) paged KV-cache library.
  *
  * One hot path: decode attention over a KV cache held in a pool of fixed
- * 16-token blocks, and the cache write that stores each new token's K and V
- * into its slot.  Sources (page titles as printed):
+ * 16-token (or 32-token) blocks, and the cache write that stores each new
+ * token's K and V into its slot.  Sources (page titles as printed):
  *
  *  [Optimizing] "Optimizing KV Cache Memory Management in vLLM with
  *     PagedAttention and Dynamic Block Allocation"
@@ -14,7 +14,9 @@
  *         (Prefill / Decode phases): prompt and decode K/V are written into
  *         the physical blocks; decode appends into the last block;
  *       - section "The Math of the KV Cache Bottleneck": GQA/MQA, fewer KV
- *         heads than query heads.
+ *         heads than query heads;
+ *       - section "Trade-offs of Block Size Tuning": block size 16 is the
+ *         default, 32 is offered for very long contexts.
  *  [Paged] the paged-attention post on zhangchitc.github.io
  *       - section "What a physical block looks like": the pool is split per
  *         layer into num_blocks blocks of [2, block_size, num_kv_heads,
@@ -42,7 +44,8 @@
  *    thread-local message.
  *  - Device data are not validated on the fast path, but kernels never
  *    read or write outside the pool, the table row, or the output: a slot or
- *    block id outside [0, num_blocks*16) / [0, num_blocks) is skipped.
+ *    block id outside [0, num_blocks*block_size) / [0, num_blocks) is
+ *    skipped.
  */
 #ifndef KVPOOL_H
 #define KVPOOL_H
@@ -89,13 +92,14 @@ typedef enum {
 } kvp_variant;
 
 /*
- * Pool geometry.  block_size must be 16 (the pages' default block).
- * head_dim 64 or 128.  dtype a kvp_dtype.
+ * Pool geometry.  block_size 16 (the pages' default block) or 32 ([Optimizing]
+ * "Trade-offs of Block Size Tuning").  head_dim 64 or 128.  dtype a
+ * kvp_dtype.  num_blocks * block_size must fit in int32.
  */
 typedef struct {
   int32_t num_layers;
   int32_t num_blocks;     /* physical blocks per layer */
-  int32_t block_size;     /* == 16 */
+  int32_t block_size;     /* 16 or 32 */
   int32_t num_kv_heads;
   int32_t head_dim;       /* 64 or 128 */
   int32_t dtype;          /* kvp_dtype */
@@ -105,16 +109,17 @@ typedef struct kvp_pool_s* kvp_pool;  /* opaque, immutable after create */
 
 /*
  * Device layout of the pool (elements of the pool dtype).  For layer l,
- * physical block b, KV head h, slot t (0..15) and dimension d:
+ * physical block b, KV head h, slot t (0..B-1, B = block_size) and
+ * dimension d:
  *
- *   blk   = (l * num_blocks + b) * 2 * num_kv_heads * 16 * head_dim
- *   K(t,d) = blk + (              h) * 16 * head_dim + t * head_dim + d
- *   V(t,d) = blk + (num_kv_heads + h) * 16 * head_dim
+ *   blk   = (l * num_blocks + b) * 2 * num_kv_heads * B * head_dim
+ *   K(t,d) = blk + (              h) * B * head_dim + t * head_dim + d
+ *   V(t,d) = blk + (num_kv_heads + h) * B * head_dim
  *                + ((t / 4) * head_dim + d) * 4 + (t % 4)
  *
  * i.e. per block all K tiles, then all V tiles; a (block, head) K tile is
- * one contiguous row-major [16][head_dim] array and a V tile is
- * [4][head_dim][4]: for each group of four slots, the four slots' values
+ * one contiguous row-major [B][head_dim] array and a V tile is
+ * [B/4][head_dim][4]: for each group of four slots, the four slots' values
  * of one dimension sit next to each other.  This is the pages' block shape
  * [2, block_size, num_kv_heads, head_dim] with heads moved outside slots
  * (one contiguous tile per head) and V's slots interleaved in fours, which
@@ -130,7 +135,7 @@ size_t kv_pool_bytes(const kvp_pool_desc* desc);
  * bytes (>= kv_pool_bytes(desc), 256-byte aligned).  The memory is not
  * touched.  The handle borrows dev_base and must not outlive it.
  * Errors: KVP_ERR_INVALID_ARG (null pointers, misalignment, too small),
- * KVP_ERR_UNSUPPORTED (block_size != 16, head_dim not 64/128, dtype).
+ * KVP_ERR_UNSUPPORTED (block_size not 16/32, head_dim not 64/128, dtype).
  */
 int32_t kv_pool_create(const kvp_pool_desc* desc, void* dev_base, size_t bytes, kvp_pool* out);
 
@@ -166,10 +171,10 @@ int64_t kv_pool_offset(kvp_pool pool, int32_t layer, int32_t block, int32_t kv, 
  *
  *   k_new, v_new : device, [num_tokens][num_kv_heads][head_dim], pool dtype
  *                  (BF16 for an FP8 pool), contiguous.
- *   slot_mapping : device int32 [num_tokens]; slot = block * 16 + offset
+ *   slot_mapping : device int32 [num_tokens]; slot = block * B + offset
  *                  ([Optimizing] "PagedAttention": floor(i/B), i mod B).
  *                  A negative slot (padding) writes nothing; a slot
- *                  >= num_blocks*16 writes nothing.  Two tokens naming the
+ *                  >= num_blocks*B writes nothing.  Two tokens naming the
  *                  same slot in one call leave that slot undefined.
  *   The copy is bit-exact.  An FP8 pool stores codes instead: each value x
  *   becomes the E4M3 code nearest to x * (1 / scale) (reciprocal and product
@@ -218,11 +223,11 @@ size_t paged_decode_workspace_bytes(kvp_pool pool, int32_t num_seqs, int32_t num
  *   says it lives.
  *
  *   Rows.  With sliding_window == 0, row s lists logical blocks
- *   0 .. (ctx-1)/16 and all ctx = seq_lens[s] tokens are attended.  With a
- *   window W > 0 ([Pool] "Hybrid models get groups") row s lists only the
- *   blocks covering positions max(0, ctx-W) .. ctx-1: logical blocks
- *   max(0,ctx-W)/16 .. (ctx-1)/16; the first max(0,ctx-W) % 16 slots of
- *   its first block are not attended.  Entries past the row's length are
+ *   0 .. (ctx-1)/B and all ctx = seq_lens[s] tokens are attended (B =
+ *   block_size).  With a window W > 0 ([Pool] "Hybrid models get groups")
+ *   row s lists only the blocks covering positions max(0, ctx-W) .. ctx-1:
+ *   logical blocks max(0,ctx-W)/B .. (ctx-1)/B; the first
+ *   max(0,ctx-W) % B slots of its first block are not attended.  Entries past the row's length are
  *   never read.  A row with ctx == 0 yields zeros.
  *
  *   out[s][h] = sum_i p_i V_i with p = softmax(K q[s][h] * scale) over the
@@ -249,7 +254,7 @@ int32_t paged_decode_attention(kvp_pool pool, const kvp_decode_args* args, hipSt
 /*
  *   Shared prefix (cascade).  shared_prefix_blocks = P > 0 promises that the
  *   first P entries of every row are the same physical blocks, all full and
- *   all attended (seq_lens[s] >= 16 P): a prompt prefix that every sequence
+ *   all attended (seq_lens[s] >= B P): a prompt prefix that every sequence
  *   of the batch reuses ([Pool] "Finding a prefix again"; [Memory] "How
  *   vLLM recognizes a reusable prefix": only full blocks are shared).  The
  *   STREAM variant then attends the prefix once per KV head for all
@@ -278,7 +283,7 @@ int32_t paged_decode_attention(kvp_pool pool, const kvp_decode_args* args, hipSt
  *                  which must be the slot of position seq_lens[s]-1 of row s
  *                  (in the row's last block, a block no other sequence
  *                  uses: copy-on-write happens first).  Negative: s has no
- *                  new token (attention only); >= num_blocks*16: nothing
+ *                  new token (attention only); >= num_blocks*B: nothing
  *                  is written.
  *
  *   Result: the pool and out are bit-identical to cache_write(num_seqs

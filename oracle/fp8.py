@@ -66,6 +66,6 @@ def quantize(x, scale: float) -> np.ndarray:
     if x.dtype == np.uint16:
         x = (x.astype(np.uint32) << 16).view(np.float32)
     inv = np.float32(1.0) / np.float32(scale)
-    with np.errstate(over="ignore"):  # a product past float32's range is inf and saturates
+    with np.errstate(over="ignore", invalid="ignore"):  # past float32's range: inf, saturates; NaN stays NaN
         y = (x.astype(np.float32) * inv).astype(np.float32)
     return e4m3_encode(y)

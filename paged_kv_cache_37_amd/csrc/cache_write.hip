@@ -4,13 +4,13 @@
 // Dynamic Block Allocation", section The Block Manager and Dynamic
 // Allocation Lifecycle: prefill writes the prompt's K/V into its blocks,
 // decode writes the new token's K/V into the free slot of the last block.
-// A slot is block * 16 + offset (section PagedAttention: Virtual Memory for
-// LLMs: block floor(i/B), offset i mod B).
+// A slot is block * B + offset (section PagedAttention: Virtual Memory for
+// LLMs: block floor(i/B), offset i mod B), B = 16 << bshift.
 //
 // One work item = (token, KV head, 16-byte chunk of head_dim): the K chunk
 // is one 16-byte store into the row of the K tile; the V chunk's elements go
 // to the quad-interleaved V tile ([4][D][4]: slot t of dimension d at
-// ((t/4)*D + d)*4 + t%4).  Bits are copied, never converted, except into an
+// ((t/4)*D + d)*4 + t%4, t < block size: 16 or 32).  Bits are copied, never converted, except into an
 // FP8 pool, where each bf16 value becomes its E4M3 code (fp8.h: nearest code
 // of x * (1 / scale), saturating) and a chunk is 8 values.
 #include "fp8.h"
@@ -24,19 +24,20 @@ template <typename W>  // W = element bits: uint16_t (bf16) or uint32_t (fp32)
 __global__ __launch_bounds__(256) void cache_write_kernel(W* __restrict__ pool, const W* __restrict__ k_new,
                                                           const W* __restrict__ v_new,
                                                           const int32_t* __restrict__ slots, int num_tokens,
-                                                          int num_blocks, int num_kv_heads, int D) {
+                                                          int num_blocks, int bshift, int num_kv_heads, int D) {
   constexpr int E = 16 / sizeof(W);
   const int chunks = D / E;
   const long items = (long)num_tokens * num_kv_heads * chunks;
-  const size_t tile = (size_t)16 * D;
+  const int B = 16 << bshift;
+  const size_t tile = (size_t)B * D;
   for (long it = (long)blockIdx.x * 256 + threadIdx.x; it < items; it += (long)gridDim.x * 256) {
     const int c = (int)(it % chunks);
     const long th = it / chunks;
     const int h = (int)(th % num_kv_heads);
     const int t = (int)(th / num_kv_heads);
     const int slot = slots[t];
-    if (slot < 0 || slot >= num_blocks * 16) continue;
-    const int blk = slot >> 4, off = slot & 15;
+    if (slot < 0 || slot >= num_blocks * B) continue;
+    const int blk = slot >> (4 + bshift), off = slot & (B - 1);
     W* base = pool + (size_t)blk * 2 * num_kv_heads * tile;
     const size_t src = ((size_t)t * num_kv_heads + h) * D + (size_t)c * E;
     *(uint4v*)(base + h * tile + (size_t)off * D + (size_t)c * E) = *(const uint4v*)(k_new + src);
@@ -54,19 +55,20 @@ __global__ __launch_bounds__(256) void cache_write_fp8_kernel(uint8_t* __restric
                                                               const uint16_t* __restrict__ k_new,
                                                               const uint16_t* __restrict__ v_new,
                                                               const int32_t* __restrict__ slots, int num_tokens,
-                                                              int num_blocks, int num_kv_heads, int D, float inv_k,
-                                                              float inv_v) {
+                                                              int num_blocks, int bshift, int num_kv_heads, int D,
+                                                              float inv_k, float inv_v) {
   const int chunks = D / 8;
   const long items = (long)num_tokens * num_kv_heads * chunks;
-  const size_t tile = (size_t)16 * D;
+  const int B = 16 << bshift;
+  const size_t tile = (size_t)B * D;
   for (long it = (long)blockIdx.x * 256 + threadIdx.x; it < items; it += (long)gridDim.x * 256) {
     const int c = (int)(it % chunks);
     const long th = it / chunks;
     const int h = (int)(th % num_kv_heads);
     const int t = (int)(th / num_kv_heads);
     const int slot = slots[t];
-    if (slot < 0 || slot >= num_blocks * 16) continue;
-    const int blk = slot >> 4, off = slot & 15;
+    if (slot < 0 || slot >= num_blocks * B) continue;
+    const int blk = slot >> (4 + bshift), off = slot & (B - 1);
     uint8_t* base = pool + (size_t)blk * 2 * num_kv_heads * tile;
     const size_t src = ((size_t)t * num_kv_heads + h) * D + (size_t)c * 8;
     *(fp8_u2*)(base + h * tile + (size_t)off * D + (size_t)c * 8) = fp8_quant8(*(const fp8_u4*)(k_new + src), inv_k);
@@ -79,7 +81,7 @@ __global__ __launch_bounds__(256) void cache_write_fp8_kernel(uint8_t* __restric
 
 }  // namespace
 
-hipError_t launch_cache_write(void* pool_layer, int dtype, int num_blocks, int num_kv_heads, int head_dim,
+hipError_t launch_cache_write(void* pool_layer, int dtype, int num_blocks, int bshift, int num_kv_heads, int head_dim,
                               const void* k_new, const void* v_new, const int32_t* slots, int num_tokens,
                               float inv_k_scale, float inv_v_scale, hipStream_t stream) {
   const int E = dtype == 0 ? 4 : 8;
@@ -89,15 +91,15 @@ hipError_t launch_cache_write(void* pool_layer, int dtype, int num_blocks, int n
   if (blocks < 1) blocks = 1;
   if (dtype == 2)
     hipLaunchKernelGGL(cache_write_fp8_kernel, dim3(blocks), dim3(256), 0, stream, (uint8_t*)pool_layer,
-                       (const uint16_t*)k_new, (const uint16_t*)v_new, slots, num_tokens, num_blocks, num_kv_heads,
-                       head_dim, inv_k_scale, inv_v_scale);
+                       (const uint16_t*)k_new, (const uint16_t*)v_new, slots, num_tokens, num_blocks, bshift,
+                       num_kv_heads, head_dim, inv_k_scale, inv_v_scale);
   else if (dtype == 1)
     hipLaunchKernelGGL(cache_write_kernel<uint16_t>, dim3(blocks), dim3(256), 0, stream, (uint16_t*)pool_layer,
-                       (const uint16_t*)k_new, (const uint16_t*)v_new, slots, num_tokens, num_blocks,
+                       (const uint16_t*)k_new, (const uint16_t*)v_new, slots, num_tokens, num_blocks, bshift,
                        num_kv_heads, head_dim);
   else
     hipLaunchKernelGGL(cache_write_kernel<uint32_t>, dim3(blocks), dim3(256), 0, stream, (uint32_t*)pool_layer,
-                       (const uint32_t*)k_new, (const uint32_t*)v_new, slots, num_tokens, num_blocks,
+                       (const uint32_t*)k_new, (const uint32_t*)v_new, slots, num_tokens, num_blocks, bshift,
                        num_kv_heads, head_dim);
   return hipGetLastError();
 }

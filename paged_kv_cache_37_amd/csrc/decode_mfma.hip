@@ -41,15 +41,20 @@ __global__ __launch_bounds__(kThreads, KVP_MFMA_WAVES_PER_EU) void decode_mfma_k
   const int h0 = kvh * P.group + qg * P.heads_per_wg;
   const int nh = min(P.heads_per_wg, P.group - qg * P.heads_per_wg);
 
-  // The sequence length, this partition's table entries (lane i holds entry
-  // part * part_blocks + i, read whenever it lies inside the table row) and
-  // the queries are independent loads, issued together.
+  // Lane i holds the id of tile part * part_blocks + i of the row.  With
+  // 16-token blocks tile j is table entry j, and the sequence length, the
+  // table entries and the queries are independent loads, issued together;
+  // 32-token blocks need the length first (a window may start in a block's
+  // second tile).
   const int ctx = P.seq_lens[s];
-  const int32_t* row = P.block_tables + (size_t)s * P.max_blocks + part * P.part_blocks;
-  const int my_id = lane < P.part_blocks && part * P.part_blocks + lane < P.max_blocks ? row[lane] : 0;
+  const int32_t* row = P.block_tables + (size_t)s * P.max_blocks;
+  const int jl = part * P.part_blocks + lane;
+  int my_id = -1;
+  if (P.bshift == 0 && lane < P.part_blocks && jl < P.max_blocks) my_id = tile_id(row, jl, 0, P.num_blocks);
   MfmaRow<D> st;
   st.load_q((const uint16_t*)P.q, (size_t)s * P.num_q_heads + h0, nh, lane);
-  const RowSpan rs = row_span(ctx, P.window, P.max_blocks);
+  const RowSpan rs = row_span(ctx, P.window, P.max_blocks, P.bshift);
+  if (P.bshift != 0 && lane < P.part_blocks && jl < rs.nblocks) my_id = tile_id(row, rs.t0 + jl, P.bshift, P.num_blocks);
   const int nparts = (rs.nblocks + P.part_blocks - 1) / P.part_blocks;
   if (rs.nblocks == 0) {
     if (part == 0)
@@ -62,12 +67,12 @@ __global__ __launch_bounds__(kThreads, KVP_MFMA_WAVES_PER_EU) void decode_mfma_k
   const int nbp = min(P.part_blocks, rs.nblocks - jb);
 
   const void* pool = P.pool_layer;
-  const MfmaLanes la = mfma_lanes<D>(P.num_kv_heads, kvh, lane);
+  const MfmaLanes la = mfma_lanes<D>(P.num_kv_heads, kvh, lane, P.bshift);
   st.reset();
   const int so = rs.start_off;
   const int send = rs.start_off + rs.n;
 
-  // Table entries of this wave: wave, wave + 4, ...; `cnt` of them.
+  // Tiles of this wave: wave, wave + 4, ...; `cnt` of them.
   const int cnt = nbp > wave ? (nbp - wave + kWaves - 1) / kWaves : 0;
   auto issue = [&](int k, MfmaTiles<D, FP8>& t) {
     const int kc = k < cnt ? k : cnt - 1;  // past the end: re-read the last block (a cache hit)

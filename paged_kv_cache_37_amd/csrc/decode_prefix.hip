@@ -54,18 +54,19 @@ __global__ __launch_bounds__(kThreads, 2) void decode_prefix_kernel(const Decode
   }
   st.reset();
 
-  // This wave's contiguous quarter of the prefix blocks; their ids (the
-  // first entries of row 0, the same in every row) 64 at a time.
-  const int nb = P.prefix_blocks;
+  // This wave's contiguous quarter of the prefix tiles (16 tokens each; a
+  // 32-token block holds two); their ids from the first entries of row 0,
+  // the same in every row.
+  const int nb = P.prefix_blocks << P.bshift;
   const int j0 = (int)(((long long)nb * wave) >> 2), j1 = (int)(((long long)nb * (wave + 1)) >> 2);
   const int cnt = j1 - j0;
-  // The wave's block ids, staged in LDS.  The row tiles of one KV head all
-  // read the same blocks: each tile starts its walk at a different block, so
-  // that concurrent waves spread over the L2 channels.
-  for (int i = lane; i < cnt; i += 64) ids_s[wave][i] = P.block_tables[j0 + i];
+  // The wave's tile ids, staged in LDS.  The row tiles of one KV head all
+  // read the same blocks: each starts its walk at a different tile, so that
+  // concurrent waves spread over the L2 channels.
+  for (int i = lane; i < cnt; i += 64) ids_s[wave][i] = tile_id(P.block_tables, j0 + i, P.bshift, P.num_blocks);
   const int rot = cnt > 0 ? (int)(((long long)tile * 37) % cnt) : 0;
   const void* pool = P.pool_layer;
-  const MfmaLanes la = mfma_lanes<D>(P.num_kv_heads, kvh, lane);
+  const MfmaLanes la = mfma_lanes<D>(P.num_kv_heads, kvh, lane, P.bshift);
   int issued = 0;
   auto issue = [&](MfmaTiles<D, FP8>& t) {
     const int k = issued < cnt ? issued : cnt - 1;  // past the end: re-read the last block (a cache hit)
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_prefix_kernel(const Decode
         if (k0 + u >= cnt) break;
         issue(buf[(u + DEPTH) % NBUF]);
         __builtin_amdgcn_sched_barrier(0);
-        // every prefix block is full: only a block id outside the pool is masked
+        // every prefix block is full: only a tile outside the pool is masked
         st.step(buf[u], 0, 0, nb * kBlock, nb, P.scale_log2, lane);
       }
     }

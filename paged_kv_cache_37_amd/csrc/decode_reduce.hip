@@ -17,7 +17,7 @@ constexpr int kRowsPerWg = 4;  // waves, one query-head row each
 template <int D, typename OutT>
 __global__ __launch_bounds__(64 * kRowsPerWg) void decode_reduce_kernel(const DecodeParams P) {
   const int s = blockIdx.y;
-  const RowSpan rs = row_span(P.seq_lens[s], P.window, P.max_blocks);
+  const RowSpan rs = row_span(P.seq_lens[s], P.window, P.max_blocks, P.bshift);
   const int nparts = (rs.nblocks + P.part_blocks - 1) / P.part_blocks;
   if (nparts <= 1) return;
   const int h = blockIdx.x * kRowsPerWg + (threadIdx.x >> 6);

@@ -2,9 +2,10 @@
 // form: a persistent grid of exactly the resident waves splits the batch's
 // work evenly, whatever the mix of sequence lengths.
 //
-// The work is the list of tiles (head group, sequence, table entry): row
-// (hg, s) has one tile per block-table entry of sequence s, each tile being
-// one 16-token block of K/V for that KV head ("PagedAttention: Virtual
+// The work is the list of tiles (head group, sequence, tile): row (hg, s)
+// has one tile per 16 tokens of sequence s's blocks (one per block-table
+// entry, two with 32-token blocks), each tile being 16 tokens of K/V for
+// that KV head ("PagedAttention: Virtual
 // Memory for LLMs" in "Optimizing KV Cache Memory Management in vLLM with
 // PagedAttention and Dynamic Block Allocation": the kernel walks the
 // sequence's block table to find each block).  Wave w streams the
@@ -80,13 +81,15 @@ struct StreamTile {
 template <int D, int DEPTH, bool FUSED, bool FP8>
 __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stream_kernel(const DecodeParams P) {
   constexpr int NBUF = DEPTH + 1;
-  __shared__ int pre[kMaxStreamSeqs + 1];  // pre[s] = table entries of sequences < s
+  __shared__ int pre[kMaxStreamSeqs + 1];  // pre[s] = tiles of sequences < s
+  __shared__ uint8_t t0s[kMaxStreamSeqs];  // the first attended tile's place in its block (32-token blocks)
   __shared__ int wsum[kWaves];
+  const int ptiles = P.prefix_blocks << P.bshift;  // tiles of the shared prefix (cascade)
   const int S = P.num_seqs;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  // Entries per sequence and their prefix sums: each thread a contiguous run
+  // Tiles per sequence and their prefix sums: each thread a contiguous run
   // of sequences, a wave scan of the runs, then the waves' totals.
   {
     const int per = (S + kThreads - 1) / kThreads;
@@ -95,8 +98,10 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
     for (int i = 0; i < per; ++i) {
       const int s = s0 + i;
       if (s < S) {
-        const int nb = max(row_span(P.seq_lens[s], P.window, P.max_blocks).nblocks - P.prefix_blocks, 0);
+        const RowSpan rs = row_span(P.seq_lens[s], P.window, P.max_blocks, P.bshift);
+        const int nb = max(rs.nblocks - ptiles, 0);
         pre[s + 1] = nb;
+        t0s[s] = (uint8_t)rs.t0;
         local += nb;
       }
     }
@@ -164,17 +169,21 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
     return min(P.heads_per_wg, P.group - (hg - kvh * P.qgroups) * P.heads_per_wg);
   };
 
+  // Tile id of tile j (counted after the shared prefix) of sequence s's row.
+  auto tid = [&](int s, int j) {
+    return tile_id(P.block_tables + (size_t)s * P.max_blocks, t0s[s] + ptiles + j, P.bshift, P.num_blocks);
+  };
+
   // ---- issue side: walks the range DEPTH tiles ahead of the compute ----
   RowCtx ir = row_at(t_begin);  // row of the next tile to issue
   int ij = (int)(t_begin - ir.a);
   int irow_id = 0;
-  const int32_t* irow = P.block_tables + (size_t)ir.s * P.max_blocks + P.prefix_blocks;
-  int ids_a = ij + lane < ir.nb ? irow[ij + lane] : 0;            // entries ij .. ij+63
-  int ids_b = ij + 64 + lane < ir.nb ? irow[ij + 64 + lane] : 0;  // entries ij+64 .. ij+127
-  int ids_base = ij;                                               // entry held by lane 0 of ids_a
-  RowCtx nr = row_after(ir);                                       // the row after, prefetched
-  int ids_n = lane < nr.nb ? P.block_tables[(size_t)nr.s * P.max_blocks + P.prefix_blocks + lane] : 0;
-  MfmaLanes ila = mfma_lanes<D>(P.num_kv_heads, ir.hg / P.qgroups, lane);
+  int ids_a = ij + lane < ir.nb ? tid(ir.s, ij + lane) : -1;            // tiles ij .. ij+63
+  int ids_b = ij + 64 + lane < ir.nb ? tid(ir.s, ij + 64 + lane) : -1;  // tiles ij+64 .. ij+127
+  int ids_base = ij;                                                     // tile held by lane 0 of ids_a
+  RowCtx nr = row_after(ir);                                             // the row after, prefetched
+  int ids_n = lane < nr.nb ? tid(nr.s, lane) : -1;
+  MfmaLanes ila = mfma_lanes<D>(P.num_kv_heads, ir.hg / P.qgroups, lane, P.bshift);
   int issued = 0;
 
   auto issue = [&](StreamTile<D, FP8>& x) {
@@ -189,17 +198,16 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
       ir = nr;
       ij = 0;
       ++irow_id;
-      irow = P.block_tables + (size_t)ir.s * P.max_blocks + P.prefix_blocks;
       ids_a = ids_n;
-      ids_b = 64 + lane < ir.nb ? irow[64 + lane] : 0;
+      ids_b = 64 + lane < ir.nb ? tid(ir.s, 64 + lane) : -1;
       ids_base = 0;
       nr = row_after(ir);
-      ids_n = lane < nr.nb ? P.block_tables[(size_t)nr.s * P.max_blocks + P.prefix_blocks + lane] : 0;
-      ila = mfma_lanes<D>(P.num_kv_heads, ir.hg / P.qgroups, lane);
-    } else if (ij - ids_base == 64) {  // next chunk of 64 entries: rotate, fetch the one after
+      ids_n = lane < nr.nb ? tid(nr.s, lane) : -1;
+      ila = mfma_lanes<D>(P.num_kv_heads, ir.hg / P.qgroups, lane, P.bshift);
+    } else if (ij - ids_base == 64) {  // next chunk of 64 tiles: rotate, fetch the one after
       ids_a = ids_b;
       ids_base += 64;
-      ids_b = ids_base + 64 + lane < ir.nb ? irow[ids_base + 64 + lane] : 0;
+      ids_b = ids_base + 64 + lane < ir.nb ? tid(ir.s, ids_base + 64 + lane) : -1;
     }
     mfma_issue(x.t, pool, ila, __builtin_amdgcn_readlane(ids_a, ij - ids_base), P.num_blocks);
     x.j = ij;
@@ -212,7 +220,7 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
   RowCtx cr = row_at(t_begin);
   int crow_id = 0;
   int c_h0 = head0(cr.hg), c_nh = heads(cr.hg);
-  RowSpan crs = row_span(P.seq_lens[cr.s], P.window, P.max_blocks);
+  RowSpan crs = row_span(P.seq_lens[cr.s], P.window, P.max_blocks, P.bshift);
   MfmaRow<D> st;
   st.load_q(q, (size_t)cr.s * P.num_q_heads + c_h0, c_nh, lane);
   st.reset();
@@ -292,7 +300,7 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
   auto load_new = [&](const RowCtx& r, uint4_v& kd, unsigned& vd, int& sd) {
     if constexpr (FUSED) {
       const int sl = __builtin_amdgcn_readfirstlane(P.slot_mapping[r.s]);
-      sd = sl >= 0 && sl < P.num_blocks * kBlock ? sl : -1;
+      sd = sl >= 0 && sl < (P.num_blocks << (4 + P.bshift)) ? sl : -1;
       const size_t tok = ((size_t)r.s * P.num_kv_heads + r.hg / P.qgroups) * D;
       kd = lane < D / 8 ? ((const uint4_v*)((const uint16_t*)P.k_new + tok))[lane] : uint4_v{0, 0, 0, 0};
       vd = lane < D / 2 ? ((const unsigned*)((const uint16_t*)P.v_new + tok))[lane] : 0u;
@@ -307,10 +315,11 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
   auto put_new = [&](MfmaTiles<D, FP8>& t) {
     const int o = (crs.start_off + crs.n - 1) & (kBlock - 1);
     const int q4 = lane >> 4, j = lane & 15;
-    const int kvh = cr.hg / P.qgroups, b = slot_c >> 4, off = slot_c & (kBlock - 1);
+    const int B = kBlock << P.bshift;  // tokens per block
+    const int kvh = cr.hg / P.qgroups, b = slot_c >> (4 + P.bshift), off = slot_c & (B - 1);
     const bool writer = cr.hg % P.qgroups == 0;
-    const size_t blk = (size_t)b * 2 * P.num_kv_heads * kBlock * D;
-    const size_t kt = blk + (size_t)kvh * kBlock * D, vt = blk + (size_t)(P.num_kv_heads + kvh) * kBlock * D;
+    const size_t blk = (size_t)b * 2 * P.num_kv_heads * B * D;
+    const size_t kt = blk + (size_t)kvh * B * D, vt = blk + (size_t)(P.num_kv_heads + kvh) * B * D;
     const int e = ((off >> 2) * D + 2 * lane) * 4 + (off & 3);  // this lane's first V element
     if constexpr (FP8) {
       const uint2_v kc = fp8_quant8(kn, P.inv_k_scale);  // codes of dims 8 lane .. +7
@@ -387,7 +396,7 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
       ++crow_id;
       c_h0 = head0(cr.hg);
       c_nh = heads(cr.hg);
-      crs = row_span(ctx_next, P.window, P.max_blocks);
+      crs = row_span(ctx_next, P.window, P.max_blocks, P.bshift);
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) st.qop[kk] = q_next[kk];
       st.reset();
@@ -399,7 +408,7 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
       for (int kk = 0; kk < D / 32; ++kk) q_next[kk] = g < nh_n ? *(const uint4_v*)(qp + 32 * kk) : uint4_v{0, 0, 0, 0};
       load_new(qn, kn_next, vn_next, slot_next);
     }
-    const int J = P.prefix_blocks + x.j;  // table entry of the tile
+    const int J = ptiles + x.j;  // the tile's place in the row span
     if constexpr (FUSED) {
       if (slot_c >= 0 && J == crs.nblocks - 1) put_new(x.t);
     }

@@ -68,13 +68,16 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
   const int h0 = kvh * P.group + qg * GT;
   const int nh = min(GT, P.group - qg * GT);
 
-  // The sequence length, this partition's table entries (lane i holds entry
-  // part * part_blocks + i, read whenever it lies inside the table row) and
-  // the queries are independent loads, issued together.
+  // Lane i holds the id of tile part * part_blocks + i of the row (with
+  // 16-token blocks, table entry part * part_blocks + i, loaded together
+  // with the sequence length; 32-token blocks need the length first).
   const int ctx = P.seq_lens[s];
-  const int32_t* row = P.block_tables + (size_t)s * P.max_blocks + part * P.part_blocks;
-  const int my_id = lane < P.part_blocks && part * P.part_blocks + lane < P.max_blocks ? row[lane] : 0;
-  const RowSpan rs = row_span(ctx, P.window, P.max_blocks);
+  const int32_t* row = P.block_tables + (size_t)s * P.max_blocks;
+  const int jl = part * P.part_blocks + lane;
+  int my_id = -1;
+  if (P.bshift == 0 && lane < P.part_blocks && jl < P.max_blocks) my_id = tile_id(row, jl, 0, P.num_blocks);
+  const RowSpan rs = row_span(ctx, P.window, P.max_blocks, P.bshift);
+  if (P.bshift != 0 && lane < P.part_blocks && jl < rs.nblocks) my_id = tile_id(row, rs.t0 + jl, P.bshift, P.num_blocks);
   const int nparts = (rs.nblocks + P.part_blocks - 1) / P.part_blocks;
   T* out = (T*)P.out;
   if (rs.nblocks == 0) {
@@ -110,7 +113,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
   }
 
   const T* pool = (const T*)P.pool_layer;
-  const size_t tile = (size_t)16 * D;
+  const size_t tile = (size_t)(16 << P.bshift) * D;  // one head's K (or V) tile of a block
   const size_t blk_stride = 2 * (size_t)P.num_kv_heads * tile;
   const size_t k_off = (size_t)kvh * tile;
   const size_t v_rel = (size_t)P.num_kv_heads * tile;
@@ -136,10 +139,10 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
   const int cnt = nbp > wave ? (nbp - wave + kWaves - 1) / kWaves : 0;
   auto issue = [&](int k, Tiles& t) {
     const int kl = k < cnt ? k : cnt - 1;  // past the end: re-read the last block (a cache hit)
-    int id = __builtin_amdgcn_readlane(my_id, wave + kl * kWaves);
-    t.bad = (unsigned)id >= (unsigned)P.num_blocks;
+    int id = __builtin_amdgcn_readlane(my_id, wave + kl * kWaves);  // tile id (tile_id())
+    t.bad = (unsigned)id >= ((unsigned)P.num_blocks << P.bshift);
     if (t.bad) id = 0;
-    const T* base = pool + (size_t)id * blk_stride + k_off;
+    const T* base = pool + (size_t)(id >> P.bshift) * blk_stride + (size_t)(id & ((1 << P.bshift) - 1)) * 16 * D + k_off;
 #pragma unroll
     for (int i = 0; i < KCH; ++i) t.k[i] = *(const uint4v*)(base + kt_tok * D + (kc + 4 * i) * E);
 #pragma unroll

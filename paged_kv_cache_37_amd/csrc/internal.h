@@ -7,11 +7,12 @@
 
 namespace kvp {
 
-constexpr int kBlock = 16;      // tokens per block (the pages' default block size)
+constexpr int kBlock = 16;      // tokens per tile: the unit every kernel streams.  A pool's
+                                // block holds 16 tokens (the pages' default) or 32 (two tiles)
 constexpr int kWaves = 4;       // waves per decode workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxStreamSeqs = 4096;  // sequences one streaming launch can take (LDS prefix sums)
-constexpr int kMaxPrefixBlocks = 4096;  // shared-prefix blocks one prefix pass takes (LDS block ids)
+constexpr int kMaxPrefixBlocks = 4096;  // shared-prefix tiles one prefix pass takes (LDS tile ids)
 
 // Geometry and arguments of one decode launch, resolved on the host.
 struct DecodeParams {
@@ -28,14 +29,15 @@ struct DecodeParams {
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t num_blocks;           // physical blocks per layer (bounds check)
+  int32_t bshift;               // log2(block_size / 16): a block (table entry) holds 1 << bshift tiles
   int32_t group;                // query heads per KV head (G)
   int32_t heads_per_wg;         // query heads one workgroup serves (<= 16)
   int32_t qgroups;              // workgroups per KV head = ceil(G / heads_per_wg)
-  int32_t part_blocks;          // table entries per partition
+  int32_t part_blocks;          // tiles per partition
   int32_t num_parts;            // partitions of the longest possible row
   float scale_log2;             // scale * log2(e): scores are kept in base 2
   int32_t depth;                // blocks of K/V a wave keeps in flight ahead of the one it computes
-  int32_t* prefix;              // [S + 1] table entries before each sequence   (streaming only)
+  int32_t* prefix;              // [S + 1] tiles before each sequence's row     (streaming only)
   int32_t stream_wgs;           // persistent workgroups of a streaming launch   (streaming only)
   const void* k_new;            // [S][Hkv][D] new token per sequence        (fused write only)
   const void* v_new;            // [S][Hkv][D]                               (fused write only)
@@ -51,30 +53,44 @@ struct DecodeParams {
   float inv_v_scale;
 };
 
-// Span of one block-table row: leading slots of the first block that are
-// not attended (sliding window only), attended keys, and entries used.
+// Span of one block-table row in 16-token tiles.  The row's first block
+// starts at a multiple of the block size; under a sliding window the first
+// attended position may lie past its first tile (t0 = 1 in a 32-token
+// block) and past slots of the tile it lies in (start_off).  Tile J of the
+// span is tile t0 + J of the row: entry (t0 + J) >> bshift, half
+// (t0 + J) & 1 of a 32-token block.
 struct RowSpan {
-  int start_off;
-  int n;
-  int nblocks;
+  int start_off;  // unattended leading slots of the first tile
+  int n;          // attended keys
+  int nblocks;    // tiles holding them
+  int t0;         // tiles of the first block before the first attended one
 };
 
-__device__ __forceinline__ RowSpan row_span(int ctx, int window, int max_blocks) {
-  RowSpan r{0, 0, 0};
+__device__ __forceinline__ RowSpan row_span(int ctx, int window, int max_blocks, int bshift) {
+  RowSpan r{0, 0, 0, 0};
   if (ctx <= 0) return r;
+  const int B = kBlock << bshift;
   const int first = (window > 0 && ctx > window) ? ctx - window : 0;
-  r.start_off = first & (kBlock - 1);
+  const int off = first & (B - 1);
+  r.t0 = off >> 4;
+  r.start_off = off & (kBlock - 1);
   r.n = ctx - first;
+  if (((unsigned)off + (unsigned)r.n + B - 1) / B > (unsigned)max_blocks)  // row longer than the table:
+    r.n = max_blocks * B - off;                                             // attend what the table holds
   r.nblocks = (r.start_off + r.n + kBlock - 1) / kBlock;
-  if (r.nblocks > max_blocks) {  // row longer than the table: attend what the table holds
-    r.nblocks = max_blocks;
-    r.n = max_blocks * kBlock - r.start_off;
-  }
   return r;
 }
 
+// Tile j of a table row (j counted from the row's first entry) as a tile
+// id: physical block << bshift plus the tile's place in the block, or -1
+// when the entry names no block of the pool.
+__device__ __forceinline__ int tile_id(const int32_t* __restrict__ row, int j, int bshift, int num_blocks) {
+  const int b = row[j >> bshift];
+  return (unsigned)b < (unsigned)num_blocks ? (b << bshift) | (j & ((1 << bshift) - 1)) : -1;
+}
+
 // Launchers (each defined next to its kernel).
-hipError_t launch_cache_write(void* pool_layer, int dtype, int num_blocks, int num_kv_heads,
+hipError_t launch_cache_write(void* pool_layer, int dtype, int num_blocks, int bshift, int num_kv_heads,
                               int head_dim, const void* k_new, const void* v_new,
                               const int32_t* slots, int num_tokens, float inv_k_scale, float inv_v_scale,
                               hipStream_t stream);

@@ -2,6 +2,7 @@
 // choice, launches.  Declared in include/kvpool.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -39,34 +40,38 @@ int32_t ok() {
 
 size_t elt_bytes(int32_t dtype) { return dtype == KVP_F32 ? 4 : dtype == KVP_BF16 ? 2 : 1; }
 
-// Elements of one layer: num_blocks * 2 * Hkv * 16 * D.
+// log2(block_size / 16): the 16-token tiles per block, as a shift.
+int32_t bshift_of(const kvp_pool_desc& d) { return d.block_size == 32 ? 1 : 0; }
+
+// Elements of one layer: num_blocks * 2 * Hkv * block_size * D.
 size_t layer_elems(const kvp_pool_desc& d) {
-  return (size_t)d.num_blocks * 2 * (size_t)d.num_kv_heads * kvp::kBlock * (size_t)d.head_dim;
+  return (size_t)d.num_blocks * 2 * (size_t)d.num_kv_heads * d.block_size * (size_t)d.head_dim;
 }
 
 int32_t check_desc(const kvp_pool_desc* d) {
   if (!d) return fail(KVP_ERR_INVALID_ARG, "desc is NULL");
   if (d->num_layers < 1 || d->num_blocks < 1 || d->num_kv_heads < 1)
     return fail(KVP_ERR_INVALID_ARG, "num_layers, num_blocks and num_kv_heads must be >= 1");
-  if (d->block_size != kvp::kBlock) return fail(KVP_ERR_UNSUPPORTED, "block_size must be 16 (got %d)", d->block_size);
+  if (d->block_size != 16 && d->block_size != 32)
+    return fail(KVP_ERR_UNSUPPORTED, "block_size must be 16 or 32 (got %d)", d->block_size);
   if (d->head_dim != 64 && d->head_dim != 128)
     return fail(KVP_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", d->head_dim);
   if (d->dtype != KVP_F32 && d->dtype != KVP_BF16 && d->dtype != KVP_FP8_E4M3)
     return fail(KVP_ERR_UNSUPPORTED, "dtype must be F32, BF16 or FP8_E4M3");
-  if ((size_t)d->num_blocks * kvp::kBlock > (size_t)INT32_MAX)
-    return fail(KVP_ERR_INVALID_ARG, "num_blocks * 16 must fit in int32 slot numbers");
+  if ((size_t)d->num_blocks * d->block_size > (size_t)INT32_MAX)
+    return fail(KVP_ERR_INVALID_ARG, "num_blocks * block_size must fit in int32 slot numbers");
   return KVP_OK;
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-// Partition size in table entries.
+// Partition size in 16-token tiles.
 int32_t resolve_part_blocks(int32_t partition_tokens, int32_t num_seqs, int32_t wg_per_seq_head_part,
-                            int32_t max_blocks) {
+                            int32_t max_tiles) {
   if (partition_tokens > 0) return partition_tokens / kvp::kBlock;
   // Auto: 512-token partitions; shorter when the grid would not fill the chip.
   int32_t pb = 32;
-  const long wgs = (long)num_seqs * wg_per_seq_head_part * ((max_blocks + pb - 1) / pb);
+  const long wgs = (long)num_seqs * wg_per_seq_head_part * ((max_tiles + pb - 1) / pb);
   if (wgs < 2048) pb = 16;
   return pb;
 }
@@ -124,9 +129,9 @@ int64_t kv_pool_offset(kvp_pool pool, int32_t layer, int32_t block, int32_t kv, 
   if (!pool) return -1;
   const kvp_pool_desc& d = pool->desc;
   if (layer < 0 || layer >= d.num_layers || block < 0 || block >= d.num_blocks || kv < 0 || kv > 1 || head < 0 ||
-      head >= d.num_kv_heads || slot < 0 || slot >= kvp::kBlock || dim < 0 || dim >= d.head_dim)
+      head >= d.num_kv_heads || slot < 0 || slot >= d.block_size || dim < 0 || dim >= d.head_dim)
     return -1;
-  const int64_t tile = (int64_t)kvp::kBlock * d.head_dim;
+  const int64_t tile = (int64_t)d.block_size * d.head_dim;
   const int64_t blk = ((int64_t)layer * d.num_blocks + block) * 2 * d.num_kv_heads * tile;
   if (kv == 0) return blk + (int64_t)head * tile + (int64_t)slot * d.head_dim + dim;
   return blk + (int64_t)(d.num_kv_heads + head) * tile + ((int64_t)(slot / 4) * d.head_dim + dim) * 4 + slot % 4;
@@ -143,7 +148,7 @@ int32_t cache_write(kvp_pool pool, int32_t layer, const void* k_new, const void*
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(slot_mapping, 4))
     return fail(KVP_ERR_INVALID_ARG, "k_new/v_new must be 16-byte aligned");
   char* base = (char*)pool->base + (size_t)layer * layer_elems(d) * elt_bytes(d.dtype);
-  const hipError_t e = kvp::launch_cache_write(base, d.dtype, d.num_blocks, d.num_kv_heads, d.head_dim, k_new,
+  const hipError_t e = kvp::launch_cache_write(base, d.dtype, d.num_blocks, bshift_of(d), d.num_kv_heads, d.head_dim, k_new,
                                                v_new, slot_mapping, num_tokens, 1.0f / pool->k_scale[layer],
                                                1.0f / pool->v_scale[layer], stream);
   if (e != hipSuccess) return fail(KVP_ERR_HIP, "cache_write launch: %s", hipGetErrorString(e));
@@ -179,8 +184,8 @@ static int32_t stream_workgroups(int32_t head_dim, int32_t depth, bool fused, bo
 // The streaming kernel keeps its tile counts in 32-bit prefix sums and its
 // split (tile * waves / tiles) exact in double arithmetic: both hold when
 // these bounds do.
-static bool stream_fits(int32_t num_seqs, int32_t max_blocks, int32_t head_groups, int32_t wgs) {
-  const double entries = (double)num_seqs * max_blocks;
+static bool stream_fits(int32_t num_seqs, int32_t max_tiles, int32_t head_groups, int32_t wgs) {
+  const double entries = (double)num_seqs * max_tiles;
   const double waves = (double)wgs * kvp::kWaves;
   return num_seqs <= kvp::kMaxStreamSeqs && entries < 2147483647.0 &&
          entries * head_groups * (waves + 1.0) < 4503599627370496.0;  // 2^52
@@ -214,6 +219,10 @@ static int32_t plan(kvp_pool pool, int32_t num_seqs, int32_t num_q_heads, int32_
     return fail(KVP_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
                 num_q_heads, d.num_kv_heads);
   if (max_blocks < 1) return fail(KVP_ERR_INVALID_ARG, "max_blocks_per_seq must be >= 1");
+  if ((int64_t)max_blocks * d.block_size > INT32_MAX)
+    return fail(KVP_ERR_INVALID_ARG, "max_blocks_per_seq * block_size must fit in int32");
+  const int32_t bs = bshift_of(d);
+  const int32_t max_tiles = max_blocks << bs;  // 16-token tiles a row can hold
   if (partition_tokens != 0 &&
       (partition_tokens % kvp::kBlock != 0 || partition_tokens < kvp::kBlock || partition_tokens > 64 * kvp::kBlock))
     return fail(KVP_ERR_INVALID_ARG, "partition_tokens must be 0 or a multiple of 16 in [16, 1024]");
@@ -229,7 +238,7 @@ static int32_t plan(kvp_pool pool, int32_t num_seqs, int32_t num_q_heads, int32_
       } else {
         const int32_t wgs =
             partition_tokens == 0 ? stream_workgroups(d.head_dim, decode_depth(PATH_STREAM, fp8), false, fp8) : 0;
-        pth = wgs > 0 && stream_fits(num_seqs, max_blocks, mfma_groups, wgs) ? PATH_STREAM : PATH_MFMA;
+        pth = wgs > 0 && stream_fits(num_seqs, max_tiles, mfma_groups, wgs) ? PATH_STREAM : PATH_MFMA;
       }
       break;
     case KVP_VARIANT_VALU:
@@ -261,7 +270,7 @@ static int32_t plan(kvp_pool pool, int32_t num_seqs, int32_t num_q_heads, int32_
   if ((long)d.num_kv_heads * qgroups > 65535) return fail(KVP_ERR_UNSUPPORTED, "too many head groups");
   // the partition size depends on the row geometry only, never on the variant,
   // so paged_decode_workspace_bytes() is valid for every variant
-  const int32_t pb = resolve_part_blocks(partition_tokens, num_seqs, d.num_kv_heads, max_blocks);
+  const int32_t pb = resolve_part_blocks(partition_tokens, num_seqs, d.num_kv_heads, max_tiles);
   std::memset(p, 0, sizeof(*p));
   p->max_blocks = max_blocks;
   p->num_seqs = num_seqs;
@@ -272,12 +281,13 @@ static int32_t plan(kvp_pool pool, int32_t num_seqs, int32_t num_q_heads, int32_
   p->heads_per_wg = hpw;
   p->qgroups = qgroups;
   p->part_blocks = pb;
-  p->num_parts = (max_blocks + pb - 1) / pb;
+  p->num_parts = (max_tiles + pb - 1) / pb;
+  p->bshift = bs;
   p->depth = decode_depth(pth, fp8);
   if (pth == PATH_STREAM) {
     p->stream_wgs = stream_workgroups(d.head_dim, p->depth, false, fp8);
     if (p->stream_wgs <= 0) return fail(KVP_ERR_HIP, "cannot size the streaming grid (no device?)");
-    if (!stream_fits(num_seqs, max_blocks, d.num_kv_heads * qgroups, p->stream_wgs))
+    if (!stream_fits(num_seqs, max_tiles, d.num_kv_heads * qgroups, p->stream_wgs))
       return fail(KVP_ERR_UNSUPPORTED, "num_seqs * max_blocks_per_seq too large for the STREAM variant");
   }
   *path = pth;
@@ -383,9 +393,10 @@ static int32_t decode(kvp_pool pool, const kvp_decode_args* a, const void* k_new
   if (a->shared_prefix_blocks < 0 || a->shared_prefix_blocks > a->max_blocks_per_seq)
     return fail(KVP_ERR_INVALID_ARG, "shared_prefix_blocks must be in [0, max_blocks_per_seq]");
   // the shared-prefix pass is a STREAM feature for full-context rows; elsewhere the hint is ignored
-  // (a shorter hint is as valid as the full one: longer prefixes use the first kMaxPrefixBlocks)
+  // (a shorter hint is as valid as the full one: longer prefixes use the blocks of the first
+  // kMaxPrefixBlocks tiles)
   if (path == PATH_STREAM && a->sliding_window == 0)
-    p.prefix_blocks = a->shared_prefix_blocks < kvp::kMaxPrefixBlocks ? a->shared_prefix_blocks : kvp::kMaxPrefixBlocks;
+    p.prefix_blocks = std::min(a->shared_prefix_blocks, kvp::kMaxPrefixBlocks >> p.bshift);
   size_t ml_off = 0;
   const StreamLayout SL = path == PATH_STREAM ? stream_workspace(p, d.head_dim) : StreamLayout{};
   const size_t ws = path == PATH_STREAM ? SL.total : grid_workspace(p, d.head_dim, &ml_off);
@@ -423,7 +434,7 @@ static int32_t decode(kvp_pool pool, const kvp_decode_args* a, const void* k_new
   p.inv_v_scale = 1.0f / pool->v_scale[a->layer];
   hipError_t e;
   if (write && path != PATH_STREAM) {
-    e = kvp::launch_cache_write(const_cast<void*>(p.pool_layer), d.dtype, d.num_blocks, d.num_kv_heads, d.head_dim,
+    e = kvp::launch_cache_write(const_cast<void*>(p.pool_layer), d.dtype, d.num_blocks, p.bshift, d.num_kv_heads, d.head_dim,
                                 k_new, v_new, slots, a->num_seqs, p.inv_k_scale, p.inv_v_scale, stream);
     if (e != hipSuccess) return fail(KVP_ERR_HIP, "cache_write launch: %s", hipGetErrorString(e));
   }
@@ -460,7 +471,7 @@ int32_t kv_pool_copy_blocks(kvp_pool pool, const int32_t* src, const int32_t* ds
   if (!src || !dst) return fail(KVP_ERR_INVALID_ARG, "NULL src or dst");
   if (!aligned(src, 4) || !aligned(dst, 4)) return fail(KVP_ERR_INVALID_ARG, "src/dst must be 4-byte aligned");
   const kvp_pool_desc& d = pool->desc;
-  const size_t block_bytes = 2 * (size_t)d.num_kv_heads * kvp::kBlock * d.head_dim * elt_bytes(d.dtype);
+  const size_t block_bytes = 2 * (size_t)d.num_kv_heads * d.block_size * d.head_dim * elt_bytes(d.dtype);
   const hipError_t e = kvp::launch_copy_blocks(pool->base, d.num_layers, d.num_blocks, block_bytes, src, dst,
                                                num_pairs, stream);
   if (e != hipSuccess) return fail(KVP_ERR_HIP, "copy_blocks launch: %s", hipGetErrorString(e));

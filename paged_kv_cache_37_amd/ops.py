@@ -13,7 +13,7 @@ import torch
 from . import _lib
 from ._lib import DecodeArgs, KVPoolError, PoolDesc, check, lib
 
-BLOCK_SIZE = 16
+BLOCK_SIZE = 16  # the default block size (32 is the other one the library takes)
 
 _DTYPES = {torch.float32: _lib.KVP_F32, torch.bfloat16: _lib.KVP_BF16, torch.float8_e4m3fn: _lib.KVP_FP8_E4M3}
 _VARIANTS = {"auto": _lib.KVP_VARIANT_AUTO, "valu": _lib.KVP_VARIANT_VALU, "mfma": _lib.KVP_VARIANT_MFMA,
@@ -51,21 +51,21 @@ class KVPool:
     to_logical) see an FP8 pool's codes as uint8."""
 
     def __init__(self, num_layers: int, num_blocks: int, num_kv_heads: int, head_dim: int,
-                 dtype: torch.dtype = torch.bfloat16, device="cuda"):
+                 dtype: torch.dtype = torch.bfloat16, device="cuda", block_size: int = BLOCK_SIZE):
         if dtype not in _DTYPES:
             raise ValueError(f"unsupported pool dtype {dtype}")
-        self.desc = PoolDesc(num_layers, num_blocks, BLOCK_SIZE, num_kv_heads, head_dim, _DTYPES[dtype])
+        self.desc = PoolDesc(num_layers, num_blocks, block_size, num_kv_heads, head_dim, _DTYPES[dtype])
         nbytes = lib.kv_pool_bytes(ctypes.byref(self.desc))
         if nbytes == 0:
-            check(_lib.KVP_ERR_UNSUPPORTED if head_dim not in (64, 128) else _lib.KVP_ERR_INVALID_ARG,
-                  "kv_pool_bytes")
+            check(_lib.KVP_ERR_UNSUPPORTED if head_dim not in (64, 128) or block_size not in (16, 32)
+                  else _lib.KVP_ERR_INVALID_ARG, "kv_pool_bytes")
         self.device = torch.device(device)
         if self.device.type == "cuda" and self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())
         self.dtype = dtype
         self.act_dtype = torch.bfloat16 if dtype == torch.float8_e4m3fn else dtype
         self.elem_dtype = torch.uint8 if dtype == torch.float8_e4m3fn else dtype
-        self.num_layers, self.num_blocks = num_layers, num_blocks
+        self.num_layers, self.num_blocks, self.block_size = num_layers, num_blocks, block_size
         self.num_kv_heads, self.head_dim = num_kv_heads, head_dim
         self.nbytes = int(nbytes)
         self.storage = torch.empty(self.nbytes, dtype=torch.uint8, device=self.device)
@@ -97,37 +97,39 @@ class KVPool:
 
     def _tiles(self) -> torch.Tensor:
         L, NB, H, D = self.num_layers, self.num_blocks, self.num_kv_heads, self.head_dim
-        return self.flat().view(L, NB, 2, H, BLOCK_SIZE * D)
+        return self.flat().view(L, NB, 2, H, self.block_size * D)
 
     def load_logical(self, logical: torch.Tensor) -> None:
         """Fill the pool from a tensor in the logical block shape
-        [L, NB, 2, 16, Hkv, D] (K = 0, V = 1)."""
-        L, NB, H, D = self.num_layers, self.num_blocks, self.num_kv_heads, self.head_dim
-        if tuple(logical.shape) != (L, NB, 2, BLOCK_SIZE, H, D):
-            raise ValueError(f"logical pool must be {(L, NB, 2, BLOCK_SIZE, H, D)}, got {tuple(logical.shape)}")
+        [L, NB, 2, B, Hkv, D] (K = 0, V = 1; B = block_size)."""
+        L, NB, H, D, B = self.num_layers, self.num_blocks, self.num_kv_heads, self.head_dim, self.block_size
+        if tuple(logical.shape) != (L, NB, 2, B, H, D):
+            raise ValueError(f"logical pool must be {(L, NB, 2, B, H, D)}, got {tuple(logical.shape)}")
         src = logical.to(device=self.device)
         if src.dtype == torch.float8_e4m3fn:
             src = src.view(torch.uint8)
         if src.dtype != self.elem_dtype:
             raise ValueError(f"logical pool dtype {src.dtype} != pool elements {self.elem_dtype}")
         tiles = self._tiles()
-        # K tile [16][D] per (block, head); V tile [4][D][4] (slot t -> (t//4, d, t%4))
-        tiles[:, :, 0].view(L, NB, H, BLOCK_SIZE, D).copy_(src[:, :, 0].permute(0, 1, 3, 2, 4))
-        tiles[:, :, 1].view(L, NB, H, 4, D, 4).copy_(
-            src[:, :, 1].reshape(L, NB, 4, 4, H, D).permute(0, 1, 4, 2, 5, 3))
+        # K tile [B][D] per (block, head); V tile [B/4][D][4] (slot t -> (t//4, d, t%4))
+        Q = B // 4
+        tiles[:, :, 0].view(L, NB, H, B, D).copy_(src[:, :, 0].permute(0, 1, 3, 2, 4))
+        tiles[:, :, 1].view(L, NB, H, Q, D, 4).copy_(
+            src[:, :, 1].reshape(L, NB, Q, 4, H, D).permute(0, 1, 4, 2, 5, 3))
 
     def to_logical(self) -> torch.Tensor:
-        """The pool in the logical block shape [L, NB, 2, 16, Hkv, D]."""
-        L, NB, H, D = self.num_layers, self.num_blocks, self.num_kv_heads, self.head_dim
+        """The pool in the logical block shape [L, NB, 2, B, Hkv, D]."""
+        L, NB, H, D, B = self.num_layers, self.num_blocks, self.num_kv_heads, self.head_dim, self.block_size
+        Q = B // 4
         tiles = self._tiles()
-        k = tiles[:, :, 0].reshape(L, NB, H, BLOCK_SIZE, D).permute(0, 1, 3, 2, 4)
-        v = tiles[:, :, 1].reshape(L, NB, H, 4, D, 4).permute(0, 1, 3, 5, 2, 4).reshape(L, NB, BLOCK_SIZE, H, D)
+        k = tiles[:, :, 0].reshape(L, NB, H, B, D).permute(0, 1, 3, 2, 4)
+        v = tiles[:, :, 1].reshape(L, NB, H, Q, D, 4).permute(0, 1, 3, 5, 2, 4).reshape(L, NB, B, H, D)
         return torch.stack([k, v], dim=2).contiguous()
 
 
 def kv_pool_create(num_layers: int, num_blocks: int, num_kv_heads: int, head_dim: int,
-                   dtype: torch.dtype = torch.bfloat16, device="cuda") -> KVPool:
-    return KVPool(num_layers, num_blocks, num_kv_heads, head_dim, dtype, device)
+                   dtype: torch.dtype = torch.bfloat16, device="cuda", block_size: int = BLOCK_SIZE) -> KVPool:
+    return KVPool(num_layers, num_blocks, num_kv_heads, head_dim, dtype, device, block_size)
 
 
 def cache_write(pool: KVPool, layer: int, k_new: torch.Tensor, v_new: torch.Tensor,

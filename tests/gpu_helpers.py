@@ -58,7 +58,8 @@ class Dev:
         self.w = w
         self.dt = torch_dtype(w)
         self.ops = ops
-        self.pool = pool or ops.KVPool(w.num_layers, w.num_blocks, w.num_kv_heads, w.head_dim, pool_dtype(w), device)
+        self.pool = pool or ops.KVPool(w.num_layers, w.num_blocks, w.num_kv_heads, w.head_dim, pool_dtype(w), device,
+                                       block_size=w.block_size)
         self.pool.load_logical(host_to_torch(w.pool, pool_dtype(w)))
         if w.dtype == "fp8":
             for layer in range(w.num_layers):
@@ -113,3 +114,41 @@ def compare(out: torch.Tensor, ref: np.ndarray, dtype: str, what: str = "") -> d
         stats["frac_of_bound"] = worst
     say(what, stats)
     return stats
+
+
+def relaid(w, B: int, seed: int = 77):
+    """A copy of workload `w` with the same sequences' K/V in a pool of
+    B-token blocks: every attended (and, with a window, every listed)
+    position copied in order into fresh blocks (ids a seeded permutation),
+    tables listing them; unlisted slots NaN.  Queries, lengths, window and
+    scale are shared."""
+    import copy
+
+    src_B = w.block_size
+    rng = np.random.default_rng(seed)
+    spans = []
+    for s in range(w.num_seqs):
+        ctx = int(w.seq_lens[s])
+        first = max(0, ctx - w.window) if w.window else 0
+        spans.append((first, ctx, first // B, ((ctx - 1) // B - first // B + 1) if ctx else 0))
+    NB = sum(n for *_, n in spans) + 2
+    ids = rng.permutation(NB).astype(np.int32)
+    L = w.pool.shape[0]
+    pool = np.empty((L, NB, 2, B) + w.pool.shape[4:], dtype=w.pool.dtype)
+    pool[:] = {np.dtype(np.uint16): np.uint16(0x7FC0), np.dtype(np.uint8): np.uint8(0x7F)}.get(
+        pool.dtype, np.float32("nan"))
+    width = max(n for *_, n in spans) + 1
+    tables = np.full((w.num_seqs, width), ids[-1], dtype=np.int32)
+    k = 0
+    for s, (first, ctx, fb, n) in enumerate(spans):
+        tables[s, :n] = ids[k:k + n]
+        src_first = first // src_B
+        for pos in range(first, ctx):
+            src = w.block_tables[s][pos // src_B - src_first]
+            pool[:, ids[k + pos // B - fb], :, pos % B] = w.pool[:, src, :, pos % src_B]
+        k += n
+    w2 = copy.copy(w)
+    w2.block_size, w2.num_blocks, w2.pool, w2.block_tables = B, NB, pool, tables
+    w2.row_blocks = np.array([n for *_, n in spans], dtype=np.int32)
+    w2.name = w.name + f"-relaid-B{B}"
+    return w2

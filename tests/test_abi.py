@@ -54,7 +54,9 @@ def test_pool_bytes(ops):
     assert ops.lib.kv_pool_bytes(ctypes.byref(d)) == 2 * 10 * 2 * 16 * 3 * 64 * 4
     d = desc(ops, dtype=1, D=128)
     assert ops.lib.kv_pool_bytes(ctypes.byref(d)) == 2 * 10 * 2 * 16 * 3 * 128 * 2
-    assert ops.lib.kv_pool_bytes(ctypes.byref(desc(ops, B=32))) == 0
+    assert ops.lib.kv_pool_bytes(ctypes.byref(desc(ops, B=32))) == 2 * 10 * 2 * 32 * 3 * 64 * 4
+    assert ops.lib.kv_pool_bytes(ctypes.byref(desc(ops, B=64))) == 0
+    assert ops.lib.kv_pool_bytes(ctypes.byref(desc(ops, B=8))) == 0
     assert ops.lib.kv_pool_bytes(ctypes.byref(desc(ops, D=96))) == 0
 
 
@@ -73,7 +75,7 @@ def test_create_checks_arguments(ops):
     h = ctypes.c_void_p()
     assert ops.lib.kv_pool_create(ctypes.byref(d), ctypes.c_void_p(0x100000), 16, ctypes.byref(h)) == \
         ops._lib.KVP_ERR_INVALID_ARG
-    bad = desc(ops, B=32)
+    bad = desc(ops, B=64)
     assert _handle(ops, bad)[0] == ops._lib.KVP_ERR_UNSUPPORTED
     st, h = _handle(ops, d)
     assert st == 0 and h.value
@@ -83,27 +85,28 @@ def test_create_checks_arguments(ops):
     assert ops.lib.kv_pool_destroy(h) == 0
 
 
-@pytest.mark.parametrize("D", [64, 128])
-def test_offsets_follow_documented_layout(ops, D):
+@pytest.mark.parametrize("D,B", [(64, 16), (128, 16), (128, 32)])
+def test_offsets_follow_documented_layout(ops, D, B):
     L, NB, H = 2, 5, 3
-    st, h = _handle(ops, desc(ops, L, NB, H, D, dtype=1))
+    st, h = _handle(ops, desc(ops, L, NB, H, D, dtype=1, B=B))
     assert st == 0
     seen = set()
     for layer in range(L):
         for b in range(NB):
             for kv in range(2):
                 for hh in range(H):
-                    for t in range(16):
+                    for t in range(B):
                         for d in (0, 1, D - 1):
                             off = ops.lib.kv_pool_offset(h, layer, b, kv, hh, t, d)
-                            block_base = ((layer * NB + b) * 2 * H) * 16 * D
+                            block_base = ((layer * NB + b) * 2 * H) * B * D
                             if kv == 0:
-                                exp = block_base + hh * 16 * D + t * D + d
+                                exp = block_base + hh * B * D + t * D + d
                             else:
-                                exp = block_base + (H + hh) * 16 * D + ((t // 4) * D + d) * 4 + t % 4
+                                exp = block_base + (H + hh) * B * D + ((t // 4) * D + d) * 4 + t % 4
                             assert off == exp
                             seen.add(off)
-    assert len(seen) == L * NB * 2 * H * 16 * 3
+    assert len(seen) == L * NB * 2 * H * B * 3
+    assert ops.lib.kv_pool_offset(h, 0, 0, 0, 0, B, 0) == -1
     assert ops.lib.kv_pool_offset(h, L, 0, 0, 0, 0, 0) == -1
     assert ops.lib.kv_pool_offset(h, 0, 0, 2, 0, 0, 0) == -1
     ops.lib.kv_pool_destroy(h)
@@ -195,3 +198,20 @@ def test_fp8_pool_variant_checks(ops):
         assert ops.lib.paged_decode_attention(h32, ctypes.byref(a), None) == E.KVP_ERR_UNSUPPORTED
     ops.lib.kv_pool_destroy(h8)
     ops.lib.kv_pool_destroy(h32)
+
+
+def test_block_size_32_geometry_checks(ops):
+    """32-token blocks: partitions and workspace count 16-token tiles, and
+    a table whose rows could hold more than 2^31 slots is refused."""
+    E = ops._lib
+    _, h = _handle(ops, desc(ops, 1, 8, 2, 64, dtype=E.KVP_BF16, B=32))
+    need = ops.lib.paged_decode_workspace_bytes(h, 2, 8, 64, 256)
+    rows = 2 * 8 * (64 * 2 // 16)  # 64 entries = 128 tiles = 8 partitions of 16 tiles
+    assert need >= rows * 64 * 4 + rows * 2 * 4  # the partitioned variant's partials fit
+    A = ops.DecodeArgs
+    a = A(layer=0, q=0x1000, out=0x2000, block_tables=0x3000, max_blocks_per_seq=(1 << 26), seq_lens=0x4000,
+          sliding_window=0, num_seqs=2, num_q_heads=8, scale=0.125, partition_tokens=256, variant=E.KVP_VARIANT_MFMA,
+          workspace=None, workspace_bytes=0)
+    assert ops.lib.paged_decode_attention(h, ctypes.byref(a), None) == E.KVP_ERR_INVALID_ARG
+    assert b"block_size" in ops.lib.kvp_last_error()
+    ops.lib.kv_pool_destroy(h)

@@ -616,3 +616,84 @@ def test_planted_fp8_mistake_is_caught(kind):
     ok_known = mutant(1.0) == 0x38
     ok_above = np.all(mutant(np.nextafter(mids, np.inf)) == np.arange(1, 0x7F, dtype=np.uint8))
     assert not (ok_ties and ok_sat and ok_known and ok_above)
+
+
+# ---------------------------------------------------------------------------
+# 32-token blocks ([Optimizing] Trade-offs of Block Size Tuning): the block
+# size changes where a key lives, never which keys are attended
+
+
+def _relaid(w16, B):
+    """The same sequences' K/V in a pool of B-token blocks: each sequence's
+    attended positions copied, in order, into fresh blocks of the new pool
+    (ids a seeded permutation), with tables listing them."""
+    rng = np.random.default_rng(77)
+    rows, per = [], []
+    for s in range(w16.num_seqs):
+        ctx = int(w16.seq_lens[s])
+        first = max(0, ctx - w16.window) if w16.window else 0
+        fb, lb = first // B, (ctx - 1) // B if ctx else -1
+        per.append((first, fb, lb - fb + 1 if ctx else 0))
+    NB = sum(n for _, _, n in per) + 2
+    ids = rng.permutation(NB).astype(np.int32)
+    pool = np.empty((1, NB, 2, B) + w16.pool.shape[4:], dtype=w16.pool.dtype)
+    pool[:] = W.BF16_NAN if pool.dtype == np.uint16 else np.nan
+    tables = np.full((w16.num_seqs, max(n for _, _, n in per) + 1), ids[-1], dtype=np.int32)
+    k = 0
+    for s, (first, fb, n) in enumerate(per):
+        ctx = int(w16.seq_lens[s])
+        tables[s, :n] = ids[k:k + n]
+        for pos in range(first, ctx):
+            blk = ids[k + pos // B - fb]
+            src16 = w16.block_tables[s][pos // 16 - first // 16]
+            pool[0, blk, 0, pos % B] = w16.pool[0, src16, 0, pos % 16]
+            pool[0, blk, 1, pos % B] = w16.pool[0, src16, 1, pos % 16]
+        k += n
+    return pool, tables
+
+
+@pytest.mark.parametrize("window", [0, 20, 40, 100])
+def test_block_size_32_is_a_relabelling(window):
+    """The same keys in 32-token blocks give bit-identical oracle outputs;
+    windows whose first position lies in a block's second half (40 at
+    contexts 57 and 95: first positions 17 and 55) included."""
+    w = W.custom(31, [1, 15, 16, 17, 31, 32, 33, 57, 64, 95, 200], num_q_heads=8, num_kv_heads=2, head_dim=16,
+                 dtype="bf16", window=window)
+    a = oracle.decode_attention(w.pool, 0, w.q, w.block_tables, w.seq_lens, w.window, w.scale)
+    pool32, tables32 = _relaid(w, 32)
+    oracle.check_tables(tables32, w.seq_lens, w.window, 32, pool32.shape[1])
+    b = oracle.decode_attention(pool32, 0, w.q, tables32, w.seq_lens, w.window, w.scale)
+    assert a.tobytes() == b.tobytes()
+    c = oracle.decode_attention_bruteforce(pool32, 0, w.q, tables32, w.seq_lens, w.window, w.scale)
+    np.testing.assert_allclose(b, c, rtol=0, atol=1e-12)
+
+
+def test_block_size_32_generated_workloads():
+    """Generated 32-token workloads keep the table rule and match the
+    independent per-position gather through SDPA."""
+    w = W.custom(32, [1, 31, 32, 33, 70, 130], num_q_heads=8, num_kv_heads=4, head_dim=16, window=48,
+                 block_size=32)
+    assert w.pool.shape[3] == 32
+    oracle.check_tables(w.block_tables, w.seq_lens, w.window, 32, w.num_blocks, w.row_blocks)
+    a = oracle.decode_attention(w.pool, 0, w.q, w.block_tables, w.seq_lens, w.window, w.scale)
+    ref = sdpa_reference(w.pool, 0, w.q, w.block_tables, w.seq_lens, w.window, w.scale)
+    np.testing.assert_allclose(a, ref, rtol=0, atol=1e-12)
+    # row spans in 32-token blocks: context 70 under window 48 attends 22..69,
+    # blocks 0..2, the first 22 slots of block 0 unattended
+    assert oracle.row_span(70, 48, 32) == (22, 48, 3)
+    assert oracle.row_span(33, 0, 32) == (0, 33, 2)
+
+
+def test_block_size_32_cache_write():
+    """slot = block * 32 + offset: the write lands at block slot // 32,
+    offset slot % 32, and attention then sees it as the last key."""
+    w = W.custom(33, [31, 32, 40], num_q_heads=4, num_kv_heads=2, head_dim=16, block_size=32)
+    W.with_next_token(w, w.unused_blocks)
+    assert [int(s) % 32 for s in w.slot_mapping] == [31, 0, 8]
+    pool = oracle.cache_write(w.pool, 0, w.k_new, w.v_new, w.slot_mapping)
+    for t, slot in enumerate(w.slot_mapping):
+        assert np.array_equal(pool[0, slot // 32, 0, slot % 32], w.k_new[t])
+        assert np.array_equal(pool[0, slot // 32, 1, slot % 32], w.v_new[t])
+    out = oracle.decode_attention(pool, 0, w.q, w.block_tables_after, w.seq_lens_after, 0, w.scale)
+    ref = sdpa_reference(pool, 0, w.q, w.block_tables_after, w.seq_lens_after, 0, w.scale)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)

@@ -33,7 +33,12 @@ The five workloads (sizes as in the write-ups' Llama-3 serving examples):
    blocks) are the same physical blocks, each with a private tail of 1..512
    tokens whose last block is partial;
 5. sliding-window layer: 32 sequences with contexts in [4096, 32768] and a
-   4096-token window; tables hold only the blocks covering the window.
+   4096-token window; tables hold only the blocks covering the window;
+6. long contexts: 16 Llama-3-8B-shaped sequences of 32768..40960 tokens (the
+   case for which a 32-token block size is offered).
+
+Blocks hold 16 tokens unless a generator is asked for block_size=32 (same
+lengths and shapes; tables in 32-token blocks).
 """
 from __future__ import annotations
 
@@ -55,6 +60,7 @@ _CONFIG_NAMES = {
     3: "llama3-70b-S128-H64/8-D128-ctx8192",
     4: "shared-prefix-S256-H32/8-D128-prefix2048+tail1..512",
     5: "sliding-window4096-S32-H32/8-D128-ctx4096..32768",
+    6: "llama3-8b-long-S16-H32/8-D128-ctx32768..40960",
 }
 
 
@@ -244,10 +250,10 @@ def _finish(w: Workload, rows, extra_cols: int = 1) -> Workload:
     return w
 
 
-def _base(config, seed, dtype, L, NB, Hq, Hkv, D, window, seq_lens) -> Workload:
+def _base(config, seed, dtype, L, NB, Hq, Hkv, D, window, seq_lens, block_size=BLOCK_SIZE) -> Workload:
     w = Workload(
         config=config, seed=seed, dtype=dtype, num_layers=L, num_blocks=NB,
-        block_size=BLOCK_SIZE, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+        block_size=block_size, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
         window=window, scale=float(np.float32(1.0 / math.sqrt(D))),
         seq_lens=np.asarray(seq_lens, dtype=np.int32),
         block_tables=np.zeros((0, 0), np.int32), row_blocks=np.zeros(0, np.int32),
@@ -256,6 +262,8 @@ def _base(config, seed, dtype, L, NB, Hq, Hkv, D, window, seq_lens) -> Workload:
     if dtype == "fp8":
         w.name += "-fp8"
         w.k_scale, w.v_scale = float(np.float32(0.37)), float(np.float32(0.61))
+    if block_size != BLOCK_SIZE:
+        w.name += f"-B{block_size}"
     return w
 
 
@@ -284,26 +292,35 @@ def config1(seed: int = 1) -> Workload:
     return with_next_token(w, list(perm[k:]))
 
 
-def config2(seed: int = 2, num_layers: int = 1, dtype: str = "bf16") -> Workload:
+def config2(seed: int = 2, num_layers: int = 1, dtype: str = "bf16", block_size: int = BLOCK_SIZE) -> Workload:
     rng = np.random.default_rng(seed)
     ctx = rng.integers(512, 4096, size=64, endpoint=True)
-    return _scattered(2, seed, rng, ctx, 32, 8, 128, 0, num_layers, dtype)
+    return _scattered(2, seed, rng, ctx, 32, 8, 128, 0, num_layers, dtype, block_size)
 
 
-def config3(seed: int = 3, num_layers: int = 1, dtype: str = "bf16") -> Workload:
+def config3(seed: int = 3, num_layers: int = 1, dtype: str = "bf16", block_size: int = BLOCK_SIZE) -> Workload:
     rng = np.random.default_rng(seed)
     ctx = np.full(128, 8192)
-    return _scattered(3, seed, rng, ctx, 64, 8, 128, 0, num_layers, dtype)
+    return _scattered(3, seed, rng, ctx, 64, 8, 128, 0, num_layers, dtype, block_size)
 
 
-def config5(seed: int = 5, num_layers: int = 1, dtype: str = "bf16") -> Workload:
+def config5(seed: int = 5, num_layers: int = 1, dtype: str = "bf16", block_size: int = BLOCK_SIZE) -> Workload:
     rng = np.random.default_rng(seed)
     ctx = rng.integers(4096, 32768, size=32, endpoint=True)
-    return _scattered(5, seed, rng, ctx, 32, 8, 128, 4096, num_layers, dtype)
+    return _scattered(5, seed, rng, ctx, 32, 8, 128, 4096, num_layers, dtype, block_size)
 
 
-def _scattered(config, seed, rng, ctx, Hq, Hkv, D, window, L, dtype="bf16") -> Workload:
-    spans = [_row_span(int(c), window, BLOCK_SIZE) for c in ctx]
+def config6(seed: int = 6, num_layers: int = 1, dtype: str = "bf16", block_size: int = BLOCK_SIZE) -> Workload:
+    """Long contexts, the case the block-size trade-off is about ([Optimizing]
+    Trade-offs of Block Size Tuning: 32-token blocks for 32k+ contexts with a
+    Llama-3-8B-shaped model): 16 sequences of U[32768, 40960] tokens."""
+    rng = np.random.default_rng(seed)
+    ctx = rng.integers(32768, 40960, size=16, endpoint=True)
+    return _scattered(6, seed, rng, ctx, 32, 8, 128, 0, num_layers, dtype, block_size)
+
+
+def _scattered(config, seed, rng, ctx, Hq, Hkv, D, window, L, dtype="bf16", block_size=BLOCK_SIZE) -> Workload:
+    spans = [_row_span(int(c), window, block_size) for c in ctx]
     need = sum(nrow for _, nrow, _ in spans)
     NB = math.ceil(1.25 * need)
     perm = rng.permutation(NB).astype(np.int32)
@@ -311,8 +328,8 @@ def _scattered(config, seed, rng, ctx, Hq, Hkv, D, window, L, dtype="bf16") -> W
     for _, nrow, _ in spans:
         rows.append(list(perm[k:k + nrow]))
         k += nrow
-    w = _base(config, seed, dtype, L, NB, Hq, Hkv, D, window, ctx)
-    w.pool = _draw_pool(seed, w.dtype, L, NB, Hkv, D, BLOCK_SIZE)
+    w = _base(config, seed, dtype, L, NB, Hq, Hkv, D, window, ctx, block_size)
+    w.pool = _draw_pool(seed, w.dtype, L, NB, Hkv, D, block_size)
     _finish(w, rows)
     _draw_q(w)
     return w
@@ -320,17 +337,18 @@ def _scattered(config, seed, rng, ctx, Hq, Hkv, D, window, L, dtype="bf16") -> W
 
 def shared_prefix(seed: int, prefix_tokens: int, tails, num_q_heads: int = 32, num_kv_heads: int = 8,
                   head_dim: int = 128, num_layers: int = 1, config: int = 0, rng=None,
-                  dtype: str = "bf16") -> Workload:
-    """bf16 batch whose rows all start with the same prefix_tokens / 16 full
-    blocks (the same physical ids in every row) followed by a private tail
-    of tails[s] tokens (0 = the prefix alone); physical ids are a seeded
-    permutation of a pool 1.25x the unique blocks."""
-    if prefix_tokens % BLOCK_SIZE:
+                  dtype: str = "bf16", block_size: int = BLOCK_SIZE) -> Workload:
+    """Batch whose rows all start with the same prefix_tokens / block_size
+    full blocks (the same physical ids in every row) followed by a private
+    tail of tails[s] tokens (0 = the prefix alone); physical ids are a
+    seeded permutation of a pool 1.25x the unique blocks."""
+    B = block_size
+    if prefix_tokens % B:
         raise ValueError("the shared prefix is a whole number of blocks")
     rng = np.random.default_rng(seed) if rng is None else rng
     tails = np.asarray(tails, dtype=np.int64)
-    prefix_blocks = prefix_tokens // BLOCK_SIZE
-    tail_blocks = [(int(t) + BLOCK_SIZE - 1) // BLOCK_SIZE for t in tails]
+    prefix_blocks = prefix_tokens // B
+    tail_blocks = [(int(t) + B - 1) // B for t in tails]
     unique = prefix_blocks + sum(tail_blocks)
     NB = math.ceil(1.25 * unique)
     perm = rng.permutation(NB).astype(np.int32)
@@ -340,41 +358,48 @@ def shared_prefix(seed: int, prefix_tokens: int, tails, num_q_heads: int = 32, n
         rows.append(prefix + list(perm[k:k + nb]))
         k += nb
     ctx = prefix_tokens + tails
-    w = _base(config, seed, dtype, num_layers, NB, num_q_heads, num_kv_heads, head_dim, 0, ctx)
-    w.pool = _draw_pool(seed, w.dtype, num_layers, NB, num_kv_heads, head_dim, BLOCK_SIZE)
+    w = _base(config, seed, dtype, num_layers, NB, num_q_heads, num_kv_heads, head_dim, 0, ctx, B)
+    w.pool = _draw_pool(seed, w.dtype, num_layers, NB, num_kv_heads, head_dim, B)
     _finish(w, rows)
     _draw_q(w)
     return w
 
 
-def config4(seed: int = 4, num_layers: int = 1, num_seqs: int = 256, dtype: str = "bf16") -> Workload:
-    """Shared 2048-token prefix (128 blocks, same physical ids in every row)
-    plus a private tail per sequence whose last block is partial."""
+def config4(seed: int = 4, num_layers: int = 1, num_seqs: int = 256, dtype: str = "bf16",
+            block_size: int = BLOCK_SIZE) -> Workload:
+    """Shared 2048-token prefix (128 blocks of 16, same physical ids in every
+    row) plus a private tail per sequence whose last 16-token block is
+    partial."""
     rng = np.random.default_rng(seed)
     tails_allowed = np.array([t for t in range(1, 513) if t % BLOCK_SIZE != 0])
     tails = rng.choice(tails_allowed, size=num_seqs)
-    return shared_prefix(seed, 2048, tails, 32, 8, 128, num_layers, config=4, rng=rng, dtype=dtype)
+    return shared_prefix(seed, 2048, tails, 32, 8, 128, num_layers, config=4, rng=rng, dtype=dtype,
+                         block_size=block_size)
 
 
-def make(config: int, seed: Optional[int] = None, num_layers: int = 1, dtype: str = "bf16") -> Workload:
-    """Workload `config` (1..5); configs 2..5 can hold their pool as fp8
-    codes instead of bf16 (dtype="fp8"), with the same shapes and tables."""
+def make(config: int, seed: Optional[int] = None, num_layers: int = 1, dtype: str = "bf16",
+         block_size: int = BLOCK_SIZE) -> Workload:
+    """Workload `config` (1..6); configs 2..6 can hold their pool as fp8
+    codes instead of bf16 (dtype="fp8") and use 32-token blocks
+    (block_size=32), with the same shapes and lengths."""
     seed = config if seed is None else seed
     if config == 1:
-        if num_layers != 1 or dtype != "bf16":
-            raise ValueError("config 1 is one fp32 layer")
+        if num_layers != 1 or dtype != "bf16" or block_size != BLOCK_SIZE:
+            raise ValueError("config 1 is one fp32 layer of 16-token blocks")
         return config1(seed)
-    return {2: config2, 3: config3, 4: config4, 5: config5}[config](seed, num_layers=num_layers, dtype=dtype)
+    return {2: config2, 3: config3, 4: config4, 5: config5, 6: config6}[config](
+        seed, num_layers=num_layers, dtype=dtype, block_size=block_size)
 
 
 def custom(seed: int, ctx, num_q_heads: int, num_kv_heads: int, head_dim: int,
            dtype: str = "bf16", window: int = 0, num_layers: int = 1,
-           pool_factor: float = 1.25, extra_blocks: int = 2) -> Workload:
+           pool_factor: float = 1.25, extra_blocks: int = 2, block_size: int = BLOCK_SIZE) -> Workload:
     """A small workload of the same structure with chosen shapes (parity
-    sweeps over lengths, head groups, head_dim and window offsets)."""
+    sweeps over lengths, head groups, head_dim, window offsets and block
+    size)."""
     rng = np.random.default_rng(seed)
     ctx = np.asarray(ctx, dtype=np.int64)
-    spans = [_row_span(int(c), window, BLOCK_SIZE) if c > 0 else (0, 0, 0) for c in ctx]
+    spans = [_row_span(int(c), window, block_size) if c > 0 else (0, 0, 0) for c in ctx]
     need = sum(nrow for _, nrow, _ in spans)
     NB = max(math.ceil(pool_factor * need), need + extra_blocks)
     perm = rng.permutation(NB).astype(np.int32)
@@ -382,8 +407,8 @@ def custom(seed: int, ctx, num_q_heads: int, num_kv_heads: int, head_dim: int,
     for _, nrow, _ in spans:
         rows.append(list(perm[k:k + nrow]))
         k += nrow
-    w = _base(0, seed, dtype, num_layers, NB, num_q_heads, num_kv_heads, head_dim, window, ctx)
-    w.pool = _draw_pool(seed, dtype, num_layers, NB, num_kv_heads, head_dim, BLOCK_SIZE)
+    w = _base(0, seed, dtype, num_layers, NB, num_q_heads, num_kv_heads, head_dim, window, ctx, block_size)
+    w.pool = _draw_pool(seed, dtype, num_layers, NB, num_kv_heads, head_dim, block_size)
     width_rows = [r if r else [] for r in rows]
     width = max([len(r) for r in width_rows] + [1]) + 1
     w.block_tables = _fill_tables(width_rows, width, 0)
