@@ -22,7 +22,7 @@ namespace {
 #define KVP_MFMA_WAVES_PER_EU 2
 #endif
 
-template <int D, int DEPTH, bool FP8>
+template <int D, int DEPTH, bool FP8, int BS>  // BS = log2(block size / 16)
 __global__ __launch_bounds__(kThreads, KVP_MFMA_WAVES_PER_EU) void decode_mfma_kernel(const DecodeParams P) {
   constexpr int NBUF = DEPTH + 1;
   __shared__ float o_s[kWaves][16][D + 1];
@@ -49,12 +49,13 @@ __global__ __launch_bounds__(kThreads, KVP_MFMA_WAVES_PER_EU) void decode_mfma_k
   const int ctx = P.seq_lens[s];
   const int32_t* row = P.block_tables + (size_t)s * P.max_blocks;
   const int jl = part * P.part_blocks + lane;
-  int my_id = -1;
-  if (P.bshift == 0 && lane < P.part_blocks && jl < P.max_blocks) my_id = tile_id(row, jl, 0, P.num_blocks);
+  int my_id = 0;
+  if (BS == 0 && lane < P.part_blocks && jl < P.max_blocks) my_id = row[jl];
   MfmaRow<D> st;
   st.load_q((const uint16_t*)P.q, (size_t)s * P.num_q_heads + h0, nh, lane);
-  const RowSpan rs = row_span(ctx, P.window, P.max_blocks, P.bshift);
-  if (P.bshift != 0 && lane < P.part_blocks && jl < rs.nblocks) my_id = tile_id(row, rs.t0 + jl, P.bshift, P.num_blocks);
+  const RowSpan rs = row_span(ctx, P.window, P.max_blocks, BS);
+  const int t0 = BS ? rs.t0 : 0;
+  if (BS != 0 && lane < P.part_blocks && jl < rs.nblocks) my_id = row[(t0 + jl) >> BS];
   const int nparts = (rs.nblocks + P.part_blocks - 1) / P.part_blocks;
   if (rs.nblocks == 0) {
     if (part == 0)
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(kThreads, KVP_MFMA_WAVES_PER_EU) void decode_mfma_k
   const int nbp = min(P.part_blocks, rs.nblocks - jb);
 
   const void* pool = P.pool_layer;
-  const MfmaLanes la = mfma_lanes<D>(P.num_kv_heads, kvh, lane, P.bshift);
+  const MfmaLanes la = mfma_lanes<D, BS>(P.num_kv_heads, kvh, lane);
   st.reset();
   const int so = rs.start_off;
   const int send = rs.start_off + rs.n;
@@ -76,7 +77,8 @@ __global__ __launch_bounds__(kThreads, KVP_MFMA_WAVES_PER_EU) void decode_mfma_k
   const int cnt = nbp > wave ? (nbp - wave + kWaves - 1) / kWaves : 0;
   auto issue = [&](int k, MfmaTiles<D, FP8>& t) {
     const int kc = k < cnt ? k : cnt - 1;  // past the end: re-read the last block (a cache hit)
-    mfma_issue(t, pool, la, __builtin_amdgcn_readlane(my_id, wave + kc * kWaves), P.num_blocks);
+    mfma_issue<BS>(t, pool, la, __builtin_amdgcn_readlane(my_id, wave + kc * kWaves),
+                   (t0 + jb + wave + kc * kWaves) & ((1 << BS) - 1), P.num_blocks);
   };
 
   // Software pipeline: the loads of block k + DEPTH are issued before block k
@@ -115,24 +117,30 @@ __global__ __launch_bounds__(kThreads, KVP_MFMA_WAVES_PER_EU) void decode_mfma_k
   finish_partition<uint16_t, D, 16>(P, o_s, m_s, l_s, s, h0, nh, part, nparts);
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, int BS>
 hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid(p.num_kv_heads * p.qgroups, p.num_seqs, p.num_parts);
   const dim3 block(kThreads);
   switch (p.depth) {
-    case 1: hipLaunchKernelGGL((decode_mfma_kernel<D, 1, FP8>), grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((decode_mfma_kernel<D, 2, FP8>), grid, block, 0, stream, p); break;
-    case 3: hipLaunchKernelGGL((decode_mfma_kernel<D, 3, FP8>), grid, block, 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((decode_mfma_kernel<D, 1, FP8, BS>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((decode_mfma_kernel<D, 2, FP8, BS>), grid, block, 0, stream, p); break;
+    case 3: hipLaunchKernelGGL((decode_mfma_kernel<D, 3, FP8, BS>), grid, block, 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_dt(const DecodeParams& p, hipStream_t stream) {
+  if (p.kv_fp8) return p.bshift ? launch_d<D, true, 1>(p, stream) : launch_d<D, true, 0>(p, stream);
+  return p.bshift ? launch_d<D, false, 1>(p, stream) : launch_d<D, false, 0>(p, stream);
+}
+
 }  // namespace
 
 hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t stream) {
-  if (head_dim == 128) return p.kv_fp8 ? launch_d<128, true>(p, stream) : launch_d<128, false>(p, stream);
-  if (head_dim == 64) return p.kv_fp8 ? launch_d<64, true>(p, stream) : launch_d<64, false>(p, stream);
+  if (head_dim == 128) return launch_dt<128>(p, stream);
+  if (head_dim == 64) return launch_dt<64>(p, stream);
   return hipErrorInvalidValue;
 }
 

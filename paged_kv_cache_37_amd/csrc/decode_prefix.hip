@@ -22,7 +22,7 @@
 namespace kvp {
 namespace {
 
-template <int D, int DEPTH, bool FP8>
+template <int D, int DEPTH, bool FP8, int BS>  // BS = log2(block size / 16)
 __global__ __launch_bounds__(kThreads, 2) void decode_prefix_kernel(const DecodeParams P) {
   constexpr int NBUF = DEPTH + 1;
   __shared__ float o_s[kWaves][16][D + 1];
@@ -57,21 +57,22 @@ __global__ __launch_bounds__(kThreads, 2) void decode_prefix_kernel(const Decode
   // This wave's contiguous quarter of the prefix tiles (16 tokens each; a
   // 32-token block holds two); their ids from the first entries of row 0,
   // the same in every row.
-  const int nb = P.prefix_blocks << P.bshift;
+  const int nb = P.prefix_blocks << BS;
   const int j0 = (int)(((long long)nb * wave) >> 2), j1 = (int)(((long long)nb * (wave + 1)) >> 2);
   const int cnt = j1 - j0;
-  // The wave's tile ids, staged in LDS.  The row tiles of one KV head all
+  // The blocks of the wave's tiles, staged in LDS.  The row tiles of one KV head all
   // read the same blocks: each starts its walk at a different tile, so that
   // concurrent waves spread over the L2 channels.
-  for (int i = lane; i < cnt; i += 64) ids_s[wave][i] = tile_id(P.block_tables, j0 + i, P.bshift, P.num_blocks);
+  for (int i = lane; i < cnt; i += 64) ids_s[wave][i] = P.block_tables[(j0 + i) >> BS];
   const int rot = cnt > 0 ? (int)(((long long)tile * 37) % cnt) : 0;
   const void* pool = P.pool_layer;
-  const MfmaLanes la = mfma_lanes<D>(P.num_kv_heads, kvh, lane, P.bshift);
+  const MfmaLanes la = mfma_lanes<D, BS>(P.num_kv_heads, kvh, lane);
   int issued = 0;
   auto issue = [&](MfmaTiles<D, FP8>& t) {
     const int k = issued < cnt ? issued : cnt - 1;  // past the end: re-read the last block (a cache hit)
     const int kr = k + rot < cnt ? k + rot : k + rot - cnt;
-    mfma_issue(t, pool, la, __builtin_amdgcn_readfirstlane(ids_s[wave][kr]), P.num_blocks);
+    mfma_issue<BS>(t, pool, la, __builtin_amdgcn_readfirstlane(ids_s[wave][kr]), (j0 + kr) & ((1 << BS) - 1),
+                   P.num_blocks);
     ++issued;
   };
 
@@ -133,24 +134,29 @@ __global__ __launch_bounds__(kThreads, 2) void decode_prefix_kernel(const Decode
   }
 }
 
+template <int D>
+hipError_t launch_p(const DecodeParams& p, unsigned grid, hipStream_t stream) {
+  const dim3 g(grid), b(kThreads);
+  if (p.kv_fp8 && p.bshift)
+    hipLaunchKernelGGL((decode_prefix_kernel<D, 2, true, 1>), g, b, 0, stream, p);
+  else if (p.kv_fp8)
+    hipLaunchKernelGGL((decode_prefix_kernel<D, 2, true, 0>), g, b, 0, stream, p);
+  else if (p.bshift)
+    hipLaunchKernelGGL((decode_prefix_kernel<D, 2, false, 1>), g, b, 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_prefix_kernel<D, 2, false, 0>), g, b, 0, stream, p);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_decode_prefix(const DecodeParams& p, int head_dim, hipStream_t stream) {
   const long long tiles = ((long long)p.num_seqs * p.group + 15) / 16;
   const long long grid = tiles * p.num_kv_heads;
   if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidValue;
-  const dim3 g((unsigned)grid), b(kThreads);
-  if (head_dim == 128 && p.kv_fp8)
-    hipLaunchKernelGGL((decode_prefix_kernel<128, 2, true>), g, b, 0, stream, p);
-  else if (head_dim == 128)
-    hipLaunchKernelGGL((decode_prefix_kernel<128, 2, false>), g, b, 0, stream, p);
-  else if (head_dim == 64 && p.kv_fp8)
-    hipLaunchKernelGGL((decode_prefix_kernel<64, 2, true>), g, b, 0, stream, p);
-  else if (head_dim == 64)
-    hipLaunchKernelGGL((decode_prefix_kernel<64, 2, false>), g, b, 0, stream, p);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (head_dim == 128) return launch_p<128>(p, (unsigned)grid, stream);
+  if (head_dim == 64) return launch_p<64>(p, (unsigned)grid, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace kvp

@@ -78,13 +78,13 @@ struct StreamTile {
 // own last block), so no ordering between waves is needed.  Into an FP8
 // pool the new token goes as its codes (the same rounding as cache_write),
 // and the attention uses those codes.
-template <int D, int DEPTH, bool FUSED, bool FP8>
+template <int D, int DEPTH, bool FUSED, bool FP8, int BS>  // BS = log2(block size / 16)
 __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stream_kernel(const DecodeParams P) {
   constexpr int NBUF = DEPTH + 1;
   __shared__ int pre[kMaxStreamSeqs + 1];  // pre[s] = tiles of sequences < s
-  __shared__ uint8_t t0s[kMaxStreamSeqs];  // the first attended tile's place in its block (32-token blocks)
+  __shared__ uint8_t t0s[BS ? kMaxStreamSeqs : 1];  // the first attended tile's place in its block
   __shared__ int wsum[kWaves];
-  const int ptiles = P.prefix_blocks << P.bshift;  // tiles of the shared prefix (cascade)
+  const int ptiles = P.prefix_blocks << BS;  // tiles of the shared prefix (cascade)
   const int S = P.num_seqs;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -98,10 +98,10 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
     for (int i = 0; i < per; ++i) {
       const int s = s0 + i;
       if (s < S) {
-        const RowSpan rs = row_span(P.seq_lens[s], P.window, P.max_blocks, P.bshift);
+        const RowSpan rs = row_span(P.seq_lens[s], P.window, P.max_blocks, BS);
         const int nb = max(rs.nblocks - ptiles, 0);
         pre[s + 1] = nb;
-        t0s[s] = (uint8_t)rs.t0;
+        if constexpr (BS != 0) t0s[s] = (uint8_t)rs.t0;
         local += nb;
       }
     }
@@ -169,28 +169,31 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
     return min(P.heads_per_wg, P.group - (hg - kvh * P.qgroups) * P.heads_per_wg);
   };
 
-  // Tile id of tile j (counted after the shared prefix) of sequence s's row.
-  auto tid = [&](int s, int j) {
-    return tile_id(P.block_tables + (size_t)s * P.max_blocks, t0s[s] + ptiles + j, P.bshift, P.num_blocks);
-  };
+  // Table entry holding tile j (counted after the shared prefix) of sequence
+  // s's row; t0 is the row's first tile in its block.
+  auto tid = [&](int s, int t0, int j) { return P.block_tables[(size_t)s * P.max_blocks + ((t0 + ptiles + j) >> BS)]; };
+  auto t0_of = [&](int s) { return BS ? (int)t0s[s] : 0; };
 
   // ---- issue side: walks the range DEPTH tiles ahead of the compute ----
   RowCtx ir = row_at(t_begin);  // row of the next tile to issue
   int ij = (int)(t_begin - ir.a);
   int irow_id = 0;
-  int ids_a = ij + lane < ir.nb ? tid(ir.s, ij + lane) : -1;            // tiles ij .. ij+63
-  int ids_b = ij + 64 + lane < ir.nb ? tid(ir.s, ij + 64 + lane) : -1;  // tiles ij+64 .. ij+127
-  int ids_base = ij;                                                     // tile held by lane 0 of ids_a
-  RowCtx nr = row_after(ir);                                             // the row after, prefetched
-  int ids_n = lane < nr.nb ? tid(nr.s, lane) : -1;
-  MfmaLanes ila = mfma_lanes<D>(P.num_kv_heads, ir.hg / P.qgroups, lane, P.bshift);
+  int it0 = t0_of(ir.s);
+  int ids_a = ij + lane < ir.nb ? tid(ir.s, it0, ij + lane) : 0;            // blocks of tiles ij .. ij+63
+  int ids_b = ij + 64 + lane < ir.nb ? tid(ir.s, it0, ij + 64 + lane) : 0;  // tiles ij+64 .. ij+127
+  int ids_base = ij;                                                         // tile held by lane 0 of ids_a
+  RowCtx nr = row_after(ir);                                                 // the row after, prefetched
+  int nt0 = t0_of(nr.s);
+  int ids_n = lane < nr.nb ? tid(nr.s, nt0, lane) : 0;
+  constexpr int SUB = (1 << BS) - 1;
+  MfmaLanes ila = mfma_lanes<D, BS>(P.num_kv_heads, ir.hg / P.qgroups, lane);
   int issued = 0;
 
   auto issue = [&](StreamTile<D, FP8>& x) {
     if (issued >= n_tiles) {  // past the range: re-issue the last tile (a cache hit), same context
-      mfma_issue(x.t, pool, ila, __builtin_amdgcn_readlane(ij - 1 - ids_base < 64 ? ids_a : ids_b,
-                                                               (ij - 1 - ids_base) & 63),
-                    P.num_blocks);
+      mfma_issue<BS>(x.t, pool, ila,
+                     __builtin_amdgcn_readlane(ij - 1 - ids_base < 64 ? ids_a : ids_b, (ij - 1 - ids_base) & 63),
+                     (it0 + ptiles + ij - 1) & SUB, P.num_blocks);
       x.j = -1;
       return;
     }
@@ -198,18 +201,21 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
       ir = nr;
       ij = 0;
       ++irow_id;
+      it0 = nt0;
       ids_a = ids_n;
-      ids_b = 64 + lane < ir.nb ? tid(ir.s, 64 + lane) : -1;
+      ids_b = 64 + lane < ir.nb ? tid(ir.s, it0, 64 + lane) : 0;
       ids_base = 0;
       nr = row_after(ir);
-      ids_n = lane < nr.nb ? tid(nr.s, lane) : -1;
-      ila = mfma_lanes<D>(P.num_kv_heads, ir.hg / P.qgroups, lane, P.bshift);
+      nt0 = t0_of(nr.s);
+      ids_n = lane < nr.nb ? tid(nr.s, nt0, lane) : 0;
+      ila = mfma_lanes<D, BS>(P.num_kv_heads, ir.hg / P.qgroups, lane);
     } else if (ij - ids_base == 64) {  // next chunk of 64 tiles: rotate, fetch the one after
       ids_a = ids_b;
       ids_base += 64;
-      ids_b = ids_base + 64 + lane < ir.nb ? tid(ir.s, ids_base + 64 + lane) : -1;
+      ids_b = ids_base + 64 + lane < ir.nb ? tid(ir.s, it0, ids_base + 64 + lane) : 0;
     }
-    mfma_issue(x.t, pool, ila, __builtin_amdgcn_readlane(ids_a, ij - ids_base), P.num_blocks);
+    mfma_issue<BS>(x.t, pool, ila, __builtin_amdgcn_readlane(ids_a, ij - ids_base), (it0 + ptiles + ij) & SUB,
+                   P.num_blocks);
     x.j = ij;
     x.row_id = irow_id;
     ++ij;
@@ -220,7 +226,7 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
   RowCtx cr = row_at(t_begin);
   int crow_id = 0;
   int c_h0 = head0(cr.hg), c_nh = heads(cr.hg);
-  RowSpan crs = row_span(P.seq_lens[cr.s], P.window, P.max_blocks, P.bshift);
+  RowSpan crs = row_span(P.seq_lens[cr.s], P.window, P.max_blocks, BS);
   MfmaRow<D> st;
   st.load_q(q, (size_t)cr.s * P.num_q_heads + c_h0, c_nh, lane);
   st.reset();
@@ -293,14 +299,14 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
 
   // The new token of the current and of the next row (FUSED only): lanes
   // 0..D/8-1 hold its key (8 dims each), lanes 0..D/2-1 its value (2 dims
-  // each); slot < 0 when the row has no token to write.
+  // each), every lane its slot as loaded.  Nothing reads them before the
+  // row's last tile, so the loads never hold up the tile loads behind them.
   uint4_v kn = {0, 0, 0, 0}, kn_next = {0, 0, 0, 0};
   unsigned vn = 0, vn_next = 0;
   int slot_c = -1, slot_next = -1;
   auto load_new = [&](const RowCtx& r, uint4_v& kd, unsigned& vd, int& sd) {
     if constexpr (FUSED) {
-      const int sl = __builtin_amdgcn_readfirstlane(P.slot_mapping[r.s]);
-      sd = sl >= 0 && sl < (P.num_blocks << (4 + P.bshift)) ? sl : -1;
+      sd = P.slot_mapping[r.s];
       const size_t tok = ((size_t)r.s * P.num_kv_heads + r.hg / P.qgroups) * D;
       kd = lane < D / 8 ? ((const uint4_v*)((const uint16_t*)P.k_new + tok))[lane] : uint4_v{0, 0, 0, 0};
       vd = lane < D / 2 ? ((const unsigned*)((const uint16_t*)P.v_new + tok))[lane] : 0u;
@@ -312,11 +318,11 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
   // The row's last block holds the new token at table slot send - 1: put
   // its key and value into this wave's operands (layouts of mfma_tile.h),
   // and store them into the pool once per KV head.
-  auto put_new = [&](MfmaTiles<D, FP8>& t) {
+  auto put_new = [&](MfmaTiles<D, FP8>& t, int slot) {
     const int o = (crs.start_off + crs.n - 1) & (kBlock - 1);
     const int q4 = lane >> 4, j = lane & 15;
-    const int B = kBlock << P.bshift;  // tokens per block
-    const int kvh = cr.hg / P.qgroups, b = slot_c >> (4 + P.bshift), off = slot_c & (B - 1);
+    constexpr int B = kBlock << BS;  // tokens per block
+    const int kvh = cr.hg / P.qgroups, b = slot >> (4 + BS), off = slot & (B - 1);
     const bool writer = cr.hg % P.qgroups == 0;
     const size_t blk = (size_t)b * 2 * P.num_kv_heads * B * D;
     const size_t kt = blk + (size_t)kvh * B * D, vt = blk + (size_t)(P.num_kv_heads + kvh) * B * D;
@@ -396,7 +402,7 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
       ++crow_id;
       c_h0 = head0(cr.hg);
       c_nh = heads(cr.hg);
-      crs = row_span(ctx_next, P.window, P.max_blocks, P.bshift);
+      crs = row_span(ctx_next, P.window, P.max_blocks, BS);
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) st.qop[kk] = q_next[kk];
       st.reset();
@@ -410,7 +416,11 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
     }
     const int J = ptiles + x.j;  // the tile's place in the row span
     if constexpr (FUSED) {
-      if (slot_c >= 0 && J == crs.nblocks - 1) put_new(x.t);
+      if (J == crs.nblocks - 1) {
+        // a slot outside the pool (or negative: no new token) writes nothing
+        const int sl = __builtin_amdgcn_readfirstlane(slot_c);
+        if (sl >= 0 && sl < (P.num_blocks << (4 + BS))) put_new(x.t, sl);
+      }
     }
     st.step(x.t, J, crs.start_off, crs.start_off + crs.n, crs.nblocks, P.scale_log2, lane);
   };
@@ -535,18 +545,18 @@ __global__ __launch_bounds__(256) void decode_stream_reduce_kernel(const DecodeP
   for (int e = 0; e < PER; ++e) out[lane + 64 * e] = bf16_rne(num[e] * inv);
 }
 
-template <int D, int DEPTH, bool FP8>
+template <int D, int DEPTH, bool FP8, int BS>
 hipError_t launch_sd(const DecodeParams& p, hipStream_t stream) {
   if (p.prefix_blocks > 0) {
     const hipError_t e = launch_decode_prefix(p, D, stream);
     if (e != hipSuccess) return e;
   }
   if (p.slot_mapping) {
-    // a deeper ring fits beside the new token's registers only with FP8 operands
-    if constexpr (DEPTH != 1 && !FP8) return hipErrorInvalidValue;
-    else hipLaunchKernelGGL((decode_stream_kernel<D, DEPTH, true, FP8>), dim3(p.stream_wgs), dim3(kThreads), 0, stream, p);
+    // the fused step runs at ring depth 1: the new token takes the registers of a deeper ring
+    if constexpr (DEPTH != 1) return hipErrorInvalidValue;
+    else hipLaunchKernelGGL((decode_stream_kernel<D, 1, true, FP8, BS>), dim3(p.stream_wgs), dim3(kThreads), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((decode_stream_kernel<D, DEPTH, false, FP8>), dim3(p.stream_wgs), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((decode_stream_kernel<D, DEPTH, false, FP8, BS>), dim3(p.stream_wgs), dim3(kThreads), 0, stream, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -555,35 +565,43 @@ hipError_t launch_sd(const DecodeParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, int BS>
 hipError_t launch_s(const DecodeParams& p, hipStream_t stream) {
   switch (p.depth) {
-    case 1: return launch_sd<D, 1, FP8>(p, stream);
-    case 2: return launch_sd<D, 2, FP8>(p, stream);
+    case 1: return launch_sd<D, 1, FP8, BS>(p, stream);
+    case 2: return launch_sd<D, 2, FP8, BS>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int D, bool FP8>
+template <int D>
+hipError_t launch_st(const DecodeParams& p, hipStream_t stream) {
+  if (p.kv_fp8) return p.bshift ? launch_s<D, true, 1>(p, stream) : launch_s<D, true, 0>(p, stream);
+  return p.bshift ? launch_s<D, false, 1>(p, stream) : launch_s<D, false, 0>(p, stream);
+}
+
+template <int D, bool FP8, int BS>
 const void* symbol_of(int depth, bool fused) {
-  if (fused) {
-    if (depth == 1) return (const void*)decode_stream_kernel<D, 1, true, FP8>;
-    if constexpr (FP8) return (const void*)decode_stream_kernel<D, 2, true, true>;
-    return nullptr;
-  }
-  return depth == 1 ? (const void*)decode_stream_kernel<D, 1, false, FP8> : (const void*)decode_stream_kernel<D, 2, false, FP8>;
+  if (fused) return depth == 1 ? (const void*)decode_stream_kernel<D, 1, true, FP8, BS> : nullptr;
+  return depth == 1 ? (const void*)decode_stream_kernel<D, 1, false, FP8, BS>
+                    : (const void*)decode_stream_kernel<D, 2, false, FP8, BS>;
+}
+
+template <int D>
+const void* symbol_d(int depth, bool fused, bool fp8, int bshift) {
+  if (fp8) return bshift ? symbol_of<D, true, 1>(depth, fused) : symbol_of<D, true, 0>(depth, fused);
+  return bshift ? symbol_of<D, false, 1>(depth, fused) : symbol_of<D, false, 0>(depth, fused);
 }
 
 }  // namespace
 
-const void* stream_kernel_symbol(int head_dim, int depth, bool fused, bool fp8) {
-  if (head_dim == 128) return fp8 ? symbol_of<128, true>(depth, fused) : symbol_of<128, false>(depth, fused);
-  return fp8 ? symbol_of<64, true>(depth, fused) : symbol_of<64, false>(depth, fused);
+const void* stream_kernel_symbol(int head_dim, int depth, bool fused, bool fp8, int bshift) {
+  return head_dim == 128 ? symbol_d<128>(depth, fused, fp8, bshift) : symbol_d<64>(depth, fused, fp8, bshift);
 }
 
 hipError_t launch_decode_stream(const DecodeParams& p, int head_dim, hipStream_t stream) {
-  if (head_dim == 128) return p.kv_fp8 ? launch_s<128, true>(p, stream) : launch_s<128, false>(p, stream);
-  if (head_dim == 64) return p.kv_fp8 ? launch_s<64, true>(p, stream) : launch_s<64, false>(p, stream);
+  if (head_dim == 128) return launch_st<128>(p, stream);
+  if (head_dim == 64) return launch_st<64>(p, stream);
   return hipErrorInvalidValue;
 }
 

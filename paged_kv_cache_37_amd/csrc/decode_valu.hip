@@ -74,10 +74,11 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
   const int ctx = P.seq_lens[s];
   const int32_t* row = P.block_tables + (size_t)s * P.max_blocks;
   const int jl = part * P.part_blocks + lane;
-  int my_id = -1;
-  if (P.bshift == 0 && lane < P.part_blocks && jl < P.max_blocks) my_id = tile_id(row, jl, 0, P.num_blocks);
+  int my_id = 0;
+  if (P.bshift == 0 && lane < P.part_blocks && jl < P.max_blocks) my_id = row[jl];
   const RowSpan rs = row_span(ctx, P.window, P.max_blocks, P.bshift);
-  if (P.bshift != 0 && lane < P.part_blocks && jl < rs.nblocks) my_id = tile_id(row, rs.t0 + jl, P.bshift, P.num_blocks);
+  const int t0 = rs.t0;  // 0 with 16-token blocks
+  if (P.bshift != 0 && lane < P.part_blocks && jl < rs.nblocks) my_id = row[(t0 + jl) >> P.bshift];
   const int nparts = (rs.nblocks + P.part_blocks - 1) / P.part_blocks;
   T* out = (T*)P.out;
   if (rs.nblocks == 0) {
@@ -139,10 +140,11 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
   const int cnt = nbp > wave ? (nbp - wave + kWaves - 1) / kWaves : 0;
   auto issue = [&](int k, Tiles& t) {
     const int kl = k < cnt ? k : cnt - 1;  // past the end: re-read the last block (a cache hit)
-    int id = __builtin_amdgcn_readlane(my_id, wave + kl * kWaves);  // tile id (tile_id())
-    t.bad = (unsigned)id >= ((unsigned)P.num_blocks << P.bshift);
+    int id = __builtin_amdgcn_readlane(my_id, wave + kl * kWaves);  // block of tile jb + wave + kl * kWaves
+    const int sub = (t0 + jb + wave + kl * kWaves) & ((1 << P.bshift) - 1);
+    t.bad = (unsigned)id >= (unsigned)P.num_blocks;
     if (t.bad) id = 0;
-    const T* base = pool + (size_t)(id >> P.bshift) * blk_stride + (size_t)(id & ((1 << P.bshift) - 1)) * 16 * D + k_off;
+    const T* base = pool + (size_t)id * blk_stride + (size_t)sub * 16 * D + k_off;
 #pragma unroll
     for (int i = 0; i < KCH; ++i) t.k[i] = *(const uint4v*)(base + kt_tok * D + (kc + 4 * i) * E);
 #pragma unroll

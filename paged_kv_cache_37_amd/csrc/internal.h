@@ -57,8 +57,10 @@ struct DecodeParams {
 // starts at a multiple of the block size; under a sliding window the first
 // attended position may lie past its first tile (t0 = 1 in a 32-token
 // block) and past slots of the tile it lies in (start_off).  Tile J of the
-// span is tile t0 + J of the row: entry (t0 + J) >> bshift, half
-// (t0 + J) & 1 of a 32-token block.
+// span is tile t0 + J of the row: tile (t0 + J) & ((1 << bshift) - 1) of
+// the block in entry (t0 + J) >> bshift.  Kernels load entries as stored
+// and check them against the pool only when they use them, so that a table
+// load never has to complete before the tile loads issued after it.
 struct RowSpan {
   int start_off;  // unattended leading slots of the first tile
   int n;          // attended keys
@@ -81,13 +83,6 @@ __device__ __forceinline__ RowSpan row_span(int ctx, int window, int max_blocks,
   return r;
 }
 
-// Tile j of a table row (j counted from the row's first entry) as a tile
-// id: physical block << bshift plus the tile's place in the block, or -1
-// when the entry names no block of the pool.
-__device__ __forceinline__ int tile_id(const int32_t* __restrict__ row, int j, int bshift, int num_blocks) {
-  const int b = row[j >> bshift];
-  return (unsigned)b < (unsigned)num_blocks ? (b << bshift) | (j & ((1 << bshift) - 1)) : -1;
-}
 
 // Launchers (each defined next to its kernel).
 hipError_t launch_cache_write(void* pool_layer, int dtype, int num_blocks, int bshift, int num_kv_heads,
@@ -102,7 +97,7 @@ hipError_t launch_decode_reduce(const DecodeParams& p, int dtype, int head_dim, 
 hipError_t launch_decode_stream(const DecodeParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_decode_prefix(const DecodeParams& p, int head_dim, hipStream_t stream);
 // The streaming kernel instance a launch would use (for occupancy queries);
-// nullptr for one that is never launched (the bf16 fused step runs at depth 1).
-const void* stream_kernel_symbol(int head_dim, int depth, bool fused, bool fp8);
+// nullptr for one that is never launched (the fused step runs at depth 1).
+const void* stream_kernel_symbol(int head_dim, int depth, bool fused, bool fp8, int bshift);
 
 }  // namespace kvp

@@ -158,17 +158,17 @@ int32_t cache_write(kvp_pool pool, int32_t layer, const void* k_new, const void*
 // Resident workgroups of the streaming kernel on the current device:
 // compute units x workgroups per compute unit at the kernel's occupancy.
 // 0 if there is no device to ask.
-static int32_t stream_workgroups(int32_t head_dim, int32_t depth, bool fused, bool fp8) {
+static int32_t stream_workgroups(int32_t head_dim, int32_t depth, bool fused, bool fp8, int32_t bshift) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  static thread_local int cached_dev = -1, cached_d = 0, cached_depth = 0, cached_wgs = 0;
+  static thread_local int cached_dev = -1, cached_d = 0, cached_depth = 0, cached_wgs = 0, cached_bs = 0;
   static thread_local bool cached_fused = false, cached_fp8 = false;
   if (dev == cached_dev && head_dim == cached_d && depth == cached_depth && fused == cached_fused &&
-      fp8 == cached_fp8)
+      fp8 == cached_fp8 && bshift == cached_bs)
     return cached_wgs;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kvp::stream_kernel_symbol(head_dim, depth, fused, fp8),
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kvp::stream_kernel_symbol(head_dim, depth, fused, fp8, bshift),
                                                    kvp::kThreads, 0) != hipSuccess ||
       per_cu <= 0)
     return 0;
@@ -177,6 +177,7 @@ static int32_t stream_workgroups(int32_t head_dim, int32_t depth, bool fused, bo
   cached_depth = depth;
   cached_fused = fused;
   cached_fp8 = fp8;
+  cached_bs = bshift;
   cached_wgs = cus * per_cu;
   return cached_wgs;
 }
@@ -207,10 +208,6 @@ static int32_t decode_depth(int32_t path, bool fp8) {
   return path == PATH_MFMA ? 2 : 1;
 }
 
-// Ring depth of the fused step: the new token's registers leave room for a
-// second tile in flight only with FP8 (8-byte) operands.
-static int32_t fused_depth(int32_t depth, bool fp8) { return fp8 ? depth : 1; }
-
 static int32_t plan(kvp_pool pool, int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks, int32_t partition_tokens,
                     int32_t variant, kvp::DecodeParams* p, int32_t* path) {
   const kvp_pool_desc& d = pool->desc;
@@ -237,7 +234,7 @@ static int32_t plan(kvp_pool pool, int32_t num_seqs, int32_t num_q_heads, int32_
         pth = PATH_VALU;
       } else {
         const int32_t wgs =
-            partition_tokens == 0 ? stream_workgroups(d.head_dim, decode_depth(PATH_STREAM, fp8), false, fp8) : 0;
+            partition_tokens == 0 ? stream_workgroups(d.head_dim, decode_depth(PATH_STREAM, fp8), false, fp8, bs) : 0;
         pth = wgs > 0 && stream_fits(num_seqs, max_tiles, mfma_groups, wgs) ? PATH_STREAM : PATH_MFMA;
       }
       break;
@@ -285,7 +282,7 @@ static int32_t plan(kvp_pool pool, int32_t num_seqs, int32_t num_q_heads, int32_
   p->bshift = bs;
   p->depth = decode_depth(pth, fp8);
   if (pth == PATH_STREAM) {
-    p->stream_wgs = stream_workgroups(d.head_dim, p->depth, false, fp8);
+    p->stream_wgs = stream_workgroups(d.head_dim, p->depth, false, fp8, bs);
     if (p->stream_wgs <= 0) return fail(KVP_ERR_HIP, "cannot size the streaming grid (no device?)");
     if (!stream_fits(num_seqs, max_tiles, d.num_kv_heads * qgroups, p->stream_wgs))
       return fail(KVP_ERR_UNSUPPORTED, "num_seqs * max_blocks_per_seq too large for the STREAM variant");
@@ -345,7 +342,7 @@ size_t paged_decode_workspace_bytes(kvp_pool pool, int32_t num_seqs, int32_t num
                                    : grid_workspace(p, pool->desc.head_dim, &a);
     if (path == PATH_STREAM) {  // the fused step's grid (its own occupancy) must fit too
       const bool fp8 = pool->desc.dtype == KVP_FP8_E4M3;
-      p.stream_wgs = stream_workgroups(pool->desc.head_dim, fused_depth(p.depth, fp8), true, fp8);
+      p.stream_wgs = stream_workgroups(pool->desc.head_dim, 1, true, fp8, p.bshift);
       const size_t nf = stream_workspace(p, pool->desc.head_dim).total;
       if (nf > n) n = nf;
     }
@@ -381,10 +378,10 @@ static int32_t decode(kvp_pool pool, const kvp_decode_args* a, const void* k_new
       return fail(KVP_ERR_INVALID_ARG, "k_new/v_new must be 16-byte aligned, slot_mapping 4-byte aligned");
   }
   if (write && path == PATH_STREAM) {
-    // the fused kernel holds the new token in registers
+    // the fused kernel holds the new token in registers: ring depth 1
     const bool fp8 = d.dtype == KVP_FP8_E4M3;
-    p.depth = fused_depth(p.depth, fp8);
-    p.stream_wgs = stream_workgroups(d.head_dim, p.depth, true, fp8);
+    p.depth = 1;
+    p.stream_wgs = stream_workgroups(d.head_dim, 1, true, fp8, p.bshift);
     if (p.stream_wgs <= 0) return fail(KVP_ERR_HIP, "cannot size the streaming grid (no device?)");
     p.k_new = k_new;
     p.v_new = v_new;

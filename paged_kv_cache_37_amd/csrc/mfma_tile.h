@@ -43,7 +43,7 @@ struct MfmaTiles {
 };
 
 // Per-wave addressing of one KV head's tiles inside a block.  A block of
-// 16 << bshift tokens holds, per head, a K tile [B][D] and a V tile
+// 16 << BS tokens holds, per head, a K tile [B][D] and a V tile
 // [B/4][D][4]; its 16-token tile u is rows 16u.. of the K tile and quads
 // 4u.. of the V tile, both at element offset 16 u D.
 struct MfmaLanes {
@@ -52,14 +52,12 @@ struct MfmaLanes {
   size_t v_rel;       // V tile = K tile + v_rel
   int k_lane;         // this lane's K element offset (+ 32 kk)
   int v_lane;         // this lane's V element offset (+ 128 m)
-  int bshift;         // log2(block size / 16)
 };
 
-template <int D>
-__device__ __forceinline__ MfmaLanes mfma_lanes(int num_kv_heads, int kvh, int lane, int bshift) {
-  const size_t tile = (size_t)(16 << bshift) * D;
+template <int D, int BS>  // BS = log2(block size / 16)
+__device__ __forceinline__ MfmaLanes mfma_lanes(int num_kv_heads, int kvh, int lane) {
+  const size_t tile = (size_t)(16 << BS) * D;
   MfmaLanes a;
-  a.bshift = bshift;
   a.blk_stride = 2 * (size_t)num_kv_heads * tile;
   a.k_off = (size_t)kvh * tile;
   a.v_rel = (size_t)num_kv_heads * tile;
@@ -68,17 +66,16 @@ __device__ __forceinline__ MfmaLanes mfma_lanes(int num_kv_heads, int kvh, int l
   return a;
 }
 
-// Issue the loads of tile `id` (tile_id(): block << bshift | tile in the
-// block; checked against the pool size, -1 = no block).
-template <int D, bool FP8>
+// Issue the loads of tile `sub` (< 1 << BS) of physical block `id` (the
+// block id is checked against the pool size here).
+template <int BS, int D, bool FP8>
 __device__ __forceinline__ void mfma_issue(MfmaTiles<D, FP8>& t, const void* __restrict__ pool, const MfmaLanes& a,
-                                           int id, int num_blocks) {
+                                           int id, int sub, int num_blocks) {
   using E = std::conditional_t<FP8, uint8_t, uint16_t>;
   using Op = typename MfmaTiles<D, FP8>::Op;
-  t.bad = (unsigned)id >= ((unsigned)num_blocks << a.bshift);
+  t.bad = (unsigned)id >= (unsigned)num_blocks;
   if (t.bad) id = 0;
-  const E* kt = (const E*)pool + (size_t)(id >> a.bshift) * a.blk_stride + (size_t)(id & ((1 << a.bshift) - 1)) * 16 * D +
-                a.k_off;
+  const E* kt = (const E*)pool + (size_t)id * a.blk_stride + (size_t)(BS ? sub : 0) * 16 * D + a.k_off;
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk) t.k[kk] = *(const Op*)(kt + a.k_lane + 32 * kk);
 #pragma unroll
