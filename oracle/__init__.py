@@ -18,6 +18,10 @@ paged KV cache computes, in float64:
   for every query head;
 * ``decode_attention_bruteforce`` -- the same result by per-token address
   translation and scalar loops (tiny inputs only);
+* ``prefill_attention`` -- multi-token (prefill / chunked-prefill)
+  attention: each query of a sequence's chunk attends, causally, the keys up
+  to its own position (``prefill_attention_bruteforce`` is the scalar
+  version for tiny inputs);
 * ``row_span`` / ``check_tables`` -- how many table entries a sequence owns
   and the rule that only a row's last block (and, under a sliding window,
   its first) may be partial.
@@ -65,3 +69,4 @@ from .paged import (  # noqa: F401
     softmax_weights,
     to_f64,
 )
+from .prefill import chunk_first, prefill_attention, prefill_attention_bruteforce, prefill_attention_seq  # noqa: F401,E501

@@ -37,6 +37,13 @@ The five workloads (sizes as in the write-ups' Llama-3 serving examples):
 6. long contexts: 16 Llama-3-8B-shaped sequences of 32768..40960 tokens (the
    case for which a 32-token block size is offered).
 
+``prefill_batch`` draws multi-token (chunked-prefill) batches: per sequence
+a prior context already cached and a chunk of q_len new tokens whose K/V
+are in the pool too; queries are packed [T, Hq, D] with offsets cu_q_lens.
+``prefill_config`` is the Llama-3-8B-shaped chunked-prefill step: 8
+sequences x 512-token chunks (4096 batched tokens) over prior contexts
+uniform in [0, 8192].
+
 Blocks hold 16 tokens unless a generator is asked for block_size=32 (same
 lengths and shapes; tables in 32-token blocks).
 """
@@ -61,6 +68,7 @@ _CONFIG_NAMES = {
     4: "shared-prefix-S256-H32/8-D128-prefix2048+tail1..512",
     5: "sliding-window4096-S32-H32/8-D128-ctx4096..32768",
     6: "llama3-8b-long-S16-H32/8-D128-ctx32768..40960",
+    7: "chunked-prefill-S8x512-H32/8-D128-prior0..8192",
 }
 
 
@@ -465,3 +473,63 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return _to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+# ---------------------------------------------------------------------------
+# multi-token (prefill / chunked-prefill) batches
+
+
+def prefill_batch(seed: int, prior, q_lens, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                  window: int = 0, dtype: str = "bf16", block_size: int = BLOCK_SIZE, num_layers: int = 1,
+                  config: int = 0, pool_factor: float = 1.25) -> Workload:
+    """Sequence s has prior[s] cached tokens and a chunk of q_lens[s] new
+    tokens (positions prior .. prior + q_len - 1, their K/V already stored);
+    seq_lens = prior + q_lens.  Table rows list the blocks covering every
+    position some query of the chunk attends (from max(0, prior + 1 - W)
+    under a window W, else 0); physical ids are a seeded permutation of a
+    pool pool_factor x the blocks in use; unowned slots NaN.  q is
+    [T, Hq, D] with sequence s's chunk at rows cu_q_lens[s] .. cu_q_lens[s+1]-1."""
+    B = block_size
+    rng = np.random.default_rng(seed)
+    prior = np.asarray(prior, dtype=np.int64)
+    q_lens = np.asarray(q_lens, dtype=np.int64)
+    ctx = prior + q_lens
+    firsts = [max(0, int(p) + 1 - window) if window > 0 else 0 for p in prior]
+    nbs = [((int(c) - 1) // B - f // B + 1) if c > 0 else 0 for c, f in zip(ctx, firsts)]
+    need = sum(nbs)
+    NB = max(math.ceil(pool_factor * need), need + 2)
+    perm = rng.permutation(NB).astype(np.int32)
+    rows, k = [], 0
+    for nb in nbs:
+        rows.append(list(perm[k:k + nb]))
+        k += nb
+    w = _base(config, seed, dtype, num_layers, NB, num_q_heads, num_kv_heads, head_dim, window, ctx, B)
+    w.pool = _draw_pool(seed, dtype, num_layers, NB, num_kv_heads, head_dim, B)
+    owned = np.zeros((NB, B), dtype=bool)
+    for s, (c, f) in enumerate(zip(ctx, firsts)):
+        for pos in range(f, int(c)):
+            owned[rows[s][pos // B - f // B], pos % B] = True
+    blk, slot = np.nonzero(~owned)
+    w.pool[:, blk, :, slot] = _nan(dtype)
+    w.unused_blocks = np.nonzero(~owned.any(axis=1))[0].astype(np.int32)
+    w.owned_slots = int(owned.sum())
+    width = max([len(r) for r in rows] + [1]) + 1
+    w.block_tables = _fill_tables(rows, width, int(w.unused_blocks[0]))
+    w.row_blocks = np.array([len(r) for r in rows], dtype=np.int32)
+    w.prior = prior.astype(np.int32)
+    w.q_lens = q_lens.astype(np.int32)
+    w.cu_q_lens = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    T = int(w.cu_q_lens[-1])
+    w.q = _store(_normal_f32(seed, 7, (T, num_q_heads, head_dim)), w.act_dtype)
+    return w
+
+
+def prefill_config(seed: int = 7, num_layers: int = 1, dtype: str = "bf16", block_size: int = BLOCK_SIZE,
+                   num_seqs: int = 8, chunk: int = 512, max_prior: int = 8192) -> Workload:
+    """The Llama-3-8B-shaped chunked-prefill step (config 7): num_seqs
+    sequences, each a chunk of `chunk` tokens after a prior context uniform
+    in [0, max_prior]."""
+    rng = np.random.default_rng(seed)
+    prior = rng.integers(0, max_prior, size=num_seqs, endpoint=True)
+    return prefill_batch(seed, prior, np.full(num_seqs, chunk), 32, 8, 128, 0, dtype, block_size, num_layers,
+                         config=7)
