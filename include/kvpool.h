@@ -318,6 +318,67 @@ int32_t paged_decode_step(kvp_pool pool, const kvp_decode_args* args, const void
 int32_t kv_pool_copy_blocks(kvp_pool pool, const int32_t* src, const int32_t* dst,
                             int32_t num_pairs, hipStream_t stream);
 
+/*
+ * Arguments of one multi-token (prefill / chunked-prefill) attention call.
+ */
+typedef struct {
+  int32_t layer;
+  const void* q;                /* device [total_q][num_q_heads][head_dim], BF16,
+                                   16-byte aligned; chunk s is rows
+                                   cu_q_lens[s] .. cu_q_lens[s+1]-1          */
+  void* out;                    /* device, same shape and dtype as q           */
+  const int32_t* cu_q_lens;     /* device int32 [num_seqs + 1], cu_q_lens[0] = 0,
+                                   nondecreasing, cu_q_lens[num_seqs] = total_q */
+  const int32_t* seq_lens;      /* device int32 [num_seqs]: context length after
+                                   the chunk (the chunk's tokens included)      */
+  const int32_t* block_tables;  /* device int32 [num_seqs][max_blocks_per_seq] */
+  int32_t max_blocks_per_seq;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t total_q;              /* rows of q and out                            */
+  int32_t max_q_len;            /* >= every chunk length: sizes the launch; rows
+                                   of a longer chunk past it are not written    */
+  int32_t sliding_window;       /* 0 = full context, else W > 0                 */
+  float scale;                  /* softmax scale, usually 1/sqrt(head_dim)     */
+} kvp_prefill_args;
+
+/*
+ * paged_prefill_attention -- attention of a batch of multi-token chunks
+ * (one layer), over keys already in the pool.
+ *   [Optimizing] "The Block Manager and Dynamic Allocation Lifecycle" (The
+ *   Prefill Phase: a prompt's K/V are computed in one parallel step and
+ *   written into its blocks) and "Production Tuning: Ratios, Failure Modes,
+ *   and Mitigations" (Failure Mode 2: chunked prefill splits a long prompt
+ *   into chunks that are processed step by step).
+ *
+ *   The chunk of sequence s is its last q_len = cu_q_lens[s+1] - cu_q_lens[s]
+ *   positions, ctx - q_len .. ctx - 1 (ctx = seq_lens[s]); their K/V must be
+ *   in the pool (cache_write, or paged_prefill_step).  The query at
+ *   position p attends the keys at positions lo(p) .. p (causal), with
+ *   lo(p) = 0, or max(0, p + 1 - W) under a sliding window W; for q_len = 1
+ *   this is decode attention at context p + 1.  Row s of block_tables
+ *   lists the blocks covering positions first .. ctx - 1, first =
+ *   lo(ctx - q_len) (logical blocks first / B .. (ctx - 1) / B).
+ *   out[row][h] = softmax over those keys of (K q * scale) times V, KV head
+ *   h / G; fp32 accumulation, BF16 output (round to nearest even).  With
+ *   an FP8 pool K and V are the codes times the layer's scales.  A chunk
+ *   longer than its context leaves zeros in its rows without a position.
+ *
+ *   Errors: KVP_ERR_INVALID_ARG (nulls, misalignment, layer, heads, sizes),
+ *   KVP_ERR_UNSUPPORTED (fp32 pools), KVP_ERR_HIP.
+ */
+int32_t paged_prefill_attention(kvp_pool pool, const kvp_prefill_args* args, hipStream_t stream);
+
+/*
+ * paged_prefill_step -- store the chunks' K/V, then attend: cache_write of
+ * total_q tokens (k_new, v_new [total_q][num_kv_heads][head_dim] BF16, 16-byte
+ * aligned; slot_mapping [total_q], the slot of each chunk token's position)
+ * followed by paged_prefill_attention on the same stream.  Same results as
+ * the two calls.  Errors as for both.
+ */
+int32_t paged_prefill_step(kvp_pool pool, const kvp_prefill_args* args, const void* k_new, const void* v_new,
+                           const int32_t* slot_mapping, hipStream_t stream);
+
 /* Static text of a status code. */
 const char* kvp_status_str(int32_t status);
 

@@ -41,6 +41,8 @@ EXPORTS = (
     "paged_decode_attention",
     "paged_decode_step",
     "kv_pool_copy_blocks",
+    "paged_prefill_attention",
+    "paged_prefill_step",
     "kvp_status_str",
     "kvp_last_error",
 )
@@ -77,6 +79,24 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
+class PrefillArgs(ctypes.Structure):
+    _fields_ = [
+        ("layer", ctypes.c_int32),
+        ("q", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+        ("cu_q_lens", ctypes.c_void_p),
+        ("seq_lens", ctypes.c_void_p),
+        ("block_tables", ctypes.c_void_p),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("num_seqs", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("total_q", ctypes.c_int32),
+        ("max_q_len", ctypes.c_int32),
+        ("sliding_window", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+    ]
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
@@ -96,6 +116,8 @@ def _load() -> ctypes.CDLL:
         "paged_decode_attention": (i32, [P, ctypes.POINTER(DecodeArgs), P]),
         "paged_decode_step": (i32, [P, ctypes.POINTER(DecodeArgs), P, P, P, P]),
         "kv_pool_copy_blocks": (i32, [P, P, P, i32, P]),
+        "paged_prefill_attention": (i32, [P, ctypes.POINTER(PrefillArgs), P]),
+        "paged_prefill_step": (i32, [P, ctypes.POINTER(PrefillArgs), P, P, P, P]),
         "kvp_status_str": (ctypes.c_char_p, [i32]),
         "kvp_last_error": (ctypes.c_char_p, []),
     }

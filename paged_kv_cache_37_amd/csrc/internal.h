@@ -53,6 +53,29 @@ struct DecodeParams {
   float inv_v_scale;
 };
 
+// Geometry and arguments of one prefill (multi-token) launch.
+struct PrefillParams {
+  const void* pool_layer;       // first element of this layer's blocks
+  const void* q;                // [T][Hq][D] bf16
+  void* out;                    // [T][Hq][D] bf16
+  const int32_t* cu_q_lens;     // [S + 1] chunk offsets into q / out
+  const int32_t* seq_lens;      // [S] context after the chunk
+  const int32_t* block_tables;  // [S][max_blocks]
+  int32_t max_blocks;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t num_blocks;
+  int32_t bshift;
+  int32_t group;                // G
+  int32_t window;
+  int32_t qtiles;               // 128-row query tiles per (sequence, KV head) for the longest chunk
+  int32_t max_q_len;            // chunk rows past it are not computed
+  int32_t total_q;              // rows of q / out (reads and writes stay inside)
+  float scale_log2;             // scale * log2(e) (* k_scale for FP8)
+  float v_scale;
+};
+
 // Span of one block-table row in 16-token tiles.  The row's first block
 // starts at a multiple of the block size; under a sliding window the first
 // attended position may lie past its first tile (t0 = 1 in a 32-token
@@ -96,6 +119,7 @@ hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t s
 hipError_t launch_decode_reduce(const DecodeParams& p, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_decode_stream(const DecodeParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_decode_prefix(const DecodeParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams& p, int head_dim, bool fp8, hipStream_t stream);
 // The streaming kernel instance a launch would use (for occupancy queries);
 // nullptr for one that is never launched (the fused step runs at depth 1).
 const void* stream_kernel_symbol(int head_dim, int depth, bool fused, bool fp8, int bshift);

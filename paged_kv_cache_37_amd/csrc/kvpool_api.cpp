@@ -460,6 +460,91 @@ int32_t paged_decode_step(kvp_pool pool, const kvp_decode_args* a, const void* k
   return decode(pool, a, k_new, v_new, slot_mapping, stream);
 }
 
+}  // extern "C"
+
+// Checks of a prefill call and its launch parameters; *launch is false when
+// there is nothing to do.
+static int32_t plan_prefill(kvp_pool pool, const kvp_prefill_args* a, kvp::PrefillParams* p, bool* launch) {
+  *launch = false;
+  if (!pool || !a) return fail(KVP_ERR_INVALID_ARG, "NULL pool or args");
+  const kvp_pool_desc& d = pool->desc;
+  if (a->layer < 0 || a->layer >= d.num_layers) return fail(KVP_ERR_INVALID_ARG, "layer %d out of range", a->layer);
+  if (d.dtype == KVP_F32) return fail(KVP_ERR_UNSUPPORTED, "prefill attention takes bf16 and fp8 pools");
+  if (a->num_seqs < 0 || a->total_q < 0 || a->max_q_len < 0)
+    return fail(KVP_ERR_INVALID_ARG, "num_seqs, total_q and max_q_len must be >= 0");
+  if (a->num_q_heads < 1 || a->num_q_heads % d.num_kv_heads != 0)
+    return fail(KVP_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                a->num_q_heads, d.num_kv_heads);
+  if (a->max_blocks_per_seq < 1) return fail(KVP_ERR_INVALID_ARG, "max_blocks_per_seq must be >= 1");
+  if ((int64_t)a->max_blocks_per_seq * d.block_size > INT32_MAX)
+    return fail(KVP_ERR_INVALID_ARG, "max_blocks_per_seq * block_size must fit in int32");
+  if (a->sliding_window < 0) return fail(KVP_ERR_INVALID_ARG, "sliding_window < 0");
+  if (!std::isfinite(a->scale)) return fail(KVP_ERR_INVALID_ARG, "scale is not finite");
+  if (a->num_seqs == 0 || a->total_q == 0 || a->max_q_len == 0) return ok();
+  if (!a->q || !a->out || !a->cu_q_lens || !a->seq_lens || !a->block_tables)
+    return fail(KVP_ERR_INVALID_ARG, "NULL q, out, cu_q_lens, seq_lens or block_tables");
+  if (!aligned(a->q, 16) || !aligned(a->out, 16) || !aligned(a->cu_q_lens, 4) || !aligned(a->seq_lens, 4) ||
+      !aligned(a->block_tables, 4))
+    return fail(KVP_ERR_INVALID_ARG, "q/out must be 16-byte aligned, index arrays 4-byte aligned");
+  const int32_t G = a->num_q_heads / d.num_kv_heads;
+  const int64_t qtiles = ((int64_t)a->max_q_len * G + 127) / 128;
+  if ((int64_t)a->num_seqs * d.num_kv_heads * qtiles > INT32_MAX || (int64_t)a->max_q_len * G > INT32_MAX)
+    return fail(KVP_ERR_UNSUPPORTED, "too many query rows for one launch");
+  const bool fp8 = d.dtype == KVP_FP8_E4M3;
+  std::memset(p, 0, sizeof(*p));
+  p->pool_layer = (const char*)pool->base + (size_t)a->layer * layer_elems(d) * elt_bytes(d.dtype);
+  p->q = a->q;
+  p->out = a->out;
+  p->cu_q_lens = a->cu_q_lens;
+  p->seq_lens = a->seq_lens;
+  p->block_tables = a->block_tables;
+  p->max_blocks = a->max_blocks_per_seq;
+  p->num_seqs = a->num_seqs;
+  p->num_q_heads = a->num_q_heads;
+  p->num_kv_heads = d.num_kv_heads;
+  p->num_blocks = d.num_blocks;
+  p->bshift = bshift_of(d);
+  p->group = G;
+  p->window = a->sliding_window;
+  p->qtiles = (int32_t)qtiles;
+  p->max_q_len = a->max_q_len;
+  p->total_q = a->total_q;
+  p->scale_log2 = a->scale * 1.4426950408889634f * (fp8 ? pool->k_scale[a->layer] : 1.0f);
+  p->v_scale = fp8 ? pool->v_scale[a->layer] : 1.0f;
+  *launch = true;
+  return KVP_OK;
+}
+
+extern "C" {
+
+int32_t paged_prefill_attention(kvp_pool pool, const kvp_prefill_args* a, hipStream_t stream) {
+  kvp::PrefillParams p;
+  bool launch = false;
+  const int32_t st = plan_prefill(pool, a, &p, &launch);
+  if (st != KVP_OK || !launch) return st;
+  const hipError_t e = kvp::launch_prefill(p, pool->desc.head_dim, pool->desc.dtype == KVP_FP8_E4M3, stream);
+  if (e != hipSuccess) return fail(KVP_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int32_t paged_prefill_step(kvp_pool pool, const kvp_prefill_args* a, const void* k_new, const void* v_new,
+                           const int32_t* slot_mapping, hipStream_t stream) {
+  kvp::PrefillParams p;
+  bool launch = false;
+  int32_t st = plan_prefill(pool, a, &p, &launch);  // every check before anything is launched
+  if (st != KVP_OK) return st;
+  if (a->total_q > 0) {
+    if (!k_new || !v_new || !slot_mapping) return fail(KVP_ERR_INVALID_ARG, "NULL k_new, v_new or slot_mapping");
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(slot_mapping, 4))
+      return fail(KVP_ERR_INVALID_ARG, "k_new/v_new must be 16-byte aligned, slot_mapping 4-byte aligned");
+  }
+  st = cache_write(pool, a->layer, k_new, v_new, slot_mapping, a->total_q, stream);
+  if (st != KVP_OK || !launch) return st;
+  const hipError_t e = kvp::launch_prefill(p, pool->desc.head_dim, pool->desc.dtype == KVP_FP8_E4M3, stream);
+  if (e != hipSuccess) return fail(KVP_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int32_t kv_pool_copy_blocks(kvp_pool pool, const int32_t* src, const int32_t* dst, int32_t num_pairs,
                             hipStream_t stream) {
   if (!pool) return fail(KVP_ERR_INVALID_ARG, "pool is NULL");

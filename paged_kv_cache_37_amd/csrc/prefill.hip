@@ -1,0 +1,356 @@
+// Multi-token (prefill / chunked-prefill) paged attention on the CDNA4
+// matrix cores.
+//
+// "Optimizing KV Cache Memory Management in vLLM with PagedAttention and
+// Dynamic Block Allocation", The Block Manager and Dynamic Allocation
+// Lifecycle (The Prefill Phase: a prompt's K/V are computed in one parallel
+// step and written into its blocks) and Production Tuning, Failure Mode 2
+// (chunked prefill: a long prompt is processed in chunks).  Sequence s's
+// chunk holds its last q_len positions; the query at position p attends the
+// keys at positions lo(p) .. p (lo(p) = 0, or p + 1 - W under a window W),
+// walking the sequence's block table like decode does.
+//
+// Unlike decode this is a dense contraction: q_len * G query rows of one KV
+// head meet the same keys.  A workgroup takes 128 query rows of one
+// (sequence, KV head) (rows r = token * G + head); its four waves hold 32
+// rows each as two 16-column blocks of the MFMA B operand.  Keys go 32 at a
+// time (two 16-token tiles): the workgroup copies their K and V from the
+// pool into LDS once (double-buffered, the next step's loads in flight
+// during this step's compute) and every wave reads its operands there.
+//   S^T = K Q^T   v_mfma_f32_16x16x32_bf16, per 16-key tile, A = K rows
+//   O  += P V     v_mfma_f32_16x16x32_bf16, A = P (the two tiles' S^T
+//                 outputs of a lane are its 8 reduction values), B = V
+//                 (one quad-interleaved 16-byte read per tile gives two
+//                 dims x four keys; two tiles give the 8 keys of B)
+// with the base-2 online softmax of the decode kernels.  P is rounded to
+// bf16 once (the result stays within the bf16 tolerance; decode's two-term
+// P keeps split-K invariance, which prefill does not need).
+#include "mfma_tile.h"
+
+namespace kvp {
+namespace {
+
+constexpr int kPfWaves = 4;
+constexpr int kPfRows = 128;  // query rows per workgroup (32 per wave)
+constexpr int kStep = 32;     // keys per step
+
+template <bool FP8>
+using Elt = std::conditional_t<FP8, uint8_t, uint16_t>;
+
+// 16 bytes of pool elements as an MFMA operand: bf16 as is, FP8 codes
+// (8 bytes) widened.
+template <bool FP8>
+__device__ __forceinline__ uint4_v lds_operand(const Elt<FP8>* p) {
+  if constexpr (FP8)
+    return fp8_widen8(*(const uint2_v*)p);
+  else
+    return *(const uint4_v*)p;
+}
+
+__device__ __forceinline__ int wave_min(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+  return v;
+}
+
+template <int D, bool FP8, int BS>
+__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParams P) {
+  using E = Elt<FP8>;
+  constexpr int CH = 16 / sizeof(E);           // elements per 16-byte copy
+  constexpr int KROW = D + CH;                 // LDS K row: 16 bytes of padding, so 16 rows hit distinct banks
+  constexpr int KCH = kStep * D / CH;          // 16-byte chunks of K per step (and of V)
+  constexpr int CPT = (KCH + kThreads - 1) / kThreads;  // chunks per thread
+  __shared__ __align__(16) E k_s[2][kStep * KROW];
+  __shared__ __align__(16) E v_s[2][kStep * D];  // two tiles of [4][D][4]
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int SK = P.num_seqs * P.num_kv_heads;
+  // heaviest tiles (latest tokens, most keys) first
+  const int qt = P.qtiles - 1 - (int)(blockIdx.x / SK);
+  const int rest = blockIdx.x - (P.qtiles - 1 - qt) * SK;
+  const int s = rest / P.num_kv_heads, kvh = rest - s * P.num_kv_heads;
+  const int G = P.group;
+  const int c0 = P.cu_q_lens[s];
+  const int q_len = P.cu_q_lens[s + 1] - c0;
+  const int ctx = P.seq_lens[s];
+  // rows computed: the chunk's, up to max_q_len tokens and inside q / out
+  const int rows = max(0, min(min(q_len, P.max_q_len), P.total_q - c0)) * G;
+  const int r_wg = qt * kPfRows;
+  if (r_wg >= rows || c0 < 0) return;  // the whole workgroup: before any barrier
+
+  // Positions: token i at p = ctx - q_len + i.  The table row starts at the
+  // block holding `first`, the first key any query of the chunk attends;
+  // span slot u is position first - so + u.
+  const int B = kBlock << BS;
+  const int p0 = ctx - q_len;
+  const int first = P.window > 0 ? max(0, p0 + 1 - P.window) : 0;
+  const int off = first & (B - 1);
+  const int t0 = off >> 4, so = off & (kBlock - 1);
+  const int base = first - so;                   // position of span slot 0
+  // span slots holding keys: [so, send); a row longer than its table
+  // attends what the table holds
+  const int send = min(so + max(ctx - first, 0), P.max_blocks * B - kBlock * t0);
+  const int ntiles = (send + kBlock - 1) / kBlock;
+  auto lo_of = [&](int p) { return P.window > 0 ? max(0, p + 1 - P.window) : 0; };
+
+  // The workgroup's key range (rows are in position order).
+  const int r_last = min(r_wg + kPfRows, rows) - 1;
+  const int pa = max(p0 + r_wg / G, 0), pb = p0 + r_last / G;
+  const int u_lo = lo_of(pa) - base, u_hi = pb - base;  // span slots some row attends
+  const int k_lo = max(u_lo, 0) / kStep, k_hi = u_hi / kStep;
+  const int nsteps = pb >= 0 ? k_hi - k_lo + 1 : 0;
+
+  // This lane's query column in each of the wave's two blocks.
+  const int q4 = lane >> 4, col = lane & 15;
+  uint4_v qop[2][D / 32];
+  int lo_c[2], hi_c[2];
+  int hrow[2];  // query row of the column, -1 past the chunk
+  for (int nb = 0; nb < 2; ++nb) {
+    const int r = r_wg + wave * 32 + nb * 16 + col;
+    const int i = r / G, g = r - (r / G) * G;
+    const int p = p0 + i;
+    const bool ok = r < rows && p >= 0;  // a row without a position (chunk longer than its context) stores zeros
+    hrow[nb] = r < rows ? r : -1;
+    lo_c[nb] = ok ? lo_of(p) - base : INT32_MAX;
+    hi_c[nb] = ok ? p - base : -1;
+    const uint16_t* qp = (const uint16_t*)P.q + ((size_t)(c0 + i) * P.num_q_heads + kvh * G + g) * D + 8 * q4;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) qop[nb][kk] = ok ? *(const uint4_v*)(qp + 32 * kk) : uint4_v{0, 0, 0, 0};
+  }
+  // the wave's own key range (its columns' union), for skipping steps
+  const int w_lo = wave_min(min(lo_c[0], lo_c[1]));
+  const int w_hi = wave_max(max(hi_c[0], hi_c[1]));
+
+  // Block ids of the tiles 64 at a time (lane i: tile jb + i), the next 64 prefetched.
+  const int32_t* row = P.block_tables + (size_t)s * P.max_blocks;
+  auto entry = [&](int J) { return J < ntiles ? row[(t0 + J) >> BS] : 0; };
+  int jb = 2 * k_lo;
+  int ids_a = entry(jb + lane), ids_b = entry(jb + 64 + lane);
+
+  const size_t tile = (size_t)B * D;  // one head's K (or V) tile of a block
+  const size_t blk_stride = 2 * (size_t)P.num_kv_heads * tile;
+  const E* pool = (const E*)P.pool_layer + (size_t)kvh * tile;
+  const size_t v_rel = (size_t)P.num_kv_heads * tile;
+
+  // Global -> registers for the step's two tiles (bad or absent tiles read
+  // block 0; their keys are masked), registers -> LDS.
+  uint4_v kreg[CPT], vreg[CPT];
+  bool bad[2] = {false, false};
+  auto fetch = [&](int k) {
+    const int J0 = 2 * k;
+    if (J0 - jb >= 64) {  // rotate the id window (uniform: every wave walks the same steps)
+      ids_a = ids_b;
+      jb += 64;
+      ids_b = entry(jb + 64 + lane);
+    }
+    const E* src[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int J = J0 + t;
+      int id = __builtin_amdgcn_readlane(J - jb < 64 ? ids_a : ids_b, (J - jb) & 63);
+      bad[t] = J >= ntiles || (unsigned)id >= (unsigned)P.num_blocks;
+      if (bad[t]) id = 0;
+      src[t] = pool + (size_t)id * blk_stride + (size_t)((t0 + J) & ((1 << BS) - 1)) * kBlock * D;
+    }
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = threadIdx.x + i * kThreads;  // K chunk: key c / (D / CH), column chunk c % (D / CH)
+      const int key = c / (D / CH), cc = c - key * (D / CH);
+      if (c < KCH) kreg[i] = *(const uint4_v*)(src[key >> 4] + (key & 15) * D + cc * CH);
+    }
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = threadIdx.x + i * kThreads;  // V chunk c of the two tiles, tile by tile
+      const int t = c / (16 * D / CH), cc = c - t * (16 * D / CH);
+      if (c < KCH) vreg[i] = *(const uint4_v*)(src[t] + v_rel + cc * CH);
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = threadIdx.x + i * kThreads;
+      const int key = c / (D / CH), cc = c - key * (D / CH);
+      if (c < KCH) *(uint4_v*)(&k_s[buf][key * KROW + cc * CH]) = kreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = threadIdx.x + i * kThreads;
+      if (c < KCH) *(uint4_v*)(&v_s[buf][c * CH]) = vreg[i];
+    }
+  };
+
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  float4_v acc[2][D / 16];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n) acc[nb][n] = float4_v{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int k, int buf, bool bad0, bool bad1) {
+    const int u0 = k * kStep;  // span slot of the step's first key
+    if (u0 + kStep - 1 < w_lo || u0 > w_hi) return;  // no column of this wave attends these keys
+    const E* ks = k_s[buf];
+    const E* vs = v_s[buf];
+    // S^T per tile and column block
+    float4_v sc[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      uint4_v kf[D / 32];
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) kf[kk] = lds_operand<FP8>(ks + (t * 16 + col) * KROW + 32 * kk + 8 * q4);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        float4_v a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk)
+          a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, kf[kk]),
+                                                      __builtin_bit_cast(bf16x8_v, qop[nb][kk]), a, 0, 0, 0);
+        sc[t][nb] = a;
+      }
+    }
+    // keys of the step outside the span (or in a bad tile) hold no data:
+    // zero their V and mask their scores for every column
+    const bool vedge = bad0 || bad1 || u0 < so || u0 + kStep > send;
+    unsigned vm[2][2];  // [tile][half]: mask words for keys 4q4 + {0,1} and {2,3}
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int u = u0 + t * 16 + 4 * q4 + 2 * h;
+        const bool tb = t ? bad1 : bad0;
+        const bool a = !tb && u >= so && u < send, b = !tb && u + 1 >= so && u + 1 < send;
+        vm[t][h] = (a ? 0xffffu : 0u) | (b ? 0xffff0000u : 0u);
+      }
+    uint4_v pa[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      float sv[2][4];
+      const bool cedge = vedge || u0 < lo_c[nb] || u0 + kStep - 1 > hi_c[nb];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int u = u0 + t * 16 + 4 * q4 + r;
+          const bool keep = !cedge || (((vm[t][r >> 1] >> (16 * (r & 1))) & 1u) && u >= lo_c[nb] && u <= hi_c[nb]);
+          sv[t][r] = keep ? sc[t][nb][r] * P.scale_log2 : -INFINITY;
+        }
+      float lmax = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) lmax = fmaxf(lmax, sv[t][r]);
+      if (__any(lmax > m_run[nb] + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run[nb], rows_max(lmax));
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run[nb] - m_use);
+        m_run[nb] = m_new;
+        l_run[nb] *= alpha;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float ar = __shfl(alpha, 4 * q4 + r);  // output rows here are columns 4 q4 + r
+#pragma unroll
+          for (int n = 0; n < D / 16; ++n) acc[nb][n][r] *= ar;
+        }
+      }
+      const float m_use = m_run[nb] == -INFINITY ? 0.f : m_run[nb];
+      float pr[2][4];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pr[t][r] = __builtin_amdgcn_exp2f(sv[t][r] - m_use);
+          l_run[nb] += pr[t][r];
+        }
+      pa[nb] = uint4_v{pack_bf16x2(pr[0][0], pr[0][1]), pack_bf16x2(pr[0][2], pr[0][3]),
+                       pack_bf16x2(pr[1][0], pr[1][1]), pack_bf16x2(pr[1][2], pr[1][3])};
+    }
+    // O += P V: B rows 8 q4 .. +7 are keys 4 q4 .. +3 of tile 0, then of tile 1
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) {
+      uint4_v v0 = lds_operand<FP8>(vs + ((q4 * D + 32 * m + 2 * col) * 4));
+      uint4_v v1 = lds_operand<FP8>(vs + 16 * D + ((q4 * D + 32 * m + 2 * col) * 4));
+      if (vedge) {
+        v0.x &= vm[0][0]; v0.y &= vm[0][1]; v0.z &= vm[0][0]; v0.w &= vm[0][1];
+        v1.x &= vm[1][0]; v1.y &= vm[1][1]; v1.z &= vm[1][0]; v1.w &= vm[1][1];
+      }
+      const uint4_v b0 = {v0.x, v0.y, v1.x, v1.y}, b1 = {v0.z, v0.w, v1.z, v1.w};
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        acc[nb][2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, pa[nb]),
+                                                                 __builtin_bit_cast(bf16x8_v, b0), acc[nb][2 * m], 0, 0, 0);
+        acc[nb][2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_v, pa[nb]), __builtin_bit_cast(bf16x8_v, b1), acc[nb][2 * m + 1], 0, 0, 0);
+      }
+    }
+  };
+
+  if (nsteps > 0) {
+    fetch(k_lo);
+    bool bad_c[2] = {bad[0], bad[1]};
+    stash(0);
+    __syncthreads();
+    for (int k = k_lo; k <= k_hi; ++k) {
+      const int buf = (k - k_lo) & 1;
+      const bool more = k < k_hi;
+      bool bad_n[2] = {false, false};
+      if (more) {
+        fetch(k + 1);
+        bad_n[0] = bad[0];
+        bad_n[1] = bad[1];
+      }
+      compute(k, buf, bad_c[0], bad_c[1]);
+      if (more) stash(buf ^ 1);
+      __syncthreads();
+      bad_c[0] = bad_n[0];
+      bad_c[1] = bad_n[1];
+    }
+  }
+
+  // normalise and store: output row 4 q4 + r of block nb is column 4 q4 + r
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const float l_tot = rows_sum(l_run[nb]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int g = 4 * q4 + r;
+      const float lg = __shfl(l_tot, g);
+      const int hr = __shfl(hrow[nb], g);
+      const float inv = lg > 0.f ? P.v_scale / lg : 0.f;
+      if (hr >= 0) {
+        const int i = hr / G, h = hr - (hr / G) * G;
+        unsigned* o = (unsigned*)((uint16_t*)P.out + ((size_t)(c0 + i) * P.num_q_heads + kvh * G + h) * D);
+#pragma unroll
+        for (int m = 0; m < D / 32; ++m)
+          o[16 * m + col] = pack_bf16x2(acc[nb][2 * m][r] * inv, acc[nb][2 * m + 1][r] * inv);
+      }
+    }
+  }
+}
+
+template <int D, bool FP8>
+hipError_t launch_pf(const PrefillParams& p, unsigned grid, hipStream_t stream) {
+  if (p.bshift)
+    hipLaunchKernelGGL((prefill_kernel<D, FP8, 1>), dim3(grid), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((prefill_kernel<D, FP8, 0>), dim3(grid), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillParams& p, int head_dim, bool fp8, hipStream_t stream) {
+  const long long grid = (long long)p.num_seqs * p.num_kv_heads * p.qtiles;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  if (head_dim == 128) return fp8 ? launch_pf<128, true>(p, (unsigned)grid, stream) : launch_pf<128, false>(p, (unsigned)grid, stream);
+  if (head_dim == 64) return fp8 ? launch_pf<64, true>(p, (unsigned)grid, stream) : launch_pf<64, false>(p, (unsigned)grid, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvp

@@ -11,7 +11,7 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import DecodeArgs, KVPoolError, PoolDesc, check, lib
+from ._lib import DecodeArgs, KVPoolError, PoolDesc, PrefillArgs, check, lib
 
 BLOCK_SIZE = 16  # the default block size (32 is the other one the library takes)
 
@@ -233,6 +233,65 @@ def paged_decode_step(pool: KVPool, layer: int, q: torch.Tensor, block_tables: t
     return out
 
 
+def _prefill_args(pool: KVPool, layer: int, q: torch.Tensor, cu_q_lens: torch.Tensor, block_tables: torch.Tensor,
+                  seq_lens: torch.Tensor, scale: float, max_q_len: int, out: Optional[torch.Tensor],
+                  sliding_window: int):
+    if q.dim() != 3 or q.shape[2] != pool.head_dim:
+        raise ValueError("q must be [total_q, num_q_heads, head_dim]")
+    T, Hq, _ = q.shape
+    _need(q, "q", pool.act_dtype, pool.device)
+    if cu_q_lens.dim() != 1 or cu_q_lens.shape[0] < 1:
+        raise ValueError("cu_q_lens must be [num_seqs + 1]")
+    S = int(cu_q_lens.shape[0]) - 1
+    _need(cu_q_lens, "cu_q_lens", torch.int32, pool.device)
+    _need(seq_lens, "seq_lens", torch.int32, pool.device, (S,))
+    if block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    _need(block_tables, "block_tables", torch.int32, pool.device)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", pool.act_dtype, pool.device, tuple(q.shape))
+    args = PrefillArgs(layer=layer, q=q.data_ptr(), out=out.data_ptr(), cu_q_lens=cu_q_lens.data_ptr(),
+                       seq_lens=seq_lens.data_ptr(), block_tables=block_tables.data_ptr(),
+                       max_blocks_per_seq=int(block_tables.shape[1]), num_seqs=S, num_q_heads=Hq, total_q=T,
+                       max_q_len=int(max_q_len), sliding_window=sliding_window, scale=float(scale))
+    return args, out
+
+
+def paged_prefill_attention(pool: KVPool, layer: int, q: torch.Tensor, cu_q_lens: torch.Tensor,
+                            block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float, max_q_len: int,
+                            out: Optional[torch.Tensor] = None, sliding_window: int = 0,
+                            stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Causal attention of multi-token chunks (q [T, Hq, D], chunk s at rows
+    cu_q_lens[s] .. cu_q_lens[s+1]-1, the last positions of a context of
+    seq_lens[s] tokens whose K/V are in the pool); max_q_len bounds every
+    chunk length."""
+    args, out = _prefill_args(pool, layer, q, cu_q_lens, block_tables, seq_lens, scale, max_q_len, out,
+                              sliding_window)
+    check(lib.paged_prefill_attention(pool.handle, ctypes.byref(args), _stream(pool.device, stream)),
+          "paged_prefill_attention")
+    return out
+
+
+def paged_prefill_step(pool: KVPool, layer: int, q: torch.Tensor, cu_q_lens: torch.Tensor,
+                       block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float, max_q_len: int,
+                       k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+                       out: Optional[torch.Tensor] = None, sliding_window: int = 0,
+                       stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Store the chunks' K/V (k_new/v_new [T, Hkv, D] at slot_mapping [T]),
+    then paged_prefill_attention."""
+    args, out = _prefill_args(pool, layer, q, cu_q_lens, block_tables, seq_lens, scale, max_q_len, out,
+                              sliding_window)
+    shape = (q.shape[0], pool.num_kv_heads, pool.head_dim)
+    _need(k_new, "k_new", pool.act_dtype, pool.device, shape)
+    _need(v_new, "v_new", pool.act_dtype, pool.device, shape)
+    _need(slot_mapping, "slot_mapping", torch.int32, pool.device, (q.shape[0],))
+    check(lib.paged_prefill_step(pool.handle, ctypes.byref(args), ctypes.c_void_p(k_new.data_ptr()),
+                                 ctypes.c_void_p(v_new.data_ptr()), ctypes.c_void_p(slot_mapping.data_ptr()),
+                                 _stream(pool.device, stream)), "paged_prefill_step")
+    return out
+
+
 def copy_blocks(pool: KVPool, src: torch.Tensor, dst: torch.Tensor,
                 stream: Optional[torch.cuda.Stream] = None) -> None:
     """Copy every layer's K/V of physical block src[i] into dst[i] (int32
@@ -246,4 +305,5 @@ def copy_blocks(pool: KVPool, src: torch.Tensor, dst: torch.Tensor,
 
 
 __all__ = ["KVPool", "KVPoolError", "kv_pool_create", "cache_write", "paged_decode_workspace_bytes",
-           "make_workspace", "paged_decode_attention", "paged_decode_step", "copy_blocks", "BLOCK_SIZE"]
+           "make_workspace", "paged_decode_attention", "paged_decode_step", "copy_blocks", "paged_prefill_attention",
+           "paged_prefill_step", "BLOCK_SIZE"]

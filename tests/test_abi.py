@@ -215,3 +215,35 @@ def test_block_size_32_geometry_checks(ops):
     assert ops.lib.paged_decode_attention(h, ctypes.byref(a), None) == E.KVP_ERR_INVALID_ARG
     assert b"block_size" in ops.lib.kvp_last_error()
     ops.lib.kv_pool_destroy(h)
+
+
+def test_prefill_rejects_bad_arguments_before_launch(ops):
+    E = ops._lib
+    A = ops._lib.PrefillArgs
+    base = dict(layer=0, q=0x1000, out=0x2000, cu_q_lens=0x3000, seq_lens=0x4000, block_tables=0x5000,
+                max_blocks_per_seq=4, num_seqs=2, num_q_heads=8, total_q=10, max_q_len=8, sliding_window=0,
+                scale=0.125)
+    _, h = _handle(ops, desc(ops, 1, 8, 2, 64, dtype=E.KVP_BF16))
+    _, h32 = _handle(ops, desc(ops, 1, 8, 2, 64, dtype=E.KVP_F32))
+
+    def call(hh=h, **kw):
+        a = A(**{**base, **kw})
+        return ops.lib.paged_prefill_attention(hh, ctypes.byref(a), None)
+
+    assert call(hh=h32) == E.KVP_ERR_UNSUPPORTED
+    assert call(layer=1) == E.KVP_ERR_INVALID_ARG
+    assert call(num_q_heads=7) == E.KVP_ERR_INVALID_ARG
+    assert call(q=None) == E.KVP_ERR_INVALID_ARG
+    assert call(q=0x1008) == E.KVP_ERR_INVALID_ARG
+    assert call(max_q_len=-1) == E.KVP_ERR_INVALID_ARG
+    assert call(sliding_window=-2) == E.KVP_ERR_INVALID_ARG
+    assert call(scale=float("inf")) == E.KVP_ERR_INVALID_ARG
+    assert call(max_blocks_per_seq=1 << 28) == E.KVP_ERR_INVALID_ARG
+    assert call(num_seqs=0) == 0 and call(total_q=0) == 0  # nothing to do
+    # the fused step checks the attention's arguments before writing anything
+    a = A(**{**base, "q": None})
+    assert ops.lib.paged_prefill_step(h, ctypes.byref(a), 0x6000, 0x7000, 0x8000, None) == E.KVP_ERR_INVALID_ARG
+    a = A(**base)
+    assert ops.lib.paged_prefill_step(h, ctypes.byref(a), None, 0x7000, 0x8000, None) == E.KVP_ERR_INVALID_ARG
+    ops.lib.kv_pool_destroy(h)
+    ops.lib.kv_pool_destroy(h32)

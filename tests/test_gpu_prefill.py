@@ -1,0 +1,146 @@
+"""GPU parity of multi-token (prefill / chunked-prefill) paged attention
+through the C-ABI against the prefill oracle: head groups, head_dim,
+sliding windows, 16- and 32-token blocks, bf16 and FP8 pools, chunks from
+one token to several 128-row tiles, fresh prompts and long prior contexts;
+the fused chunk write; relabelling invariance; the chunked-prefill batch
+at full size on sampled tokens."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_helpers import compare, host_to_torch, pool_dtype, say, torch_dtype, torch_to_bits
+
+pytestmark = pytest.mark.gpu
+
+
+class PDev:
+    """A prefill workload resident on the GPU."""
+
+    def __init__(self, w, device="cuda:0"):
+        from paged_kv_cache_37_amd import ops
+
+        self.w, self.ops = w, ops
+        self.dt = torch_dtype(w)
+        self.pool = ops.KVPool(w.num_layers, w.num_blocks, w.num_kv_heads, w.head_dim, pool_dtype(w), device,
+                               block_size=w.block_size)
+        self.pool.load_logical(host_to_torch(w.pool, pool_dtype(w)))
+        if w.dtype == "fp8":
+            self.pool.set_fp8_scales(0, w.k_scale, w.v_scale)
+        self.q = host_to_torch(w.q, self.dt).to(device)
+        self.cu = torch.from_numpy(w.cu_q_lens).to(device)
+        self.tables = torch.from_numpy(np.ascontiguousarray(w.block_tables)).to(device)
+        self.lens = torch.from_numpy(np.ascontiguousarray(w.seq_lens)).to(device)
+
+    def attend(self, max_q_len=None):
+        out = self.ops.paged_prefill_attention(self.pool, 0, self.q, self.cu, self.tables, self.lens, self.w.scale,
+                                               int(max(self.w.q_lens)) if max_q_len is None else max_q_len,
+                                               sliding_window=self.w.window)
+        torch.cuda.synchronize()
+        return out
+
+
+def ref_of(w, pool=None):
+    return oracle.prefill_attention(w.pool if pool is None else pool, 0, w.q, w.cu_q_lens, w.block_tables,
+                                    w.seq_lens, w.window, w.scale, k_scale=w.k_scale, v_scale=w.v_scale)
+
+
+PRIOR = [0, 1, 15, 16, 100, 0, 300, 37]
+QLEN = [1, 16, 17, 5, 64, 200, 33, 129]
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(8, 2, 128), (32, 8, 128), (8, 8, 64), (32, 1, 128), (12, 4, 64),
+                                      (64, 8, 128)])
+def test_prefill_shapes(gpu, Hq, Hkv, D):
+    """G = 4, 4, 1, 32, 3, 8; chunks of 1..200 tokens, fresh and continued."""
+    w = W.prefill_batch(100 + Hq + D, PRIOR, QLEN, Hq, Hkv, D)
+    say("prefill", Hq, Hkv, D, "T", int(w.cu_q_lens[-1]))
+    compare(PDev(w).attend(), ref_of(w), "bf16", f"prefill G{Hq // Hkv} D{D}")
+
+
+@pytest.mark.parametrize("dtype,B,window", [("bf16", 16, 40), ("bf16", 32, 0), ("bf16", 32, 40), ("fp8", 16, 0),
+                                            ("fp8", 32, 24), ("bf16", 16, 1)])
+def test_prefill_windows_blocks_dtypes(gpu, dtype, B, window):
+    w = W.prefill_batch(200 + B + window, PRIOR, QLEN, 32, 8, 128, window=window, dtype=dtype, block_size=B)
+    say("prefill", dtype, B, window)
+    compare(PDev(w).attend(), ref_of(w), "bf16", f"prefill {dtype} B{B} W{window}")
+
+
+def test_prefill_single_token_chunks_match_decode(gpu):
+    """q_len = 1: the same attention as decode at context p + 1 (both
+    within the bound of the oracle; only the P rounding differs)."""
+    prior = [0, 15, 16, 1000, 4095]
+    w = W.prefill_batch(300, prior, [1] * len(prior), 32, 8, 128)
+    out = PDev(w).attend()
+    ref = ref_of(w)
+    compare(out, ref, "bf16", "prefill q_len 1")
+    from paged_kv_cache_37_amd import ops
+
+    d = PDev(w)
+    dec = ops.paged_decode_attention(d.pool, 0, d.q, d.tables, d.lens, w.scale)
+    torch.cuda.synchronize()
+    compare(dec, ref, "bf16", "decode of the same tokens")
+
+
+def test_prefill_step_writes_then_attends(gpu):
+    """paged_prefill_step: the chunk's K/V go to their slots (bit-exact),
+    then the chunk attends them."""
+    w = W.prefill_batch(400, [0, 20, 64, 5], [40, 17, 100, 1], 16, 4, 128)
+    rng = np.random.default_rng(4)
+    T = int(w.cu_q_lens[-1])
+    k_new = W.f32_to_bf16_bits(rng.standard_normal((T, 4, 128)).astype(np.float32))
+    v_new = W.f32_to_bf16_bits(rng.standard_normal((T, 4, 128)).astype(np.float32))
+    slots = np.empty(T, np.int32)
+    for s in range(w.num_seqs):
+        ctx, q_len = int(w.seq_lens[s]), int(w.q_lens[s])
+        for i in range(q_len):
+            p = ctx - q_len + i
+            slots[w.cu_q_lens[s] + i] = w.block_tables[s][p // 16] * 16 + p % 16
+    d = PDev(w)
+    out = d.ops.paged_prefill_step(d.pool, 0, d.q, d.cu, d.tables, d.lens, w.scale, int(max(w.q_lens)),
+                                   host_to_torch(k_new, d.dt).cuda(), host_to_torch(v_new, d.dt).cuda(),
+                                   torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    pool_ref = oracle.cache_write(w.pool, 0, k_new, v_new, slots)
+    assert torch_to_bits(d.pool.to_logical()).tobytes() == np.ascontiguousarray(pool_ref).tobytes()
+    compare(out, ref_of(w, pool_ref), "bf16", "prefill step")
+
+
+def test_prefill_relabelling_is_bitwise_invisible(gpu):
+    w = W.prefill_batch(500, PRIOR, QLEN, 32, 8, 128)
+    a = PDev(w).attend()
+    perm = np.random.default_rng(9).permutation(w.num_blocks).astype(np.int32)
+    w2 = W.prefill_batch(500, PRIOR, QLEN, 32, 8, 128)
+    w2.pool = np.empty_like(w.pool)
+    w2.pool[:, perm] = w.pool
+    w2.block_tables = perm[np.asarray(w.block_tables)]
+    b = PDev(w2).attend()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_prefill_chunk_longer_than_context(gpu):
+    """Rows without a position (a chunk longer than its context) are zero;
+    the rest follow the oracle."""
+    w = W.prefill_batch(600, [0, 10], [20, 30], 8, 2, 128)
+    w.seq_lens = np.array([12, 40], np.int32)  # sequence 0: 8 of its 20 chunk rows have no position
+    out = PDev(w).attend()
+    ref = ref_of(w)
+    assert float(out[:8].abs().max()) == 0.0
+    compare(out, ref, "bf16", "chunk longer than context")
+
+
+def test_prefill_config_sampled(gpu):
+    """The chunked-prefill batch (8 x 512-token chunks over priors up to
+    8192), sampled tokens against the oracle."""
+    w = W.prefill_config()
+    out = PDev(w).attend()
+    rows, refs = [], []
+    for s in range(w.num_seqs):
+        toks = [0, 1, 127, 128, 300, 511]
+        a = int(w.cu_q_lens[s])
+        ref = oracle.prefill_attention_seq(w.pool, 0, w.q[a:a + int(w.q_lens[s])], w.block_tables[s],
+                                           int(w.seq_lens[s]), 0, w.scale, tokens=toks)
+        rows += [a + t for t in toks]
+        refs.append(ref[toks])
+    compare(out[rows], np.concatenate(refs), "bf16", "chunked-prefill batch (sampled)")
