@@ -10,6 +10,7 @@ served from the 256 MB last-level cache.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--kv-dtype bf16|fp8]
                     [--block-size 16|32]
+    python bench.py --mode prefill [...]   # the chunked-prefill step (config 7)
 
 Prints one JSON line.  `value` is the step's algorithmic bytes (K/V of the
 attended slots, each physical slot once, queries, outputs, tables, the
@@ -33,9 +34,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention: achieved HBM GB/s (% of peak) + seq·layer steps/s"
+PREFILL_METRIC = "paged prefill attention: achieved TFLOP/s (% of dense bf16 MFMA peak) + tokens/s"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 (no sparsity)
 DEFAULT_LAYERS = {1: 1, 2: 2, 3: 1, 4: 4, 5: 2, 6: 1}  # layer slices so that each step reads >= ~1 GB
-KERNEL_SOURCES = ("decode_stream.hip", "decode_prefix.hip", "copy_blocks.hip", "decode_mfma.hip", "decode_valu.hip",
+KERNEL_SOURCES = ("decode_stream.hip", "decode_prefix.hip", "prefill.hip", "copy_blocks.hip", "decode_mfma.hip",
+                  "decode_valu.hip",
                   "decode_reduce.hip", "cache_write.hip", "mfma_tile.h", "decode_common.h", "internal.h",
                   "fp8.h", "kvpool_api.cpp")
 
@@ -135,8 +139,179 @@ def cpu_baseline(w, budget_s: float = 10.0) -> dict:
     }
 
 
+def prefill_flops(w) -> int:
+    """Algorithmic FLOPs of one prefill call: per query token and query
+    head, 2 D multiply-adds per attended key for q.K and 2 D for p.V."""
+    import numpy as np
+
+    keys = 0
+    for s in range(w.num_seqs):
+        ctx, q_len = int(w.seq_lens[s]), int(w.q_lens[s])
+        p = ctx - q_len + np.arange(q_len)
+        lo = np.maximum(0, p + 1 - w.window) if w.window else np.zeros_like(p)
+        keys += int(np.maximum(p - lo + 1, 0).sum())
+    return 4 * w.head_dim * w.num_q_heads * keys
+
+
+def cpu_baseline_prefill(w, budget_s: float = 10.0) -> dict:
+    """The prefill oracle (as it is, one thread) on a bounded sample: whole
+    chunks' tokens, a few at a time, all heads, until ~budget_s."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    flops, done = 0, 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s:
+            for s in range(w.num_seqs):
+                a, q_len, ctx = int(w.cu_q_lens[s]), int(w.q_lens[s]), int(w.seq_lens[s])
+                toks = list(range(done % q_len, q_len, max(1, q_len // 8)))[:8]
+                oracle.prefill_attention_seq(w.pool, 0, w.q[a:a + q_len], w.block_tables[s], ctx, w.window,
+                                             w.scale, k_scale=w.k_scale, v_scale=w.v_scale, tokens=toks)
+                for i in toks:
+                    p = ctx - q_len + i
+                    lo = max(0, p + 1 - w.window) if w.window else 0
+                    flops += 4 * w.head_dim * w.num_q_heads * (p - lo + 1)
+                done += len(toks)
+                if time.perf_counter() - t0 > budget_s:
+                    break
+        dt = time.perf_counter() - t0
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done} query tokens (all {w.num_q_heads} heads, eight spread over each chunk per pass; fp64 "
+                  f"numpy, one thread): {done / dt:.1f} tokens/s",
+        "seconds": round(dt, 3),
+    }
+
+
+def bench_prefill(args) -> int:
+    """One step = paged_prefill_step of the whole chunked-prefill batch on
+    one layer slice: the chunks' K/V stored into their slots, then causal
+    attention of every chunk token over its context."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from paged_kv_cache_37_amd import ops
+
+    dev = torch.device("cuda:0")
+    L = args.layers or (8 if args.kv_dtype == "bf16" else 16)
+    log(f"generating the chunked-prefill batch with {L} layer slice(s)")
+    w = W.prefill_config(num_layers=L, dtype=args.kv_dtype, block_size=args.block_size)
+    log(f"generated: {w.name}, {w.num_blocks} blocks/layer")
+    pool_dt = {"bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[w.dtype]
+    pool = ops.KVPool(L, w.num_blocks, w.num_kv_heads, w.head_dim, pool_dt, dev, block_size=w.block_size)
+    if w.dtype == "bf16":
+        pool.load_logical(torch.from_numpy(w.pool.view(np.int16)).view(torch.bfloat16))
+    else:
+        pool.load_logical(torch.from_numpy(w.pool))
+        for layer in range(L):
+            pool.set_fp8_scales(layer, w.k_scale, w.v_scale)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    T = int(w.cu_q_lens[-1])
+    q = up(w.q)
+    rng = np.random.default_rng(7)
+    k_new = up(W.f32_to_bf16_bits(rng.standard_normal((T, w.num_kv_heads, w.head_dim)).astype(np.float32)))
+    v_new = up(W.f32_to_bf16_bits(rng.standard_normal((T, w.num_kv_heads, w.head_dim)).astype(np.float32)))
+    B = w.block_size
+    slots = np.empty(T, np.int32)
+    for s in range(w.num_seqs):
+        ctx, q_len = int(w.seq_lens[s]), int(w.q_lens[s])
+        for i in range(q_len):
+            p = ctx - q_len + i
+            slots[w.cu_q_lens[s] + i] = w.block_tables[s][p // B] * B + p % B
+    slots_t = torch.from_numpy(slots).to(dev)
+    cu = torch.from_numpy(w.cu_q_lens).to(dev)
+    tables = torch.from_numpy(np.ascontiguousarray(w.block_tables)).to(dev)
+    lens = torch.from_numpy(np.ascontiguousarray(w.seq_lens)).to(dev)
+    out = torch.empty_like(q)
+    mq = int(max(w.q_lens))
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        ops.paged_prefill_step(pool, i % L, q, cu, tables, lens, w.scale, mq, k_new, v_new, slots_t, out=out,
+                               stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(K):
+        step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / K
+    # per-call events: the write, then the attention
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for i in range(K):
+        ev[i][0].record(stream)
+        ops.cache_write(pool, i % L, k_new, v_new, slots_t, stream=stream)
+        ev[i][1].record(stream)
+        ops.paged_prefill_attention(pool, i % L, q, cu, tables, lens, w.scale, mq, out=out, stream=stream)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    write_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    attn_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    log(f"step {ms_per_step * 1e3:.1f} us; per call (write {write_ms * 1e3:.1f} us, attention {attn_ms * 1e3:.1f} us)")
+    flops = prefill_flops(w)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    result = {
+        "metric": PREFILL_METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "fp8 KV, bf16 MFMA",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "kv_dtype": w.dtype, "num_seqs": w.num_seqs, "chunk_tokens": T,
+            "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+            "block_size": w.block_size, "prior_tokens": [int(x) for x in w.prior], "layer_slices": L,
+            "seed": w.seed,
+        },
+        "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
+        "attention_us": round(attn_ms * 1e3, 2),
+        "cache_write_us": round(write_ms * 1e3, 2),
+        "flops_per_call": flops,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": traffic_from_profiles(w.name, "prefill"),
+            "kernel": "paged_prefill_attention (prefill_kernel)",
+            "flops_per_call": flops,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline_prefill(w)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
+    ap.add_argument("--mode", default="decode", choices=["decode", "prefill"],
+                    help="decode (the default step) or the chunked-prefill step")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
@@ -169,6 +344,8 @@ def main() -> int:
     if args.copy_probe:
         copy_probe(args.copy_probe)
         return 0
+    if args.mode == "prefill":
+        return bench_prefill(args)
 
     import workloads as W
     from paged_kv_cache_37_amd import ops

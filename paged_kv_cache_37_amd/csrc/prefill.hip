@@ -13,10 +13,11 @@
 // Unlike decode this is a dense contraction: q_len * G query rows of one KV
 // head meet the same keys.  A workgroup takes 128 query rows of one
 // (sequence, KV head) (rows r = token * G + head); its four waves hold 32
-// rows each as two 16-column blocks of the MFMA B operand.  Keys go 32 at a
-// time (two 16-token tiles): the workgroup copies their K and V from the
+// rows each as two 16-column blocks of the MFMA B operand.  Keys go 64 at a
+// time (four 16-token tiles): the workgroup copies their K and V from the
 // pool into LDS once (double-buffered, the next step's loads in flight
-// during this step's compute) and every wave reads its operands there.
+// during this step's compute) and every wave reads its operands there,
+// 32 keys per MFMA round.
 //   S^T = K Q^T   v_mfma_f32_16x16x32_bf16, per 16-key tile, A = K rows
 //   O  += P V     v_mfma_f32_16x16x32_bf16, A = P (the two tiles' S^T
 //                 outputs of a lane are its 8 reduction values), B = V
@@ -30,9 +31,9 @@
 namespace kvp {
 namespace {
 
-constexpr int kPfWaves = 4;
-constexpr int kPfRows = 128;  // query rows per workgroup (32 per wave)
-constexpr int kStep = 32;     // keys per step
+constexpr int kPfRows = 128;         // query rows per workgroup (32 per wave)
+constexpr int kTiles = 4;            // 16-token tiles per step
+constexpr int kStep = 16 * kTiles;   // keys per step (loaded together; computed 32 at a time)
 
 template <bool FP8>
 using Elt = std::conditional_t<FP8, uint8_t, uint16_t>;
@@ -47,15 +48,16 @@ __device__ __forceinline__ uint4_v lds_operand(const Elt<FP8>* p) {
     return *(const uint4_v*)p;
 }
 
+// Wave-wide min / max, returned as a scalar (uniform) value.
 __device__ __forceinline__ int wave_min(int v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
-  return v;
+  return __builtin_amdgcn_readfirstlane(v);
 }
 __device__ __forceinline__ int wave_max(int v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
-  return v;
+  return __builtin_amdgcn_readfirstlane(v);
 }
 
 template <int D, bool FP8, int BS>
@@ -64,9 +66,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
   constexpr int CH = 16 / sizeof(E);           // elements per 16-byte copy
   constexpr int KROW = D + CH;                 // LDS K row: 16 bytes of padding, so 16 rows hit distinct banks
   constexpr int KCH = kStep * D / CH;          // 16-byte chunks of K per step (and of V)
+  static_assert(kTiles % 2 == 0, "steps of whole 32-key rounds");
   constexpr int CPT = (KCH + kThreads - 1) / kThreads;  // chunks per thread
   __shared__ __align__(16) E k_s[2][kStep * KROW];
-  __shared__ __align__(16) E v_s[2][kStep * D];  // two tiles of [4][D][4]
+  __shared__ __align__(16) E v_s[2][kStep * D];  // kTiles tiles of [4][D][4]
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -126,11 +129,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
   // the wave's own key range (its columns' union), for skipping steps
   const int w_lo = wave_min(min(lo_c[0], lo_c[1]));
   const int w_hi = wave_max(max(hi_c[0], hi_c[1]));
+  // keys every column of the wave attends: a round inside [w_in_lo, w_in_hi]
+  // needs no per-column mask (a wave with a column that attends nothing
+  // always masks)
+  const bool all_cols = wave_min((lo_c[0] != INT32_MAX) & (lo_c[1] != INT32_MAX)) != 0;
+  const int w_in_lo = all_cols ? wave_max(max(lo_c[0], lo_c[1])) : INT32_MAX;
+  const int w_in_hi = all_cols ? wave_min(min(hi_c[0], hi_c[1])) : -1;
 
   // Block ids of the tiles 64 at a time (lane i: tile jb + i), the next 64 prefetched.
   const int32_t* row = P.block_tables + (size_t)s * P.max_blocks;
   auto entry = [&](int J) { return J < ntiles ? row[(t0 + J) >> BS] : 0; };
-  int jb = 2 * k_lo;
+  int jb = kTiles * k_lo;
   int ids_a = entry(jb + lane), ids_b = entry(jb + 64 + lane);
 
   const size_t tile = (size_t)B * D;  // one head's K (or V) tile of a block
@@ -141,34 +150,36 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
   // Global -> registers for the step's two tiles (bad or absent tiles read
   // block 0; their keys are masked), registers -> LDS.
   uint4_v kreg[CPT], vreg[CPT];
-  bool bad[2] = {false, false};
+  unsigned bad = 0;  // bit t: tile t of the fetched step holds no keys (past the span, or no block)
   auto fetch = [&](int k) {
-    const int J0 = 2 * k;
+    const int J0 = kTiles * k;
     if (J0 - jb >= 64) {  // rotate the id window (uniform: every wave walks the same steps)
       ids_a = ids_b;
       jb += 64;
       ids_b = entry(jb + 64 + lane);
     }
-    const E* src[2];
+    const E* src[kTiles];
+    bad = 0;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < kTiles; ++t) {
       const int J = J0 + t;
       int id = __builtin_amdgcn_readlane(J - jb < 64 ? ids_a : ids_b, (J - jb) & 63);
-      bad[t] = J >= ntiles || (unsigned)id >= (unsigned)P.num_blocks;
-      if (bad[t]) id = 0;
+      const bool b = J >= ntiles || (unsigned)id >= (unsigned)P.num_blocks;
+      bad |= (b ? 1u : 0u) << t;
+      if (b) id = 0;
       src[t] = pool + (size_t)id * blk_stride + (size_t)((t0 + J) & ((1 << BS) - 1)) * kBlock * D;
     }
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = threadIdx.x + i * kThreads;  // K chunk: key c / (D / CH), column chunk c % (D / CH)
       const int key = c / (D / CH), cc = c - key * (D / CH);
-      if (c < KCH) kreg[i] = *(const uint4_v*)(src[key >> 4] + (key & 15) * D + cc * CH);
+      if (KCH % kThreads == 0 || c < KCH) kreg[i] = *(const uint4_v*)(src[key >> 4] + (key & 15) * D + cc * CH);
     }
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int c = threadIdx.x + i * kThreads;  // V chunk c of the two tiles, tile by tile
+      const int c = threadIdx.x + i * kThreads;  // V chunk c of the step's tiles, tile by tile
       const int t = c / (16 * D / CH), cc = c - t * (16 * D / CH);
-      if (c < KCH) vreg[i] = *(const uint4_v*)(src[t] + v_rel + cc * CH);
+      if (KCH % kThreads == 0 || c < KCH) vreg[i] = *(const uint4_v*)(src[t] + v_rel + cc * CH);
     }
   };
   auto stash = [&](int buf) {
@@ -176,12 +187,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
     for (int i = 0; i < CPT; ++i) {
       const int c = threadIdx.x + i * kThreads;
       const int key = c / (D / CH), cc = c - key * (D / CH);
-      if (c < KCH) *(uint4_v*)(&k_s[buf][key * KROW + cc * CH]) = kreg[i];
+      if (KCH % kThreads == 0 || c < KCH) *(uint4_v*)(&k_s[buf][key * KROW + cc * CH]) = kreg[i];
     }
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = threadIdx.x + i * kThreads;
-      if (c < KCH) *(uint4_v*)(&v_s[buf][c * CH]) = vreg[i];
+      if (KCH % kThreads == 0 || c < KCH) *(uint4_v*)(&v_s[buf][c * CH]) = vreg[i];
     }
   };
 
@@ -192,11 +203,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
 #pragma unroll
     for (int n = 0; n < D / 16; ++n) acc[nb][n] = float4_v{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int k, int buf, bool bad0, bool bad1) {
-    const int u0 = k * kStep;  // span slot of the step's first key
-    if (u0 + kStep - 1 < w_lo || u0 > w_hi) return;  // no column of this wave attends these keys
-    const E* ks = k_s[buf];
-    const E* vs = v_s[buf];
+  // One round of 32 keys (tiles 2h, 2h+1 of the step in LDS buffer buf).
+  auto compute = [&](int k, int h, int buf, bool bad0, bool bad1) {
+    const int u0 = k * kStep + 32 * h;  // span slot of the round's first key
+    if (u0 + 31 < w_lo || u0 > w_hi) return;  // no column of this wave attends these keys
+    const E* ks = k_s[buf] + 32 * h * KROW;
+    const E* vs = v_s[buf] + 32 * h * D;
     // S^T per tile and column block
     float4_v sc[2][2];
 #pragma unroll
@@ -216,30 +228,39 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
     }
     // keys of the step outside the span (or in a bad tile) hold no data:
     // zero their V and mask their scores for every column
-    const bool vedge = bad0 || bad1 || u0 < so || u0 + kStep > send;
-    unsigned vm[2][2];  // [tile][half]: mask words for keys 4q4 + {0,1} and {2,3}
+    // (wave-uniform decisions: the masked paths are branches of the whole wave)
+    const bool vedge = bad0 || bad1 || u0 < so || u0 + 32 > send;
+    const bool cedge = vedge || u0 < w_in_lo || u0 + 31 > w_in_hi;
+    unsigned vm[2][2] = {{~0u, ~0u}, {~0u, ~0u}};  // [tile][half]: keys 4q4 + {0,1} and {2,3} hold data
+    if (vedge) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int u = u0 + t * 16 + 4 * q4 + 2 * h;
-        const bool tb = t ? bad1 : bad0;
-        const bool a = !tb && u >= so && u < send, b = !tb && u + 1 >= so && u + 1 < send;
-        vm[t][h] = (a ? 0xffffu : 0u) | (b ? 0xffff0000u : 0u);
-      }
+        for (int h = 0; h < 2; ++h) {
+          const int u = u0 + t * 16 + 4 * q4 + 2 * h;
+          const bool tb = t ? bad1 : bad0;
+          const bool a = !tb & (u >= so) & (u < send), b = !tb & (u + 1 >= so) & (u + 1 < send);
+          vm[t][h] = (a ? 0xffffu : 0u) | (b ? 0xffff0000u : 0u);
+        }
+    }
     uint4_v pa[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       float sv[2][4];
-      const bool cedge = vedge || u0 < lo_c[nb] || u0 + kStep - 1 > hi_c[nb];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int u = u0 + t * 16 + 4 * q4 + r;
-          const bool keep = !cedge || (((vm[t][r >> 1] >> (16 * (r & 1))) & 1u) && u >= lo_c[nb] && u <= hi_c[nb]);
-          sv[t][r] = keep ? sc[t][nb][r] * P.scale_log2 : -INFINITY;
-        }
+        for (int r = 0; r < 4; ++r) sv[t][r] = sc[t][nb][r] * P.scale_log2;
+      if (cedge) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int u = u0 + t * 16 + 4 * q4 + r;
+            const bool keep = ((vm[t][r >> 1] >> (16 * (r & 1))) & 1u) & (u >= lo_c[nb]) & (u <= hi_c[nb]);
+            sv[t][r] = keep ? sv[t][r] : -INFINITY;
+          }
+      }
       float lmax = -INFINITY;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -292,23 +313,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
 
   if (nsteps > 0) {
     fetch(k_lo);
-    bool bad_c[2] = {bad[0], bad[1]};
+    unsigned bad_c = bad;
     stash(0);
     __syncthreads();
     for (int k = k_lo; k <= k_hi; ++k) {
       const int buf = (k - k_lo) & 1;
       const bool more = k < k_hi;
-      bool bad_n[2] = {false, false};
-      if (more) {
-        fetch(k + 1);
-        bad_n[0] = bad[0];
-        bad_n[1] = bad[1];
-      }
-      compute(k, buf, bad_c[0], bad_c[1]);
+      if (more) fetch(k + 1);
+#pragma unroll
+      for (int h = 0; h < kTiles / 2; ++h) compute(k, h, buf, (bad_c >> (2 * h)) & 1u, (bad_c >> (2 * h + 1)) & 1u);
       if (more) stash(buf ^ 1);
       __syncthreads();
-      bad_c[0] = bad_n[0];
-      bad_c[1] = bad_n[1];
+      bad_c = bad;
     }
   }
 
