@@ -20,9 +20,10 @@
 // 32 keys per MFMA round.
 //   S^T = K Q^T   v_mfma_f32_16x16x32_bf16, per 16-key tile, A = K rows
 //   O  += P V     v_mfma_f32_16x16x32_bf16, A = P (the two tiles' S^T
-//                 outputs of a lane are its 8 reduction values), B = V
-//                 (one quad-interleaved 16-byte read per tile gives two
-//                 dims x four keys; two tiles give the 8 keys of B)
+//                 outputs of a lane are its 8 reduction values), B = V:
+//                 LDS holds a round's V as [quad][dim][tile][4 keys], so
+//                 one 16-byte read gives a dim's four keys of both tiles,
+//                 the 8 keys of B in the order of A
 // with the base-2 online softmax of the decode kernels.  P is rounded to
 // bf16 once (the result stays within the bf16 tolerance; decode's two-term
 // P keeps split-K invariance, which prefill does not need).
@@ -65,11 +66,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
   using E = Elt<FP8>;
   constexpr int CH = 16 / sizeof(E);           // elements per 16-byte copy
   constexpr int KROW = D + CH;                 // LDS K row: 16 bytes of padding, so 16 rows hit distinct banks
-  constexpr int KCH = kStep * D / CH;          // 16-byte chunks of K per step (and of V)
+  constexpr int TCH = 16 * D / CH;             // 16-byte chunks of one tile's K (and of its V)
   static_assert(kTiles % 2 == 0, "steps of whole 32-key rounds");
-  constexpr int CPT = (KCH + kThreads - 1) / kThreads;  // chunks per thread
+  static_assert(TCH <= kThreads, "one chunk per thread and tile");
   __shared__ __align__(16) E k_s[2][kStep * KROW];
-  __shared__ __align__(16) E v_s[2][kStep * D];  // kTiles tiles of [4][D][4]
+  __shared__ __align__(16) E v_s[2][kStep * D];  // per 32-key round: [4 quads][D][2 tiles][4 keys]
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
 
   // Global -> registers for the step's two tiles (bad or absent tiles read
   // block 0; their keys are masked), registers -> LDS.
-  uint4_v kreg[CPT], vreg[CPT];
+  uint4_v kreg[kTiles], vreg[kTiles];  // thread tid's chunk of each tile of the step
   unsigned bad = 0;  // bit t: tile t of the fetched step holds no keys (past the span, or no block)
   auto fetch = [&](int k) {
     const int J0 = kTiles * k;
@@ -158,7 +159,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
       jb += 64;
       ids_b = entry(jb + 64 + lane);
     }
-    const E* src[kTiles];
     bad = 0;
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
@@ -167,32 +167,31 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
       const bool b = J >= ntiles || (unsigned)id >= (unsigned)P.num_blocks;
       bad |= (b ? 1u : 0u) << t;
       if (b) id = 0;
-      src[t] = pool + (size_t)id * blk_stride + (size_t)((t0 + J) & ((1 << BS) - 1)) * kBlock * D;
-    }
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = threadIdx.x + i * kThreads;  // K chunk: key c / (D / CH), column chunk c % (D / CH)
-      const int key = c / (D / CH), cc = c - key * (D / CH);
-      if (KCH % kThreads == 0 || c < KCH) kreg[i] = *(const uint4_v*)(src[key >> 4] + (key & 15) * D + cc * CH);
-    }
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = threadIdx.x + i * kThreads;  // V chunk c of the step's tiles, tile by tile
-      const int t = c / (16 * D / CH), cc = c - t * (16 * D / CH);
-      if (KCH % kThreads == 0 || c < KCH) vreg[i] = *(const uint4_v*)(src[t] + v_rel + cc * CH);
+      // tile t's K rows and V quads: a uniform base, this thread's chunk
+      const E* src = pool + (size_t)id * blk_stride + (size_t)((t0 + J) & ((1 << BS) - 1)) * kBlock * D;
+      if (TCH % kThreads == 0 || threadIdx.x < TCH) {
+        kreg[t] = *(const uint4_v*)(src + threadIdx.x * CH);          // key tid / (D / CH), chunk tid % (D / CH)
+        vreg[t] = *(const uint4_v*)(src + v_rel + threadIdx.x * CH);  // elements 16 tid .. of [4][D][4]
+      }
     }
   };
   auto stash = [&](int buf) {
+    if (TCH % kThreads != 0 && threadIdx.x >= TCH) return;
+    const int key = threadIdx.x / (D / CH), cc = threadIdx.x - key * (D / CH);
+    // this thread's V chunk: CH / 4 dims x 4 keys of quad q
+    const int e0 = threadIdx.x * CH, q = e0 / (4 * D), d = (e0 - q * 4 * D) >> 2;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = threadIdx.x + i * kThreads;
-      const int key = c / (D / CH), cc = c - key * (D / CH);
-      if (KCH % kThreads == 0 || c < KCH) *(uint4_v*)(&k_s[buf][key * KROW + cc * CH]) = kreg[i];
-    }
+    for (int t = 0; t < kTiles; ++t) {
+      *(uint4_v*)(&k_s[buf][(16 * t + key) * KROW + cc * CH]) = kreg[t];
+      // per dim, its 4 keys beside the other tile's of the same 32-key round
+      E* dst = &v_s[buf][(t >> 1) * 32 * D + ((q * D + d) * 2 + (t & 1)) * 4];
+      if constexpr (FP8) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = threadIdx.x + i * kThreads;
-      if (KCH % kThreads == 0 || c < KCH) *(uint4_v*)(&v_s[buf][c * CH]) = vreg[i];
+        for (int j = 0; j < 4; ++j) *(unsigned*)(dst + 8 * j) = vreg[t][j];
+      } else {
+        *(uint2_v*)dst = uint2_v{vreg[t].x, vreg[t].y};
+        *(uint2_v*)(dst + 8) = uint2_v{vreg[t].z, vreg[t].w};
+      }
     }
   };
 
@@ -294,13 +293,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
     // O += P V: B rows 8 q4 .. +7 are keys 4 q4 .. +3 of tile 0, then of tile 1
 #pragma unroll
     for (int m = 0; m < D / 32; ++m) {
-      uint4_v v0 = lds_operand<FP8>(vs + ((q4 * D + 32 * m + 2 * col) * 4));
-      uint4_v v1 = lds_operand<FP8>(vs + 16 * D + ((q4 * D + 32 * m + 2 * col) * 4));
+      uint4_v b0 = lds_operand<FP8>(vs + ((q4 * D + 32 * m + 2 * col) * 2) * 4);
+      uint4_v b1 = lds_operand<FP8>(vs + ((q4 * D + 32 * m + 2 * col + 1) * 2) * 4);
       if (vedge) {
-        v0.x &= vm[0][0]; v0.y &= vm[0][1]; v0.z &= vm[0][0]; v0.w &= vm[0][1];
-        v1.x &= vm[1][0]; v1.y &= vm[1][1]; v1.z &= vm[1][0]; v1.w &= vm[1][1];
+        b0.x &= vm[0][0]; b0.y &= vm[0][1]; b0.z &= vm[1][0]; b0.w &= vm[1][1];
+        b1.x &= vm[0][0]; b1.y &= vm[0][1]; b1.z &= vm[1][0]; b1.w &= vm[1][1];
       }
-      const uint4_v b0 = {v0.x, v0.y, v1.x, v1.y}, b1 = {v0.z, v0.w, v1.z, v1.w};
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         acc[nb][2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, pa[nb]),
