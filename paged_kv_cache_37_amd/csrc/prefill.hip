@@ -181,16 +181,19 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
     // this thread's V chunk: CH / 4 dims x 4 keys of quad q
     const int e0 = threadIdx.x * CH, q = e0 / (4 * D), d = (e0 - q * 4 * D) >> 2;
 #pragma unroll
-    for (int t = 0; t < kTiles; ++t) {
-      *(uint4_v*)(&k_s[buf][(16 * t + key) * KROW + cc * CH]) = kreg[t];
-      // per dim, its 4 keys beside the other tile's of the same 32-key round
-      E* dst = &v_s[buf][(t >> 1) * 32 * D + ((q * D + d) * 2 + (t & 1)) * 4];
+    for (int t = 0; t < kTiles; ++t) *(uint4_v*)(&k_s[buf][(16 * t + key) * KROW + cc * CH]) = kreg[t];
+    // per dim, its 4 keys of tile 2h beside those of tile 2h + 1 (this thread
+    // holds the same quad and dims of both)
+#pragma unroll
+    for (int h = 0; h < kTiles / 2; ++h) {
+      E* dst = &v_s[buf][h * 32 * D + (q * D + d) * 8];
+      const uint4_v a = vreg[2 * h], b = vreg[2 * h + 1];
       if constexpr (FP8) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) *(unsigned*)(dst + 8 * j) = vreg[t][j];
+        for (int j = 0; j < 4; ++j) *(uint2_v*)(dst + 8 * j) = uint2_v{a[j], b[j]};
       } else {
-        *(uint2_v*)dst = uint2_v{vreg[t].x, vreg[t].y};
-        *(uint2_v*)(dst + 8) = uint2_v{vreg[t].z, vreg[t].w};
+        *(uint4_v*)dst = uint4_v{a.x, a.y, b.x, b.y};
+        *(uint4_v*)(dst + 8) = uint4_v{a.z, a.w, b.z, b.w};
       }
     }
   };
