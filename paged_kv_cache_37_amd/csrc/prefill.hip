@@ -74,11 +74,21 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int SK = P.num_seqs * P.num_kv_heads;
-  // heaviest tiles (latest tokens, most keys) first
-  const int qt = P.qtiles - 1 - (int)(blockIdx.x / SK);
-  const int rest = blockIdx.x - (P.qtiles - 1 - qt) * SK;
-  const int s = rest / P.num_kv_heads, kvh = rest - s * P.num_kv_heads;
+  const int SK = P.num_seqs * P.num_kv_heads;  // (sequence, KV head) groups
+  // Heaviest tiles (latest tokens, most keys) first.  Workgroup b runs on
+  // XCD b mod 8: when the groups split evenly, group g goes to XCD g mod 8,
+  // so all query tiles of a group share one L2 (its K/V fetched once) and
+  // every XCD gets one KV head of every sequence.
+  int qt, g;
+  if (SK % 8 == 0) {
+    const int x = blockIdx.x & 7, k = blockIdx.x >> 3, nx = SK >> 3;
+    qt = P.qtiles - 1 - k / nx;
+    g = x + 8 * (k - (k / nx) * nx);
+  } else {
+    qt = P.qtiles - 1 - (int)(blockIdx.x / SK);
+    g = blockIdx.x - (P.qtiles - 1 - qt) * SK;
+  }
+  const int s = g / P.num_kv_heads, kvh = g - s * P.num_kv_heads;
   const int G = P.group;
   const int c0 = P.cu_q_lens[s];
   const int q_len = P.cu_q_lens[s + 1] - c0;
