@@ -269,9 +269,12 @@ int32_t paged_decode_attention(kvp_pool pool, const kvp_decode_args* args, hipSt
  *   of the batch reuses ([Pool] "Finding a prefix again"; [Memory] "How
  *   vLLM recognizes a reusable prefix": only full blocks are shared).  The
  *   STREAM variant then attends the prefix once per KV head for all
- *   sequences (a dense pass whose MFMA columns are 16 query rows of any
- *   sequences), streams only the private tails, and merges the two; the
- *   result is the same attention up to fp32 rounding.  Other variants, and
+ *   sequences (a dense pass: 128 query rows of any sequences per workgroup
+ *   share the prefix's K/V tiles in LDS, and the prefix's keys are split
+ *   into up to 8 chunks, each leaving its own partial result), streams only
+ *   the private tails, and merges the two; the result is the same
+ *   attention up to fp32 rounding (KVP_PREFIX_PIECES=1..8 sets the number
+ *   of chunks, read at each call).  Other variants, and
  *   rows with a sliding window, ignore the hint.  P must be <=
  *   max_blocks_per_seq (KVP_ERR_INVALID_ARG otherwise); if the promise does
  *   not hold the outputs are unspecified (memory is still only read inside

@@ -21,7 +21,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvpool.so")
 
 SOURCES = ["kvpool_api.cpp", "cache_write.hip", "copy_blocks.hip", "decode_mfma.hip", "decode_valu.hip", "decode_reduce.hip",
-           "decode_stream.hip", "decode_prefix.hip", "prefill.hip"]
+           "decode_stream.hip", "prefill.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

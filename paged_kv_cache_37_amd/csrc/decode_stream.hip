@@ -625,17 +625,29 @@ __global__ __launch_bounds__(256) void decode_stream_reduce_kernel(const DecodeP
   // do not depend on the prefix sums: their loads go out with them.
   float rm = -INFINITY, rl = 0.f, ro[PER];
   if (cascade) {
-    const size_t qh = (size_t)s * P.num_q_heads + h;
+    // the prefix pass's pieces (one per key chunk, in chunk order)
+    static_assert(kMaxPrefixPieces <= kMergeChunk, "one merge round takes every prefix piece");
+    const size_t qh = (size_t)s * P.num_q_heads + h, pstride = (size_t)S * P.num_q_heads;
+    float m[kMergeChunk], l[kMergeChunk], v[kMergeChunk][PER];
+#pragma unroll
+    for (int u = 0; u < kMergeChunk; ++u) {
+      const bool use = u < P.prefix_pieces;
+      const size_t pq = qh + (use ? u : 0) * pstride;
+      const float2 ml = *(const float2*)(P.pre_ml + pq * 2);
+      m[u] = use ? ml.x : -INFINITY;
+      l[u] = use ? ml.y : 0.f;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const float x = P.pre_o[pq * D + lane + 64 * e];
+        v[u][e] = use ? x : 0.f;
+      }
+    }
     const size_t rb = ((size_t)hg * S + s) * P.heads_per_wg + hh;
-    M = P.pre_ml[qh * 2];
-    den = P.pre_ml[qh * 2 + 1];
     rm = P.row_ml[rb * 2];
     rl = P.row_ml[rb * 2 + 1];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      num[e] = P.pre_o[qh * D + lane + 64 * e];
-      ro[e] = P.row_o[rb * D + lane + 64 * e];
-    }
+    for (int e = 0; e < PER; ++e) ro[e] = P.row_o[rb * D + lane + 64 * e];
+    merge_round(M, den, num, m, l, v);
   }
   const int pre_s = P.prefix[s], nb = P.prefix[s + 1] - pre_s, per_row = P.prefix[S];
   if (nb == 0 && !cascade) return;
@@ -685,10 +697,36 @@ __global__ __launch_bounds__(256) void decode_stream_reduce_kernel(const DecodeP
   for (int e = 0; e < PER; ++e) out[lane + 64 * e] = bf16_rne(num[e] * inv);
 }
 
+// The shared-prefix pass on the prefill kernel: all S * G decode queries of
+// a KV head against the prefix, key chunk by key chunk.
+hipError_t launch_prefix(const DecodeParams& p, int head_dim, hipStream_t stream) {
+  PrefillParams f{};
+  f.pool_layer = p.pool_layer;
+  f.q = p.q;
+  f.block_tables = p.block_tables;
+  f.max_blocks = p.max_blocks;
+  f.num_seqs = p.num_seqs;
+  f.num_q_heads = p.num_q_heads;
+  f.num_kv_heads = p.num_kv_heads;
+  f.num_blocks = p.num_blocks;
+  f.bshift = p.bshift;
+  f.group = p.group;
+  f.window = 0;
+  f.qtiles = (p.num_seqs * p.group + 127) / 128;
+  f.scale_log2 = p.scale_log2;
+  f.v_scale = p.v_scale;
+  f.prefix_blocks = p.prefix_blocks;
+  f.prefix_pieces = p.prefix_pieces;
+  f.prefix_chunk = p.prefix_chunk;
+  f.pre_o = p.pre_o;
+  f.pre_ml = p.pre_ml;
+  return launch_prefix_pass(f, head_dim, p.kv_fp8 != 0, stream);
+}
+
 template <int D, int DEPTH, bool FP8, int BS>
 hipError_t launch_sd(const DecodeParams& p, hipStream_t stream) {
   if (p.prefix_blocks > 0) {
-    const hipError_t e = launch_decode_prefix(p, D, stream);
+    const hipError_t e = launch_prefix(p, D, stream);
     if (e != hipSuccess) return e;
   }
   if (p.slot_mapping) {

@@ -13,7 +13,7 @@ constexpr int kWaves = 4;       // waves per decode workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxStreamSeqs = 4096;  // sequences one streaming launch can take (LDS prefix sums)
 constexpr int kMaxStreamWaves = 16384;  // waves of a streaming grid (one arrival counter each)
-constexpr int kMaxPrefixBlocks = 4096;  // shared-prefix tiles one prefix pass takes (LDS tile ids)
+constexpr int kMaxPrefixPieces = 8;    // key chunks of the shared-prefix pass
 
 // Geometry and arguments of one decode launch, resolved on the host.
 struct DecodeParams {
@@ -46,8 +46,10 @@ struct DecodeParams {
   const void* v_new;            // [S][Hkv][D]                               (fused write only)
   const int32_t* slot_mapping;  // [S]; NULL: attention only                 (fused write only)
   int32_t prefix_blocks;        // table entries every row shares (cascade); 0: none   (streaming only)
-  float* pre_o;                 // [S][Hq][D] prefix pass: unnormalised output         (cascade only)
-  float* pre_ml;                // [S][Hq][2] prefix pass: (max, sum)                  (cascade only)
+  int32_t prefix_pieces;        // key chunks of the prefix pass (cascade only)
+  int32_t prefix_chunk;         // tiles per chunk, a multiple of 4 (cascade only)
+  float* pre_o;                 // [pieces][S][Hq][D] prefix pass: unnormalised output (cascade only)
+  float* pre_ml;                // [pieces][S][Hq][2] prefix pass: (max, sum)          (cascade only)
   float* row_o;                 // [rows][heads_per_wg][D] tails held whole by a wave  (cascade only)
   float* row_ml;                // [rows][heads_per_wg][2]                             (cascade only)
   int32_t kv_fp8;               // the pool holds E4M3 codes (K scale folded into scale_log2)
@@ -77,6 +79,16 @@ struct PrefillParams {
   int32_t total_q;              // rows of q / out (reads and writes stay inside)
   float scale_log2;             // scale * log2(e) (* k_scale for FP8)
   float v_scale;
+  // The shared-prefix pass of cascade decode runs on the same kernel: every
+  // sequence's decode query against the first prefix_blocks entries of the
+  // table's first row, the prefix's tiles split into prefix_pieces chunks
+  // of prefix_chunk tiles (a multiple of the 4-tile step), each chunk
+  // leaving (max, sum, unnormalised output) per (sequence, query head).
+  int32_t prefix_blocks;
+  int32_t prefix_pieces;
+  int32_t prefix_chunk;
+  float* pre_o;                 // [pieces][S][Hq][D]
+  float* pre_ml;                // [pieces][S][Hq][2]
 };
 
 // Span of one block-table row in 16-token tiles.  The row's first block
@@ -121,8 +133,8 @@ hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int head_dim, hi
 hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeParams& p, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_decode_stream(const DecodeParams& p, int head_dim, hipStream_t stream);
-hipError_t launch_decode_prefix(const DecodeParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, bool fp8, hipStream_t stream);
+hipError_t launch_prefix_pass(const PrefillParams& p, int head_dim, bool fp8, hipStream_t stream);
 // The streaming kernel instance a launch would use (for occupancy queries);
 // nullptr for one that is never launched (the fused step runs at depth 1).
 const void* stream_kernel_symbol(int head_dim, int depth, bool fused, bool fp8, int bshift);

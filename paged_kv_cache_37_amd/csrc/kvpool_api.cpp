@@ -330,9 +330,10 @@ static StreamLayout stream_workspace(const kvp::DecodeParams& p, int32_t head_di
   L.prefix = kSyncBytes;
   L.ml = L.prefix + align256((size_t)(p.num_seqs + 1) * sizeof(int32_t));
   L.o = L.ml + align256(slots * 2 * sizeof(float));
+  const size_t pieces = kvp::kMaxPrefixPieces;
   L.pre_ml = L.o + align256(slots * head_dim * sizeof(float));
-  L.pre_o = L.pre_ml + align256(qh * 2 * sizeof(float));
-  L.row_ml = L.pre_o + align256(qh * head_dim * sizeof(float));
+  L.pre_o = L.pre_ml + align256(pieces * qh * 2 * sizeof(float));
+  L.row_ml = L.pre_o + align256(pieces * qh * head_dim * sizeof(float));
   L.row_o = L.row_ml + align256(rows * 2 * sizeof(float));
   L.total = L.row_o + rows * head_dim * sizeof(float);
   return L;
@@ -399,10 +400,21 @@ static int32_t decode(kvp_pool pool, const kvp_decode_args* a, const void* k_new
   if (a->shared_prefix_blocks < 0 || a->shared_prefix_blocks > a->max_blocks_per_seq)
     return fail(KVP_ERR_INVALID_ARG, "shared_prefix_blocks must be in [0, max_blocks_per_seq]");
   // the shared-prefix pass is a STREAM feature for full-context rows; elsewhere the hint is ignored
-  // (a shorter hint is as valid as the full one: longer prefixes use the blocks of the first
-  // kMaxPrefixBlocks tiles)
-  if (path == PATH_STREAM && a->sliding_window == 0)
-    p.prefix_blocks = std::min(a->shared_prefix_blocks, kvp::kMaxPrefixBlocks >> p.bshift);
+  if (path == PATH_STREAM && a->sliding_window == 0) p.prefix_blocks = a->shared_prefix_blocks;
+  if (p.prefix_blocks > 0) {
+    // split the prefix's keys so that the pass has about as many
+    // workgroups as the streaming grid (two per CU), in chunks of whole
+    // 4-tile steps; KVP_PREFIX_PIECES (1..8) overrides the count
+    const int32_t tiles = p.prefix_blocks << p.bshift;
+    const long long units = (long long)d.num_kv_heads * ((a->num_seqs * p.group + 127) / 128);
+    long long want = (p.stream_wgs + units - 1) / units;
+    const char* ev = getenv("KVP_PREFIX_PIECES");
+    if (ev && atoi(ev) >= 1) want = atoi(ev);
+    want = std::max(1LL, std::min<long long>(want, kvp::kMaxPrefixPieces));
+    const int32_t per = (int32_t)((tiles + want - 1) / want);
+    p.prefix_chunk = (per + 3) / 4 * 4;
+    p.prefix_pieces = (tiles + p.prefix_chunk - 1) / p.prefix_chunk;
+  }
   size_t o_off = 0, ml_off = 0;
   const StreamLayout SL = path == PATH_STREAM ? stream_workspace(p, d.head_dim) : StreamLayout{};
   const size_t ws = path == PATH_STREAM ? SL.total : grid_workspace(p, d.head_dim, &o_off, &ml_off);

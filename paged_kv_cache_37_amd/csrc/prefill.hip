@@ -61,7 +61,10 @@ __device__ __forceinline__ int wave_max(int v) {
   return __builtin_amdgcn_readfirstlane(v);
 }
 
-template <int D, bool FP8, int BS>
+// PREFIX: the shared-prefix pass of cascade decode instead: the rows are
+// the decode queries of all sequences, the keys one chunk of the shared
+// prefix blocks (no causal mask), and a partial result goes out.
+template <int D, bool FP8, int BS, bool PREFIX>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParams P) {
   using E = Elt<FP8>;
   constexpr int CH = 16 / sizeof(E);           // elements per 16-byte copy
@@ -74,68 +77,120 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int SK = P.num_seqs * P.num_kv_heads;  // (sequence, KV head) groups
-  // Heaviest tiles (latest tokens, most keys) first.  Workgroup b runs on
-  // XCD b mod 8: when the groups split evenly, group g goes to XCD g mod 8,
-  // so all query tiles of a group share one L2 (its K/V fetched once) and
-  // every XCD gets one KV head of every sequence.
-  int qt, g;
-  if (SK % 8 == 0) {
-    const int x = blockIdx.x & 7, k = blockIdx.x >> 3, nx = SK >> 3;
-    qt = P.qtiles - 1 - k / nx;
-    g = x + 8 * (k - (k / nx) * nx);
-  } else {
-    qt = P.qtiles - 1 - (int)(blockIdx.x / SK);
-    g = blockIdx.x - (P.qtiles - 1 - qt) * SK;
-  }
-  const int s = g / P.num_kv_heads, kvh = g - s * P.num_kv_heads;
   const int G = P.group;
-  const int c0 = P.cu_q_lens[s];
-  const int q_len = P.cu_q_lens[s + 1] - c0;
-  const int ctx = P.seq_lens[s];
-  // rows computed: the chunk's, up to max_q_len tokens and inside q / out
-  const int rows = max(0, min(min(q_len, P.max_q_len), P.total_q - c0)) * G;
-  const int r_wg = qt * kPfRows;
-  if (r_wg >= rows || c0 < 0) return;  // the whole workgroup: before any barrier
-
-  // Positions: token i at p = ctx - q_len + i.  The table row starts at the
-  // block holding `first`, the first key any query of the chunk attends;
-  // span slot u is position first - so + u.
   const int B = kBlock << BS;
-  const int p0 = ctx - q_len;
-  const int first = P.window > 0 ? max(0, p0 + 1 - P.window) : 0;
-  const int off = first & (B - 1);
-  const int t0 = off >> 4, so = off & (kBlock - 1);
-  const int base = first - so;                   // position of span slot 0
-  // span slots holding keys: [so, send); a row longer than its table
-  // attends what the table holds
-  const int send = min(so + max(ctx - first, 0), P.max_blocks * B - kBlock * t0);
-  const int ntiles = (send + kBlock - 1) / kBlock;
-  auto lo_of = [&](int p) { return P.window > 0 ? max(0, p + 1 - P.window) : 0; };
-
-  // The workgroup's key range (rows are in position order).
-  const int r_last = min(r_wg + kPfRows, rows) - 1;
-  const int pa = max(p0 + r_wg / G, 0), pb = p0 + r_last / G;
-  const int u_lo = lo_of(pa) - base, u_hi = pb - base;  // span slots some row attends
-  const int k_lo = max(u_lo, 0) / kStep, k_hi = u_hi / kStep;
-  const int nsteps = pb >= 0 ? k_hi - k_lo + 1 : 0;
-
-  // This lane's query column in each of the wave's two blocks.
   const int q4 = lane >> 4, col = lane & 15;
+  // Per workgroup: the table row and span of the keys, the steps, the KV
+  // head; per lane: this column's query in each of the wave's two blocks
+  // and the span slots it attends.
+  const int32_t* row;
+  int kvh, t0, so, send, ntiles, k_lo, k_hi;
   uint4_v qop[2][D / 32];
   int lo_c[2], hi_c[2];
-  int hrow[2];  // query row of the column, -1 past the chunk
-  for (int nb = 0; nb < 2; ++nb) {
-    const int r = r_wg + wave * 32 + nb * 16 + col;
-    const int i = r / G, g = r - (r / G) * G;
-    const int p = p0 + i;
-    const bool ok = r < rows && p >= 0;  // a row without a position (chunk longer than its context) stores zeros
-    hrow[nb] = r < rows ? r : -1;
-    lo_c[nb] = ok ? lo_of(p) - base : INT32_MAX;
-    hi_c[nb] = ok ? p - base : -1;
-    const uint16_t* qp = (const uint16_t*)P.q + ((size_t)(c0 + i) * P.num_q_heads + kvh * G + g) * D + 8 * q4;
+  int hrow[2];  // query row of the column, -1 past the rows
+  int s = 0, c0 = 0, kc = 0;
+  if constexpr (PREFIX) {
+    // rows r = s * G + g of one KV head, 128 per workgroup, against key
+    // chunk kc; every workgroup of KV head h on XCD h mod 8 (the head's
+    // prefix fetched into one L2)
+    const int rows = P.num_seqs * G;
+    const int per_head = P.qtiles * P.prefix_pieces;
+    int rest;
+    if (P.num_kv_heads % 8 == 0) {
+      const int x = blockIdx.x & 7, k = blockIdx.x >> 3, nx = P.num_kv_heads >> 3;
+      rest = k / nx;
+      kvh = x + 8 * (k - rest * nx);
+    } else {
+      kvh = blockIdx.x / per_head;
+      rest = blockIdx.x - kvh * per_head;
+    }
+    kc = rest / P.qtiles;
+    const int qt = rest - kc * P.qtiles;
+    const int r_wg = qt * kPfRows;
+    if (r_wg >= rows) return;  // the whole workgroup: before any barrier
+    // every prefix block is full and attended by every row; the chunk's
+    // tiles [j0, ntiles) start on a step
+    row = P.block_tables;
+    // 0: the shared prefix starts at position 0 (read from the parameters,
+    // which hold 0 here: folded as constants they made the compiler spill)
+    t0 = P.window;
+    so = P.window;
+    const int j0 = kc * P.prefix_chunk;
+    ntiles = min(j0 + P.prefix_chunk, P.prefix_blocks << BS);
+    send = ntiles * kBlock;
+    k_lo = j0 / kTiles;
+    k_hi = (send - 1) / kStep;
+    for (int nb = 0; nb < 2; ++nb) {
+      const int r = r_wg + wave * 32 + nb * 16 + col;
+      const bool ok = r < rows;
+      const int sq = r / G, g = r - sq * G;
+      hrow[nb] = ok ? r : -1;
+      lo_c[nb] = ok ? 0 : INT32_MAX;
+      hi_c[nb] = ok ? send - 1 : -1;
+      const uint16_t* qp = (const uint16_t*)P.q + ((size_t)sq * P.num_q_heads + kvh * G + g) * D + 8 * q4;
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) qop[nb][kk] = ok ? *(const uint4_v*)(qp + 32 * kk) : uint4_v{0, 0, 0, 0};
+      for (int kk = 0; kk < D / 32; ++kk) qop[nb][kk] = ok ? *(const uint4_v*)(qp + 32 * kk) : uint4_v{0, 0, 0, 0};
+    }
+  } else {
+    const int SK = P.num_seqs * P.num_kv_heads;  // (sequence, KV head) groups
+    // Heaviest tiles (latest tokens, most keys) first.  Workgroup b runs on
+    // XCD b mod 8: when the groups split evenly, group g goes to XCD g mod 8,
+    // so all query tiles of a group share one L2 (its K/V fetched once) and
+    // every XCD gets one KV head of every sequence.
+    int qt, grp;
+    if (SK % 8 == 0) {
+      const int x = blockIdx.x & 7, k = blockIdx.x >> 3, nx = SK >> 3;
+      qt = P.qtiles - 1 - k / nx;
+      grp = x + 8 * (k - (k / nx) * nx);
+    } else {
+      qt = P.qtiles - 1 - (int)(blockIdx.x / SK);
+      grp = blockIdx.x - (P.qtiles - 1 - qt) * SK;
+    }
+    s = grp / P.num_kv_heads;
+    kvh = grp - s * P.num_kv_heads;
+    c0 = P.cu_q_lens[s];
+    const int q_len = P.cu_q_lens[s + 1] - c0;
+    const int ctx = P.seq_lens[s];
+    // rows computed: the chunk's, up to max_q_len tokens and inside q / out
+    const int rows = max(0, min(min(q_len, P.max_q_len), P.total_q - c0)) * G;
+    const int r_wg = qt * kPfRows;
+    if (r_wg >= rows || c0 < 0) return;  // the whole workgroup: before any barrier
+
+    // Positions: token i at p = ctx - q_len + i.  The table row starts at the
+    // block holding `first`, the first key any query of the chunk attends;
+    // span slot u is position first - so + u.
+    const int p0 = ctx - q_len;
+    const int first = P.window > 0 ? max(0, p0 + 1 - P.window) : 0;
+    const int off = first & (B - 1);
+    t0 = off >> 4;
+    so = off & (kBlock - 1);
+    const int base = first - so;                   // position of span slot 0
+    // span slots holding keys: [so, send); a row longer than its table
+    // attends what the table holds
+    send = min(so + max(ctx - first, 0), P.max_blocks * B - kBlock * t0);
+    ntiles = (send + kBlock - 1) / kBlock;
+    row = P.block_tables + (size_t)s * P.max_blocks;
+    auto lo_of = [&](int p) { return P.window > 0 ? max(0, p + 1 - P.window) : 0; };
+
+    // The workgroup's key range (rows are in position order).
+    const int r_last = min(r_wg + kPfRows, rows) - 1;
+    const int pa = max(p0 + r_wg / G, 0), pb = p0 + r_last / G;
+    const int u_lo = lo_of(pa) - base, u_hi = pb - base;  // span slots some row attends
+    k_lo = max(u_lo, 0) / kStep;
+    k_hi = pb >= 0 ? u_hi / kStep : k_lo - 1;  // no steps when no row has a position
+
+    for (int nb = 0; nb < 2; ++nb) {
+      const int r = r_wg + wave * 32 + nb * 16 + col;
+      const int i = r / G, g = r - (r / G) * G;
+      const int p = p0 + i;
+      const bool ok = r < rows && p >= 0;  // a row without a position (chunk longer than its context) stores zeros
+      hrow[nb] = r < rows ? r : -1;
+      lo_c[nb] = ok ? lo_of(p) - base : INT32_MAX;
+      hi_c[nb] = ok ? p - base : -1;
+      const uint16_t* qp = (const uint16_t*)P.q + ((size_t)(c0 + i) * P.num_q_heads + kvh * G + g) * D + 8 * q4;
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) qop[nb][kk] = ok ? *(const uint4_v*)(qp + 32 * kk) : uint4_v{0, 0, 0, 0};
+    }
   }
   // the wave's own key range (its columns' union), for skipping steps
   const int w_lo = wave_min(min(lo_c[0], lo_c[1]));
@@ -148,7 +203,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
   const int w_in_hi = all_cols ? wave_min(min(hi_c[0], hi_c[1])) : -1;
 
   // Block ids of the tiles 64 at a time (lane i: tile jb + i), the next 64 prefetched.
-  const int32_t* row = P.block_tables + (size_t)s * P.max_blocks;
   auto entry = [&](int J) { return J < ntiles ? row[(t0 + J) >> BS] : 0; };
   int jb = kTiles * k_lo;
   int ids_a = entry(jb + lane), ids_b = entry(jb + 64 + lane);
@@ -255,7 +309,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
           vm[t][h] = (a ? 0xffffu : 0u) | (b ? 0xffff0000u : 0u);
         }
     }
-    uint4_v pa[2];
+    uint4_v pa[2], pl[2];  // P as bf16, and (shared-prefix pass) the bf16 rest P - pa
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       float sv[2][4];
@@ -302,6 +356,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
         }
       pa[nb] = uint4_v{pack_bf16x2(pr[0][0], pr[0][1]), pack_bf16x2(pr[0][2], pr[0][3]),
                        pack_bf16x2(pr[1][0], pr[1][1]), pack_bf16x2(pr[1][2], pr[1][3])};
+      if constexpr (PREFIX) {
+        // the decode kernels carry P as two bf16 terms; the cascade's prefix
+        // pieces keep their precision, so cascade and plain decode agree
+        pl[nb] = uint4_v{pack_bf16x2(pr[0][0] - bf16_lo(pa[nb].x), pr[0][1] - bf16_hi(pa[nb].x)),
+                         pack_bf16x2(pr[0][2] - bf16_lo(pa[nb].y), pr[0][3] - bf16_hi(pa[nb].y)),
+                         pack_bf16x2(pr[1][0] - bf16_lo(pa[nb].z), pr[1][1] - bf16_hi(pa[nb].z)),
+                         pack_bf16x2(pr[1][2] - bf16_lo(pa[nb].w), pr[1][3] - bf16_hi(pa[nb].w))};
+      }
     }
     // O += P V: B rows 8 q4 .. +7 are keys 4 q4 .. +3 of tile 0, then of tile 1
 #pragma unroll
@@ -318,11 +380,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
                                                                  __builtin_bit_cast(bf16x8_v, b0), acc[nb][2 * m], 0, 0, 0);
         acc[nb][2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             __builtin_bit_cast(bf16x8_v, pa[nb]), __builtin_bit_cast(bf16x8_v, b1), acc[nb][2 * m + 1], 0, 0, 0);
+        if constexpr (PREFIX) {
+          acc[nb][2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_v, pl[nb]), __builtin_bit_cast(bf16x8_v, b0), acc[nb][2 * m], 0, 0, 0);
+          acc[nb][2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_v, pl[nb]), __builtin_bit_cast(bf16x8_v, b1), acc[nb][2 * m + 1], 0, 0, 0);
+        }
       }
     }
   };
 
-  if (nsteps > 0) {
+  if (k_hi >= k_lo) {
     fetch(k_lo);
     unsigned bad_c = bad;
     stash(0);
@@ -339,7 +407,33 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
     }
   }
 
-  // normalise and store: output row 4 q4 + r of block nb is column 4 q4 + r
+  // output row 4 q4 + r of block nb is column 4 q4 + r
+  if constexpr (PREFIX) {
+    // (max, sum, unnormalised output) of query (s, h) over chunk kc, for
+    // the merge with the other chunks and the tails
+    const size_t piece = (size_t)kc * P.num_seqs * P.num_q_heads;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const float l_tot = rows_sum(l_run[nb]);
+      if (lane < 16 && hrow[nb] >= 0) {
+        const int sq = hrow[nb] / G, g = hrow[nb] - sq * G;
+        const size_t qh = piece + (size_t)sq * P.num_q_heads + kvh * G + g;
+        *(float2*)(P.pre_ml + qh * 2) = make_float2(m_run[nb], l_tot);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int hr = __shfl(hrow[nb], 4 * q4 + r);
+        if (hr >= 0) {
+          const int sq = hr / G, g = hr - sq * G;
+          float2* o = (float2*)(P.pre_o + (piece + (size_t)sq * P.num_q_heads + kvh * G + g) * D);
+#pragma unroll
+          for (int m = 0; m < D / 32; ++m) o[16 * m + col] = make_float2(acc[nb][2 * m][r], acc[nb][2 * m + 1][r]);
+        }
+      }
+    }
+    return;
+  }
+  // normalise and store
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const float l_tot = rows_sum(l_run[nb]);
@@ -360,24 +454,33 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
   }
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, bool PREFIX>
 hipError_t launch_pf(const PrefillParams& p, unsigned grid, hipStream_t stream) {
   if (p.bshift)
-    hipLaunchKernelGGL((prefill_kernel<D, FP8, 1>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((prefill_kernel<D, FP8, 1, PREFIX>), dim3(grid), dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, FP8, 0>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((prefill_kernel<D, FP8, 0, PREFIX>), dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
+}
+
+template <bool PREFIX>
+hipError_t launch_any(const PrefillParams& p, long long grid, int head_dim, bool fp8, hipStream_t stream) {
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  const unsigned g = (unsigned)grid;
+  if (head_dim == 128) return fp8 ? launch_pf<128, true, PREFIX>(p, g, stream) : launch_pf<128, false, PREFIX>(p, g, stream);
+  if (head_dim == 64) return fp8 ? launch_pf<64, true, PREFIX>(p, g, stream) : launch_pf<64, false, PREFIX>(p, g, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, bool fp8, hipStream_t stream) {
-  const long long grid = (long long)p.num_seqs * p.num_kv_heads * p.qtiles;
-  if (grid <= 0) return hipSuccess;
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  if (head_dim == 128) return fp8 ? launch_pf<128, true>(p, (unsigned)grid, stream) : launch_pf<128, false>(p, (unsigned)grid, stream);
-  if (head_dim == 64) return fp8 ? launch_pf<64, true>(p, (unsigned)grid, stream) : launch_pf<64, false>(p, (unsigned)grid, stream);
-  return hipErrorInvalidValue;
+  return launch_any<false>(p, (long long)p.num_seqs * p.num_kv_heads * p.qtiles, head_dim, fp8, stream);
+}
+
+hipError_t launch_prefix_pass(const PrefillParams& p, int head_dim, bool fp8, hipStream_t stream) {
+  return launch_any<true>(p, (long long)p.num_kv_heads * p.qtiles * p.prefix_pieces, head_dim, fp8, stream);
 }
 
 }  // namespace kvp
