@@ -21,9 +21,12 @@
 //   S^T = K Q^T   v_mfma_f32_16x16x32_bf16, per 16-key tile, A = K rows
 //   O  += P V     v_mfma_f32_16x16x32_bf16, A = P (the two tiles' S^T
 //                 outputs of a lane are its 8 reduction values), B = V:
-//                 LDS holds a round's V as [quad][dim][tile][4 keys], so
+//                 LDS holds a round's V as [quad][dim'][tile][4 keys], so
 //                 one 16-byte read gives a dim's four keys of both tiles,
-//                 the 8 keys of B in the order of A
+//                 the 8 keys of B in the order of A; within each 32-dim
+//                 group dim' puts the even dims first, then the odd ones,
+//                 so the 16 lanes reading dims 2 col (or 2 col + 1) read
+//                 16 consecutive 16-byte rows (no LDS bank conflicts)
 // with the base-2 online softmax of the decode kernels.  P is rounded to
 // bf16 once (the result stays within the bf16 tolerance; decode's two-term
 // P keeps split-K invariance, which prefill does not need).
@@ -247,17 +250,21 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) *(uint4_v*)(&k_s[buf][(16 * t + key) * KROW + cc * CH]) = kreg[t];
     // per dim, its 4 keys of tile 2h beside those of tile 2h + 1 (this thread
-    // holds the same quad and dims of both)
+    // holds the same quad and dims of both); even dim d of its 32-dim group
+    // at row (d mod 32) / 2 of the group, odd dim d + 1 at row 16 + that
+    const int d_even = (d & ~31) + ((d & 31) >> 1);
 #pragma unroll
     for (int h = 0; h < kTiles / 2; ++h) {
-      E* dst = &v_s[buf][h * 32 * D + (q * D + d) * 8];
+      E* dst_e = &v_s[buf][h * 32 * D + (q * D + d_even) * 8];
+      E* dst_o = dst_e + 16 * 8;
       const uint4_v a = vreg[2 * h], b = vreg[2 * h + 1];
       if constexpr (FP8) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) *(uint2_v*)(dst + 8 * j) = uint2_v{a[j], b[j]};
+        // dims d .. d + 3: d and d + 2 in adjacent even rows, d + 1 and d + 3 in odd rows
+        *(uint4_v*)dst_e = uint4_v{a[0], b[0], a[2], b[2]};
+        *(uint4_v*)dst_o = uint4_v{a[1], b[1], a[3], b[3]};
       } else {
-        *(uint4_v*)dst = uint4_v{a.x, a.y, b.x, b.y};
-        *(uint4_v*)(dst + 8) = uint4_v{a.z, a.w, b.z, b.w};
+        *(uint4_v*)dst_e = uint4_v{a.x, a.y, b.x, b.y};
+        *(uint4_v*)dst_o = uint4_v{a.z, a.w, b.z, b.w};
       }
     }
   };
@@ -368,8 +375,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
     // O += P V: B rows 8 q4 .. +7 are keys 4 q4 .. +3 of tile 0, then of tile 1
 #pragma unroll
     for (int m = 0; m < D / 32; ++m) {
-      uint4_v b0 = lds_operand<FP8>(vs + ((q4 * D + 32 * m + 2 * col) * 2) * 4);
-      uint4_v b1 = lds_operand<FP8>(vs + ((q4 * D + 32 * m + 2 * col + 1) * 2) * 4);
+      uint4_v b0 = lds_operand<FP8>(vs + (q4 * D + 32 * m + col) * 8);       // dim 32 m + 2 col
+      uint4_v b1 = lds_operand<FP8>(vs + (q4 * D + 32 * m + 16 + col) * 8);  // dim 32 m + 2 col + 1
       if (vedge) {
         b0.x &= vm[0][0]; b0.y &= vm[0][1]; b0.z &= vm[1][0]; b0.w &= vm[1][1];
         b1.x &= vm[0][0]; b1.y &= vm[0][1]; b1.z &= vm[1][0]; b1.w &= vm[1][1];
