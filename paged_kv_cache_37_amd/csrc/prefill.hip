@@ -133,6 +133,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
       const uint16_t* qp = (const uint16_t*)P.q + ((size_t)sq * P.num_q_heads + kvh * G + g) * D + 8 * q4;
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) qop[nb][kk] = ok ? *(const uint4_v*)(qp + 32 * kk) : uint4_v{0, 0, 0, 0};
+      if (P.scale_log2 < 0.f) {  // c |scale| (-q) = scale q
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) qop[nb][kk] ^= 0x80008000u;
+      }
     }
   } else {
     const int SK = P.num_seqs * P.num_kv_heads;  // (sequence, KV head) groups
@@ -193,6 +197,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
       const uint16_t* qp = (const uint16_t*)P.q + ((size_t)(c0 + i) * P.num_q_heads + kvh * G + g) * D + 8 * q4;
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) qop[nb][kk] = ok ? *(const uint4_v*)(qp + 32 * kk) : uint4_v{0, 0, 0, 0};
+      if (P.scale_log2 < 0.f) {  // c |scale| (-q) = scale q
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) qop[nb][kk] ^= 0x80008000u;
+      }
     }
   }
   // the wave's own key range (its columns' union), for skipping steps
@@ -269,17 +277,27 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
     }
   };
 
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  // Scores in base 2 are c * (K . q) with c > 0: a negative scale was folded
+  // into the queries' signs (exact in bf16); scale 0 becomes a vanishing c,
+  // which gives the same uniform weights.
+  const float c = fmaxf(fabsf(P.scale_log2), 1e-30f);
+  float m_run[2] = {-INFINITY, -INFINITY};
   float4_v acc[2][D / 16];
+  float4_v acc_l[2];  // [nb][r]: weight sum of output row 4 q4 + r (an MFMA of P with a ones operand)
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
+  for (int nb = 0; nb < 2; ++nb) {
+    acc_l[nb] = float4_v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int n = 0; n < D / 16; ++n) acc[nb][n] = float4_v{0.f, 0.f, 0.f, 0.f};
+  }
+  const bf16x8_v ones = __builtin_bit_cast(bf16x8_v, uint4_v{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
 
   // One round of 32 keys (tiles 2h, 2h+1 of the step in LDS buffer buf).
-  auto compute = [&](int k, int h, int buf, bool bad0, bool bad1) {
-    const int u0 = k * kStep + 32 * h;  // span slot of the round's first key
-    if (u0 + 31 < w_lo || u0 > w_hi) return;  // no column of this wave attends these keys
+  // EDGE rounds hold keys outside the span, in a bad tile, or outside some
+  // column's range: they mask; the others run without a branch except the
+  // (rare) rescale, so the compiler can interleave softmax and MFMAs.
+  auto round = [&](auto edge, int u0, int buf, int h, bool vedge, bool bad0, bool bad1) {
+    constexpr bool EDGE = decltype(edge)::value;
     const E* ks = k_s[buf] + 32 * h * KROW;
     const E* vs = v_s[buf] + 32 * h * D;
     // S^T per tile and column block
@@ -301,66 +319,67 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
     }
     // keys of the step outside the span (or in a bad tile) hold no data:
     // zero their V and mask their scores for every column
-    // (wave-uniform decisions: the masked paths are branches of the whole wave)
-    const bool vedge = bad0 || bad1 || u0 < so || u0 + 32 > send;
-    const bool cedge = vedge || u0 < w_in_lo || u0 + 31 > w_in_hi;
     unsigned vm[2][2] = {{~0u, ~0u}, {~0u, ~0u}};  // [tile][half]: keys 4q4 + {0,1} and {2,3} hold data
-    if (vedge) {
+    if constexpr (EDGE) {
+      if (vedge) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int u = u0 + t * 16 + 4 * q4 + 2 * h;
-          const bool tb = t ? bad1 : bad0;
-          const bool a = !tb & (u >= so) & (u < send), b = !tb & (u + 1 >= so) & (u + 1 < send);
-          vm[t][h] = (a ? 0xffffu : 0u) | (b ? 0xffff0000u : 0u);
-        }
-    }
-    uint4_v pa[2], pl[2];  // P as bf16, and (shared-prefix pass) the bf16 rest P - pa
+          for (int hh = 0; hh < 2; ++hh) {
+            const int u = u0 + t * 16 + 4 * q4 + 2 * hh;
+            const bool tb = t ? bad1 : bad0;
+            const bool a = !tb & (u >= so) & (u < send), b = !tb & (u + 1 >= so) & (u + 1 < send);
+            vm[t][hh] = (a ? 0xffffu : 0u) | (b ? 0xffff0000u : 0u);
+          }
+      }
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      float sv[2][4];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sv[t][r] = sc[t][nb][r] * P.scale_log2;
-      if (cedge) {
+      for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int u = u0 + t * 16 + 4 * q4 + r;
             const bool keep = ((vm[t][r >> 1] >> (16 * (r & 1))) & 1u) & (u >= lo_c[nb]) & (u <= hi_c[nb]);
-            sv[t][r] = keep ? sv[t][r] : -INFINITY;
+            sc[t][nb][r] = keep ? sc[t][nb][r] : -INFINITY;
           }
-      }
+    }
+    // running max: raised (for both column blocks) only when a score passes
+    // it by more than the slack; max(c s) = c max(s) as c > 0
+    float mc[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
       float lmax = -INFINITY;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) lmax = fmaxf(lmax, sv[t][r]);
-      if (__any(lmax > m_run[nb] + kRescaleSlack)) {
-        const float m_new = fmaxf(m_run[nb], rows_max(lmax));
+        for (int r = 0; r < 4; ++r) lmax = fmaxf(lmax, sc[t][nb][r]);
+      mc[nb] = lmax * c;
+    }
+    if (__any((mc[0] > m_run[0] + kRescaleSlack) | (mc[1] > m_run[1] + kRescaleSlack))) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const float m_new = fmaxf(m_run[nb], rows_max(mc[nb]));
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
         const float alpha = __builtin_amdgcn_exp2f(m_run[nb] - m_use);
         m_run[nb] = m_new;
-        l_run[nb] *= alpha;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float ar = __shfl(alpha, 4 * q4 + r);  // output rows here are columns 4 q4 + r
+          acc_l[nb][r] *= ar;
 #pragma unroll
           for (int n = 0; n < D / 16; ++n) acc[nb][n][r] *= ar;
         }
       }
-      const float m_use = m_run[nb] == -INFINITY ? 0.f : m_run[nb];
+    }
+    uint4_v pa[2], pl[2];  // P as bf16, and (shared-prefix pass) the bf16 rest P - pa
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const float neg_m = m_run[nb] == -INFINITY ? 0.f : -m_run[nb];
       float pr[2][4];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pr[t][r] = __builtin_amdgcn_exp2f(sv[t][r] - m_use);
-          l_run[nb] += pr[t][r];
-        }
+        for (int r = 0; r < 4; ++r) pr[t][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][nb][r], c, neg_m));
       pa[nb] = uint4_v{pack_bf16x2(pr[0][0], pr[0][1]), pack_bf16x2(pr[0][2], pr[0][3]),
                        pack_bf16x2(pr[1][0], pr[1][1]), pack_bf16x2(pr[1][2], pr[1][3])};
       if constexpr (PREFIX) {
@@ -377,9 +396,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
     for (int m = 0; m < D / 32; ++m) {
       uint4_v b0 = lds_operand<FP8>(vs + (q4 * D + 32 * m + col) * 8);       // dim 32 m + 2 col
       uint4_v b1 = lds_operand<FP8>(vs + (q4 * D + 32 * m + 16 + col) * 8);  // dim 32 m + 2 col + 1
-      if (vedge) {
-        b0.x &= vm[0][0]; b0.y &= vm[0][1]; b0.z &= vm[1][0]; b0.w &= vm[1][1];
-        b1.x &= vm[0][0]; b1.y &= vm[0][1]; b1.z &= vm[1][0]; b1.w &= vm[1][1];
+      if constexpr (EDGE) {
+        if (vedge) {
+          b0.x &= vm[0][0]; b0.y &= vm[0][1]; b0.z &= vm[1][0]; b0.w &= vm[1][1];
+          b1.x &= vm[0][0]; b1.y &= vm[0][1]; b1.z &= vm[1][0]; b1.w &= vm[1][1];
+        }
       }
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
@@ -395,23 +416,65 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
         }
       }
     }
+    // row sums of the same rounded weights the outputs use
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      acc_l[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, pa[nb]), ones, acc_l[nb], 0, 0, 0);
+      if constexpr (PREFIX)
+        acc_l[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, pl[nb]), ones, acc_l[nb], 0, 0, 0);
+    }
   };
 
-  if (k_hi >= k_lo) {
-    fetch(k_lo);
-    unsigned bad_c = bad;
-    stash(0);
-    __syncthreads();
-    for (int k = k_lo; k <= k_hi; ++k) {
+  // Steps k .. k_end in one form (EDGE: every round masks what it must and
+  // skips what no column of the wave attends), each with the next step's
+  // loads in flight; the unmasked form stops at a step holding a bad tile.
+  // Every wave runs every step once whatever its split into these loops,
+  // so the workgroup's barriers match.
+  unsigned bad_c = 0;
+  auto steps = [&](auto edge, int k, int k_end) {
+    constexpr bool EDGE = decltype(edge)::value;
+    for (; k <= k_end; ++k) {
+      if constexpr (!EDGE) {
+        if (bad_c) break;
+      }
       const int buf = (k - k_lo) & 1;
       const bool more = k < k_hi;
       if (more) fetch(k + 1);
 #pragma unroll
-      for (int h = 0; h < kTiles / 2; ++h) compute(k, h, buf, (bad_c >> (2 * h)) & 1u, (bad_c >> (2 * h + 1)) & 1u);
+      for (int h = 0; h < kTiles / 2; ++h) {
+        const int u0 = k * kStep + 32 * h;  // span slot of the round's first key
+        if constexpr (EDGE) {
+          if (u0 + 31 < w_lo || u0 > w_hi) continue;  // no column of this wave attends these keys
+          const bool bad0 = (bad_c >> (2 * h)) & 1u, bad1 = (bad_c >> (2 * h + 1)) & 1u;
+          round(edge, u0, buf, h, bad0 || bad1 || u0 < so || u0 + 32 > send, bad0, bad1);
+        } else {
+          round(edge, u0, buf, h, false, false, false);
+        }
+      }
       if (more) stash(buf ^ 1);
       __syncthreads();
       bad_c = bad;
     }
+    return k;
+  };
+
+  if (k_hi >= k_lo) {
+    fetch(k_lo);
+    bad_c = bad;
+    stash(0);
+    __syncthreads();
+    // interior steps: every key in the span and every column of the wave
+    // attending all of them (w_in_lo = INT32_MAX when a column attends none)
+    const int in_lo = max(so, w_in_lo), in_hi = min(send - 1, w_in_hi);
+    int k_a = in_lo == INT32_MAX ? k_hi + 1 : max(k_lo, (in_lo + kStep - 1) / kStep);
+    int k_b = in_hi < 0 ? k_lo - 1 : min(k_hi, (in_hi + 1) / kStep - 1);
+    if (k_a > k_b) {
+      k_a = k_hi + 1;
+      k_b = k_hi;
+    }
+    int k = steps(std::true_type{}, k_lo, k_a - 1);
+    k = steps(std::false_type{}, k, k_b);
+    steps(std::true_type{}, k, k_hi);
   }
 
   // output row 4 q4 + r of block nb is column 4 q4 + r
@@ -421,7 +484,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
     const size_t piece = (size_t)kc * P.num_seqs * P.num_q_heads;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const float l_tot = rows_sum(l_run[nb]);
+      // the sum of column col lives in register col % 4 of the lanes with q4 = col / 4
+      const int j = lane & 3;
+      const float lsel = j == 0 ? acc_l[nb][0] : j == 1 ? acc_l[nb][1] : j == 2 ? acc_l[nb][2] : acc_l[nb][3];
+      const float l_tot = __shfl(lsel, 16 * (col >> 2) + (col & 3));
       if (lane < 16 && hrow[nb] >= 0) {
         const int sq = hrow[nb] / G, g = hrow[nb] - sq * G;
         const size_t qh = piece + (size_t)sq * P.num_q_heads + kvh * G + g;
@@ -443,11 +509,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
   // normalise and store
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    const float l_tot = rows_sum(l_run[nb]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int g = 4 * q4 + r;
-      const float lg = __shfl(l_tot, g);
+      const float lg = acc_l[nb][r];
       const int hr = __shfl(hrow[nb], g);
       const float inv = lg > 0.f ? P.v_scale / lg : 0.f;
       if (hr >= 0) {
