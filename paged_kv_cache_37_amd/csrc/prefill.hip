@@ -42,6 +42,7 @@ constexpr int kStep = 16 * kTiles;   // keys per step (loaded together; computed
 template <bool FP8>
 using Elt = std::conditional_t<FP8, uint8_t, uint16_t>;
 
+
 // 16 bytes of pool elements as an MFMA operand: bf16 as is, FP8 codes
 // (8 bytes) widened.
 template <bool FP8>
@@ -362,13 +363,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
         const float alpha = __builtin_amdgcn_exp2f(m_run[nb] - m_use);
         m_run[nb] = m_new;
+        // output rows here are columns 4 q4 + r; whole-vector products keep
+        // each accumulator in its registers
+        const float4_v ar = {__shfl(alpha, 4 * q4), __shfl(alpha, 4 * q4 + 1), __shfl(alpha, 4 * q4 + 2),
+                             __shfl(alpha, 4 * q4 + 3)};
+        acc_l[nb] *= ar;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float ar = __shfl(alpha, 4 * q4 + r);  // output rows here are columns 4 q4 + r
-          acc_l[nb][r] *= ar;
-#pragma unroll
-          for (int n = 0; n < D / 16; ++n) acc[nb][n][r] *= ar;
-        }
+        for (int n = 0; n < D / 16; ++n) acc[nb][n] *= ar;
       }
     }
     uint4_v pa[2], pl[2];  // P as bf16, and (shared-prefix pass) the bf16 rest P - pa
