@@ -372,7 +372,25 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
         for (int n = 0; n < D / 16; ++n) acc[nb][n] *= ar;
       }
     }
-    uint4_v pa[2], pl[2];  // P as bf16, and (shared-prefix pass) the bf16 rest P - pa
+    // V operands of the round (B rows 8 q4 .. +7 are keys 4 q4 .. +3 of
+    // tile 0, then of tile 1)
+    uint4_v vb[D / 32][2];
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) {
+      vb[m][0] = lds_operand<FP8>(vs + (q4 * D + 32 * m + col) * 8);       // dim 32 m + 2 col
+      vb[m][1] = lds_operand<FP8>(vs + (q4 * D + 32 * m + 16 + col) * 8);  // dim 32 m + 2 col + 1
+      if constexpr (EDGE) {
+        if (vedge) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            vb[m][i].x &= vm[0][0]; vb[m][i].y &= vm[0][1]; vb[m][i].z &= vm[1][0]; vb[m][i].w &= vm[1][1];
+          }
+        }
+      }
+    }
+    // per column block: P = 2^(c s - m) as bf16 (and, in the shared-prefix
+    // pass, the bf16 rest P - pa), then O += P V and the row sums; block 1's
+    // softmax can run while block 0's products are in the matrix core
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const float neg_m = m_run[nb] == -INFINITY ? 0.f : -m_run[nb];
@@ -381,48 +399,31 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) pr[t][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][nb][r], c, neg_m));
-      pa[nb] = uint4_v{pack_bf16x2(pr[0][0], pr[0][1]), pack_bf16x2(pr[0][2], pr[0][3]),
-                       pack_bf16x2(pr[1][0], pr[1][1]), pack_bf16x2(pr[1][2], pr[1][3])};
+      const uint4_v pa = uint4_v{pack_bf16x2(pr[0][0], pr[0][1]), pack_bf16x2(pr[0][2], pr[0][3]),
+                                 pack_bf16x2(pr[1][0], pr[1][1]), pack_bf16x2(pr[1][2], pr[1][3])};
+      uint4_v pl;
       if constexpr (PREFIX) {
         // the decode kernels carry P as two bf16 terms; the cascade's prefix
         // pieces keep their precision, so cascade and plain decode agree
-        pl[nb] = uint4_v{pack_bf16x2(pr[0][0] - bf16_lo(pa[nb].x), pr[0][1] - bf16_hi(pa[nb].x)),
-                         pack_bf16x2(pr[0][2] - bf16_lo(pa[nb].y), pr[0][3] - bf16_hi(pa[nb].y)),
-                         pack_bf16x2(pr[1][0] - bf16_lo(pa[nb].z), pr[1][1] - bf16_hi(pa[nb].z)),
-                         pack_bf16x2(pr[1][2] - bf16_lo(pa[nb].w), pr[1][3] - bf16_hi(pa[nb].w))};
+        pl = uint4_v{pack_bf16x2(pr[0][0] - bf16_lo(pa.x), pr[0][1] - bf16_hi(pa.x)),
+                     pack_bf16x2(pr[0][2] - bf16_lo(pa.y), pr[0][3] - bf16_hi(pa.y)),
+                     pack_bf16x2(pr[1][0] - bf16_lo(pa.z), pr[1][1] - bf16_hi(pa.z)),
+                     pack_bf16x2(pr[1][2] - bf16_lo(pa.w), pr[1][3] - bf16_hi(pa.w))};
       }
-    }
-    // O += P V: B rows 8 q4 .. +7 are keys 4 q4 .. +3 of tile 0, then of tile 1
 #pragma unroll
-    for (int m = 0; m < D / 32; ++m) {
-      uint4_v b0 = lds_operand<FP8>(vs + (q4 * D + 32 * m + col) * 8);       // dim 32 m + 2 col
-      uint4_v b1 = lds_operand<FP8>(vs + (q4 * D + 32 * m + 16 + col) * 8);  // dim 32 m + 2 col + 1
-      if constexpr (EDGE) {
-        if (vedge) {
-          b0.x &= vm[0][0]; b0.y &= vm[0][1]; b0.z &= vm[1][0]; b0.w &= vm[1][1];
-          b1.x &= vm[0][0]; b1.y &= vm[0][1]; b1.z &= vm[1][0]; b1.w &= vm[1][1];
+      for (int m = 0; m < D / 32; ++m)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          acc[nb][2 * m + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_v, pa), __builtin_bit_cast(bf16x8_v, vb[m][i]), acc[nb][2 * m + i], 0, 0, 0);
+          if constexpr (PREFIX)
+            acc[nb][2 * m + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_v, pl), __builtin_bit_cast(bf16x8_v, vb[m][i]), acc[nb][2 * m + i], 0, 0, 0);
         }
-      }
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        acc[nb][2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, pa[nb]),
-                                                                 __builtin_bit_cast(bf16x8_v, b0), acc[nb][2 * m], 0, 0, 0);
-        acc[nb][2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8_v, pa[nb]), __builtin_bit_cast(bf16x8_v, b1), acc[nb][2 * m + 1], 0, 0, 0);
-        if constexpr (PREFIX) {
-          acc[nb][2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8_v, pl[nb]), __builtin_bit_cast(bf16x8_v, b0), acc[nb][2 * m], 0, 0, 0);
-          acc[nb][2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8_v, pl[nb]), __builtin_bit_cast(bf16x8_v, b1), acc[nb][2 * m + 1], 0, 0, 0);
-        }
-      }
-    }
-    // row sums of the same rounded weights the outputs use
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      acc_l[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, pa[nb]), ones, acc_l[nb], 0, 0, 0);
+      // row sums of the same rounded weights the outputs use
+      acc_l[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, pa), ones, acc_l[nb], 0, 0, 0);
       if constexpr (PREFIX)
-        acc_l[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, pl[nb]), ones, acc_l[nb], 0, 0, 0);
+        acc_l[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, pl), ones, acc_l[nb], 0, 0, 0);
     }
   };
 
