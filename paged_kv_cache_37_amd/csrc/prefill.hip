@@ -27,7 +27,9 @@
 //                 group dim' puts the even dims first, then the odd ones,
 //                 so the 16 lanes reading dims 2 col (or 2 col + 1) read
 //                 16 consecutive 16-byte rows (no LDS bank conflicts)
-// with the base-2 online softmax of the decode kernels.  P is rounded to
+// with the base-2 online softmax of the decode kernels.  An FP8 pool's codes
+// are widened to bf16 when a step is staged into LDS, so the operand reads
+// are the bf16 path's.  P is rounded to
 // bf16 once (the result stays within the bf16 tolerance; decode's two-term
 // P keeps split-K invariance, which prefill does not need).
 #include "mfma_tile.h"
@@ -42,16 +44,6 @@ constexpr int kStep = 16 * kTiles;   // keys per step (loaded together; computed
 template <bool FP8>
 using Elt = std::conditional_t<FP8, uint8_t, uint16_t>;
 
-
-// 16 bytes of pool elements as an MFMA operand: bf16 as is, FP8 codes
-// (8 bytes) widened.
-template <bool FP8>
-__device__ __forceinline__ uint4_v lds_operand(const Elt<FP8>* p) {
-  if constexpr (FP8)
-    return fp8_widen8(*(const uint2_v*)p);
-  else
-    return *(const uint4_v*)p;
-}
 
 // Wave-wide min / max, returned as a scalar (uniform) value.
 __device__ __forceinline__ int wave_min(int v) {
@@ -72,12 +64,14 @@ template <int D, bool FP8, int BS, bool PREFIX>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParams P) {
   using E = Elt<FP8>;
   constexpr int CH = 16 / sizeof(E);           // elements per 16-byte copy
-  constexpr int KROW = D + CH;                 // LDS K row: 16 bytes of padding, so 16 rows hit distinct banks
+  constexpr int KROW = D + 8;                  // LDS K row (bf16): 16 bytes of padding, so 16 rows hit distinct banks
   constexpr int TCH = 16 * D / CH;             // 16-byte chunks of one tile's K (and of its V)
   static_assert(kTiles % 2 == 0, "steps of whole 32-key rounds");
   static_assert(TCH <= kThreads, "one chunk per thread and tile");
-  __shared__ __align__(16) E k_s[2][kStep * KROW];
-  __shared__ __align__(16) E v_s[2][kStep * D];  // per 32-key round: [4 quads][D][2 tiles][4 keys]
+  // LDS holds bf16 whatever the pool's type: FP8 codes are widened once,
+  // when a step is staged, not by each of the four waves that read them
+  __shared__ __align__(16) uint16_t k_s[2][kStep * KROW];
+  __shared__ __align__(16) uint16_t v_s[2][kStep * D];  // per 32-key round: [4 quads][D][2 tiles][4 keys]
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -257,20 +251,32 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
     // this thread's V chunk: CH / 4 dims x 4 keys of quad q
     const int e0 = threadIdx.x * CH, q = e0 / (4 * D), d = (e0 - q * 4 * D) >> 2;
 #pragma unroll
-    for (int t = 0; t < kTiles; ++t) *(uint4_v*)(&k_s[buf][(16 * t + key) * KROW + cc * CH]) = kreg[t];
+    for (int t = 0; t < kTiles; ++t) {
+      uint16_t* dk = &k_s[buf][(16 * t + key) * KROW + cc * CH];
+      if constexpr (FP8) {
+        *(uint4_v*)dk = fp8_widen8(uint2_v{kreg[t].x, kreg[t].y});
+        *(uint4_v*)(dk + 8) = fp8_widen8(uint2_v{kreg[t].z, kreg[t].w});
+      } else {
+        *(uint4_v*)dk = kreg[t];
+      }
+    }
     // per dim, its 4 keys of tile 2h beside those of tile 2h + 1 (this thread
     // holds the same quad and dims of both); even dim d of its 32-dim group
     // at row (d mod 32) / 2 of the group, odd dim d + 1 at row 16 + that
     const int d_even = (d & ~31) + ((d & 31) >> 1);
 #pragma unroll
     for (int h = 0; h < kTiles / 2; ++h) {
-      E* dst_e = &v_s[buf][h * 32 * D + (q * D + d_even) * 8];
-      E* dst_o = dst_e + 16 * 8;
+      uint16_t* dst_e = &v_s[buf][h * 32 * D + (q * D + d_even) * 8];
+      uint16_t* dst_o = dst_e + 16 * 8;
       const uint4_v a = vreg[2 * h], b = vreg[2 * h + 1];
       if constexpr (FP8) {
-        // dims d .. d + 3: d and d + 2 in adjacent even rows, d + 1 and d + 3 in odd rows
-        *(uint4_v*)dst_e = uint4_v{a[0], b[0], a[2], b[2]};
-        *(uint4_v*)dst_o = uint4_v{a[1], b[1], a[3], b[3]};
+        // dims d .. d + 3 (four codes each): d and d + 2 in adjacent even
+        // rows, d + 1 and d + 3 in odd rows, widened to bf16
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint2_v wa = fp8_widen4(a[j]), wb = fp8_widen4(b[j]);
+          *(uint4_v*)((j & 1 ? dst_o : dst_e) + 8 * (j >> 1)) = uint4_v{wa.x, wa.y, wb.x, wb.y};
+        }
       } else {
         *(uint4_v*)dst_e = uint4_v{a.x, a.y, b.x, b.y};
         *(uint4_v*)dst_o = uint4_v{a.z, a.w, b.z, b.w};
@@ -299,15 +305,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
   // (rare) rescale, so the compiler can interleave softmax and MFMAs.
   auto round = [&](auto edge, int u0, int buf, int h, bool vedge, bool bad0, bool bad1) {
     constexpr bool EDGE = decltype(edge)::value;
-    const E* ks = k_s[buf] + 32 * h * KROW;
-    const E* vs = v_s[buf] + 32 * h * D;
+    const uint16_t* ks = k_s[buf] + 32 * h * KROW;
+    const uint16_t* vs = v_s[buf] + 32 * h * D;
     // S^T per tile and column block
     float4_v sc[2][2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       uint4_v kf[D / 32];
 #pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) kf[kk] = lds_operand<FP8>(ks + (t * 16 + col) * KROW + 32 * kk + 8 * q4);
+      for (int kk = 0; kk < D / 32; ++kk) kf[kk] = *(const uint4_v*)(ks + (t * 16 + col) * KROW + 32 * kk + 8 * q4);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         float4_v a = {0.f, 0.f, 0.f, 0.f};
@@ -377,8 +383,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
     uint4_v vb[D / 32][2];
 #pragma unroll
     for (int m = 0; m < D / 32; ++m) {
-      vb[m][0] = lds_operand<FP8>(vs + (q4 * D + 32 * m + col) * 8);       // dim 32 m + 2 col
-      vb[m][1] = lds_operand<FP8>(vs + (q4 * D + 32 * m + 16 + col) * 8);  // dim 32 m + 2 col + 1
+      vb[m][0] = *(const uint4_v*)(vs + (q4 * D + 32 * m + col) * 8);       // dim 32 m + 2 col
+      vb[m][1] = *(const uint4_v*)(vs + (q4 * D + 32 * m + 16 + col) * 8);  // dim 32 m + 2 col + 1
       if constexpr (EDGE) {
         if (vedge) {
 #pragma unroll
