@@ -151,3 +151,18 @@ def test_cascade_hint_beyond_table_is_rejected(gpu):
     dev = Dev(w)
     with pytest.raises(KVPoolError):
         dev.attend(shared_prefix_blocks=np.asarray(w.block_tables).shape[1] + 1)
+
+
+@pytest.mark.parametrize("scale", [-0.0884, 0.0])
+def test_cascade_scale_sign_and_zero(gpu, scale):
+    """The prefix pass runs on the prefill kernel, which carries a negative
+    scale in the queries' signs and makes a zero scale a vanishing one: the
+    cascade still matches the oracle and the plain call."""
+    w = W.shared_prefix(950, 256, [0, 1, 17, 100, 300], 32, 8, 128)
+    w.scale = float(np.float32(scale))  # float32-representable, as the kernel receives it
+    dev = Dev(w)
+    out_c = dev.attend(shared_prefix_blocks=16)
+    out_p = dev.attend()
+    ref = reference(w)
+    compare(out_c, ref, "bf16", f"cascade scale {scale}")
+    close_to_plain(out_c, out_p, ref, f"cascade scale {scale}")

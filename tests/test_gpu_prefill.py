@@ -144,3 +144,14 @@ def test_prefill_config_sampled(gpu):
         rows += [a + t for t in toks]
         refs.append(ref[toks])
     compare(out[rows], np.concatenate(refs), "bf16", "chunked-prefill batch (sampled)")
+
+
+@pytest.mark.parametrize("scale", [-0.0884, 0.0, 2.5])
+def test_prefill_scale_sign_and_zero(gpu, scale):
+    """The kernel keeps scores as c (K . q) with c > 0: a negative scale is
+    carried by the queries' signs, a zero scale gives uniform weights over
+    each row's keys, a large one sharp weights; all against the oracle."""
+    w = W.prefill_batch(700, [0, 30, 300], [40, 17, 129], 16, 4, 128)
+    w.scale = float(np.float32(scale))  # float32-representable, as the kernel receives it
+    say("prefill scale", scale)
+    compare(PDev(w).attend(), ref_of(w), "bf16", f"prefill scale {scale}")
