@@ -322,6 +322,18 @@ struct StreamLayout {
   size_t prefix, ml, o, pre_ml, pre_o, row_ml, row_o, total;
 };
 
+// Key chunks of the shared-prefix pass: enough that the pass has about as
+// many workgroups as the streaming grid (two per CU), at most
+// kMaxPrefixPieces; KVP_PREFIX_PIECES (1..8, read at each call) overrides.
+// The chunks actually used can be fewer (a chunk is whole 4-tile steps).
+static int32_t prefix_pieces_wanted(const kvp::DecodeParams& p) {
+  const long long units = (long long)p.num_kv_heads * ((p.num_seqs * p.group + 127) / 128);
+  long long want = units > 0 ? (p.stream_wgs + units - 1) / units : 1;
+  const char* ev = getenv("KVP_PREFIX_PIECES");
+  if (ev && atoi(ev) >= 1) want = atoi(ev);
+  return (int32_t)std::max(1LL, std::min<long long>(want, kvp::kMaxPrefixPieces));
+}
+
 static StreamLayout stream_workspace(const kvp::DecodeParams& p, int32_t head_dim) {
   StreamLayout L;
   const size_t slots = (size_t)p.stream_wgs * kvp::kWaves * 2 * p.heads_per_wg;
@@ -330,7 +342,7 @@ static StreamLayout stream_workspace(const kvp::DecodeParams& p, int32_t head_di
   L.prefix = kSyncBytes;
   L.ml = L.prefix + align256((size_t)(p.num_seqs + 1) * sizeof(int32_t));
   L.o = L.ml + align256(slots * 2 * sizeof(float));
-  const size_t pieces = kvp::kMaxPrefixPieces;
+  const size_t pieces = prefix_pieces_wanted(p);
   L.pre_ml = L.o + align256(slots * head_dim * sizeof(float));
   L.pre_o = L.pre_ml + align256(pieces * qh * 2 * sizeof(float));
   L.row_ml = L.pre_o + align256(pieces * qh * head_dim * sizeof(float));
@@ -402,16 +414,11 @@ static int32_t decode(kvp_pool pool, const kvp_decode_args* a, const void* k_new
   // the shared-prefix pass is a STREAM feature for full-context rows; elsewhere the hint is ignored
   if (path == PATH_STREAM && a->sliding_window == 0) p.prefix_blocks = a->shared_prefix_blocks;
   if (p.prefix_blocks > 0) {
-    // split the prefix's keys so that the pass has about as many
-    // workgroups as the streaming grid (two per CU), in chunks of whole
-    // 4-tile steps; KVP_PREFIX_PIECES (1..8) overrides the count
+    // split the prefix's keys into chunks of whole 4-tile steps (the
+    // workspace holds as many pieces as prefix_pieces_wanted gives)
     const int32_t tiles = p.prefix_blocks << p.bshift;
-    const long long units = (long long)d.num_kv_heads * ((a->num_seqs * p.group + 127) / 128);
-    long long want = (p.stream_wgs + units - 1) / units;
-    const char* ev = getenv("KVP_PREFIX_PIECES");
-    if (ev && atoi(ev) >= 1) want = atoi(ev);
-    want = std::max(1LL, std::min<long long>(want, kvp::kMaxPrefixPieces));
-    const int32_t per = (int32_t)((tiles + want - 1) / want);
+    const int32_t want = prefix_pieces_wanted(p);
+    const int32_t per = (tiles + want - 1) / want;
     p.prefix_chunk = (per + 3) / 4 * 4;
     p.prefix_pieces = (tiles + p.prefix_chunk - 1) / p.prefix_chunk;
   }
