@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_helpers import compare, host_to_torch, pool_dtype, say, torch_dtype, torch_to_bits
+from gpu_helpers import compare, host_to_torch, pool_dtype, say, to_f64, torch_dtype, torch_to_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -155,3 +155,39 @@ def test_prefill_scale_sign_and_zero(gpu, scale):
     w.scale = float(np.float32(scale))  # float32-representable, as the kernel receives it
     say("prefill scale", scale)
     compare(PDev(w).attend(), ref_of(w), "bf16", f"prefill scale {scale}")
+
+
+@pytest.mark.parametrize("bad_entry", [-1, 10 ** 6])
+def test_prefill_bad_table_entry_is_skipped(gpu, bad_entry):
+    """A table entry outside the pool, inside a row: the kernel leaves its
+    unmasked step loop at that step and skips the block's keys.  With no
+    window every chunk query attends all earlier keys, so the result is the
+    oracle's on the same row with that block taken out (16 fewer keys).
+    The other sequence is untouched; every output is finite."""
+    w = W.prefill_batch(800, [300, 200], [129, 64], 16, 4, 128)
+    rows = [list(np.asarray(w.block_tables[s])) for s in range(2)]
+    d = PDev(w)
+    tables = np.ascontiguousarray(w.block_tables).copy()
+    tables[0, 5] = bad_entry  # positions 80 .. 95 of sequence 0
+    d.tables = torch.from_numpy(tables).cuda()
+    out = d.attend()
+    got = to_f64(out)
+    assert np.isfinite(got).all()
+    w2 = W.prefill_batch(800, [300, 200], [129, 64], 16, 4, 128)
+    t2 = np.full_like(tables, 0)
+    r0 = rows[0][:5] + rows[0][6:]
+    t2[0, :len(r0)] = r0
+    t2[1, :len(rows[1])] = rows[1]
+    w2.block_tables = t2
+    w2.seq_lens = np.array([int(w.seq_lens[0]) - 16, int(w.seq_lens[1])], np.int32)
+    ref = oracle.prefill_attention(w.pool, 0, w.q, w.cu_q_lens, t2, w2.seq_lens, 0, w.scale)
+    compare(out, ref, "bf16", f"prefill with table entry {bad_entry} skipped")
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,B,window", [(8, 2, 64, 16, 0), (16, 16, 64, 32, 24), (32, 8, 128, 32, 0)])
+def test_prefill_fp8_shapes(gpu, Hq, Hkv, D, B, window):
+    """FP8 pools (codes widened when staged into LDS) at head_dim 64 and 128,
+    G = 1 and 4, 16- and 32-token blocks, with and without a window."""
+    w = W.prefill_batch(900 + D + B + window, PRIOR, QLEN, Hq, Hkv, D, window=window, dtype="fp8", block_size=B)
+    say("prefill fp8", Hq, Hkv, D, B, window)
+    compare(PDev(w).attend(), ref_of(w), "bf16", f"prefill fp8 G{Hq // Hkv} D{D} B{B} W{window}")
