@@ -109,10 +109,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
     // every prefix block is full and attended by every row; the chunk's
     // tiles [j0, ntiles) start on a step
     row = P.block_tables;
-    // 0: the shared prefix starts at position 0 (read from the parameters,
-    // which hold 0 here: folded as constants they made the compiler spill)
-    t0 = P.window;
-    so = P.window;
+    t0 = 0;  // the shared prefix starts at position 0
+    so = 0;
     const int j0 = kc * P.prefix_chunk;
     ntiles = min(j0 + P.prefix_chunk, P.prefix_blocks << BS);
     send = ntiles * kBlock;
