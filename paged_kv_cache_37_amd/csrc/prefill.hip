@@ -305,8 +305,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
     constexpr bool EDGE = decltype(edge)::value;
     const uint16_t* ks = k_s[buf] + 32 * h * KROW;
     const uint16_t* vs = v_s[buf] + 32 * h * D;
-    // S^T per tile and column block
+    // S^T per tile and column block, issued at a raised wave priority so
+    // that of the two waves on a SIMD the one in its product phase issues
+    // first and the other fills the gaps with its softmax
     float4_v sc[2][2];
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       uint4_v kf[D / 32];
@@ -322,6 +325,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
         sc[t][nb] = a;
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     // keys of the step outside the span (or in a bad tile) hold no data:
     // zero their V and mask their scores for every column
     unsigned vm[2][2] = {{~0u, ~0u}, {~0u, ~0u}};  // [tile][half]: keys 4q4 + {0,1} and {2,3} hold data
