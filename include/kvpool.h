@@ -209,10 +209,7 @@ typedef struct {
 
 /*
  * Bytes of workspace paged_decode_attention needs for these sizes (0 when a
- * single pass suffices, i.e. every row fits in one partition).  A workspace
- * must be zero-filled once, before its first use: its first 64 KiB hold
- * the STREAM variant's arrival counters, which every call leaves at zero
- * again and nothing else writes.  The rest needs no initialisation.
+ * single pass suffices, i.e. every row fits in one partition).
  */
 size_t paged_decode_workspace_bytes(kvp_pool pool, int32_t num_seqs, int32_t num_q_heads,
                                     int32_t max_blocks_per_seq, int32_t partition_tokens);
@@ -242,20 +239,14 @@ size_t paged_decode_workspace_bytes(kvp_pool pool, int32_t num_seqs, int32_t num
  *   Long rows are split into partitions of partition_tokens table slots;
  *   each partition leaves its partial result (running max, sum and
  *   unnormalised output) in `workspace` (paged_decode_workspace_bytes()
- *   bytes, zero-filled before its first use) and a second kernel on the
+ *   bytes, contents need no initialisation) and a second kernel on the
  *   same stream merges them.  The STREAM variant splits the batch's tiles
- *   evenly over its waves; the rows cut between waves are merged by a
- *   second kernel, or (KVP_STREAM_MERGE=inkernel, no shared prefix) each by
- *   the wave that finishes its piece last, counted in the workspace.  Calls
- *   that share one workspace must not overlap.
+ *   evenly over its waves; the rows cut between waves are merged the same
+ *   way.  Calls that share one workspace must not overlap.
  *
  *   Environment: KVP_DECODE_DEPTH (1..3 for the MFMA variant, 1..2 for
  *   the others) overrides how many blocks each wave keeps in flight ahead
- *   of the one it computes (a tuning knob, read once per process);
- *   KVP_STREAM_MERGE=inkernel makes the STREAM variant merge cut rows in
- *   the decode kernel itself: one launch instead of two, faster on long
- *   uniform rows, slower on short mixed ones (read at each call; the same
- *   bits either way).
+ *   of the one it computes (a tuning knob, read once per process).
  *
  *   Errors: KVP_ERR_INVALID_ARG (nulls, layer, heads, partition size),
  *   KVP_ERR_UNSUPPORTED (variant/dtype/head group combination),

@@ -15,18 +15,7 @@
 // while the current row streams.  A row that lies wholly inside a wave's
 // range is normalised and stored by that wave; the (at most two) rows cut by
 // a range boundary leave a partial result (running max, sum, unnormalised
-// output), merged into the row's output by decode_stream_reduce or, when
-// the launch passes arrival counters, by whichever wave holding a piece of
-// it finishes last.
-//
-// The in-kernel merge needs no fence that writes back an L2: the pieces are
-// stored and read with agent-scope relaxed atomic accesses, which the
-// CDNA3/CDNA4 memory model keeps coherent across the XCDs' L2s, and each
-// wave waits for its own stores to complete (vmcnt 0) before it adds its
-// arrival to the row's counter.  The wave that brings the counter to the
-// row's piece count therefore reads every piece complete; it then resets
-// the counter to zero for the next launch.  Counters start at zero in a
-// fresh (zero-filled) workspace.
+// output) that a second kernel merges.
 //
 // Ranges are contiguous per XCD (workgroup i runs on XCD i mod 8): the
 // tiles of one head group, which share physical blocks across sequences
@@ -67,8 +56,8 @@ __device__ __forceinline__ long long floor_div(long long num, long long den) {
 // Pieces of a cut row, merged in wave order kMergeChunk at a time: each
 // round takes the round's largest max, rescales what was merged so far once,
 // then adds the round's pieces (max m, sum l, unnormalised o; an absent
-// piece is m = -inf, l = 0, o = 0).  The in-kernel merge and the merge
-// kernel both use it, so either gives the same bits.
+// piece is m = -inf, l = 0, o = 0).  Both merge kernels use it, so they
+// give the same bits.
 constexpr int kMergeChunk = 8;
 
 template <int PER, int CH>
@@ -90,21 +79,6 @@ __device__ __forceinline__ void merge_round(float& M, float& den, float (&num)[P
     for (int e = 0; e < PER; ++e) num[e] += f * v[u][e];
   }
   M = Mc;
-}
-
-// Agent-scope relaxed atomic accesses (global stores and loads with sc1 on
-// this target): coherent across the XCDs without an L2 write-back.
-__device__ __forceinline__ void store_coherent(float* p, float a, float b) {
-  const unsigned long long bits = ((unsigned long long)__float_as_uint(b) << 32) | __float_as_uint(a);
-  __hip_atomic_store((unsigned long long*)p, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float2 load_coherent2(const float* p) {
-  const unsigned long long bits =
-      __hip_atomic_load((const unsigned long long*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return make_float2(__uint_as_float((unsigned)bits), __uint_as_float((unsigned)(bits >> 32)));
-}
-__device__ __forceinline__ float load_coherent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The pieces of a cut row [a, a + nb) of the work list (T tiles over W
@@ -317,11 +291,6 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
     for (int kk = 0; kk < D / 32; ++kk) q_next[kk] = g < nh_n ? *(const uint4_v*)(qp + 32 * kk) : uint4_v{0, 0, 0, 0};
   }
 
-  // Rows of this wave cut by a range boundary (at most its first and its
-  // last), for the arrival after the loop (in-kernel merge only).
-  int n_cut = 0;
-  RowCtx cut0 = cr, cut1 = cr;
-
   auto finish_row = [&]() {
     const float l_tot = rows_sum(st.l_run);
     const int q4 = lane >> 4;
@@ -361,30 +330,17 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
     } else {
       const int slot = ra <= t_begin ? 0 : 1;
       const size_t pbase = (size_t)(widx * 2 + slot) * P.heads_per_wg;
-      const bool merge_here = P.arrive != nullptr;  // else the merge kernel reads the pieces
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int g = 4 * q4 + r4;
         if (g < c_nh) {
-          float* o = P.part_o + (pbase + g) * D;
+          float2* o = (float2*)(P.part_o + (pbase + g) * D);
 #pragma unroll
-          for (int m = 0; m < D / 32; ++m) {
-            float* e = o + 2 * (16 * m + (lane & 15));
-            if (merge_here) store_coherent(e, st.acc[2 * m][r4], st.acc[2 * m + 1][r4]);
-            else *(float2*)e = make_float2(st.acc[2 * m][r4], st.acc[2 * m + 1][r4]);
-          }
+          for (int m = 0; m < D / 32; ++m)
+            o[16 * m + (lane & 15)] = make_float2(st.acc[2 * m][r4], st.acc[2 * m + 1][r4]);
         }
       }
-      if (lane < c_nh) {
-        float* e = P.part_ml + (pbase + lane) * 2;
-        if (merge_here) store_coherent(e, st.m_run, l_tot);
-        else *(float2*)e = make_float2(st.m_run, l_tot);
-      }
-      if (merge_here) {  // arrive after the loop, once these stores are complete
-        if (n_cut == 0) cut0 = cr;
-        else cut1 = cr;
-        ++n_cut;
-      }
+      if (lane < c_nh) *(float2*)(P.part_ml + (pbase + lane) * 2) = make_float2(st.m_run, l_tot);
     }
   };
 
@@ -532,68 +488,6 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
     }
   }
   finish_row();
-  if (n_cut == 0) return;
-
-  // Arrival at the cut rows, then the merge of those this wave completes.
-  // Each cut row's counter is that of the wave holding its last tile (the
-  // row is that wave's first, so no two rows share one).
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's piece stores are complete
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  constexpr int PER = D / 64, CH = kMergeChunk;
-  for (int c = 0; c < n_cut; ++c) {
-    const RowCtx r = c == 0 ? cut0 : cut1;
-    const CutPieces pc(r.a, r.nb, T, W);
-    int old = 0;
-    if (lane == 0) old = __hip_atomic_fetch_add(P.arrive + pc.w_last, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    old = __builtin_amdgcn_readfirstlane(old);
-    if (old != pc.n - 1) continue;
-    if (lane == 0) __hip_atomic_store(P.arrive + pc.w_last, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int h0 = head0(r.hg), nh = heads(r.hg);
-    for (int g0 = 0; g0 < nh; g0 += 4) {  // four heads per pass, lane l holding dims l + 64 e
-      float M[4], den[4], num[4][PER];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        M[g] = -INFINITY;
-        den[g] = 0.f;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) num[g][e] = 0.f;
-      }
-      for (int k0 = 0; k0 < pc.n; k0 += CH) {
-        // every load is of a piece and head that exist (the last ones for
-        // absent places), and absent places weigh nothing
-        float m[4][CH], l[4][CH], v[4][CH][PER];
-#pragma unroll
-        for (int u = 0; u < CH; ++u) {
-          const bool use = k0 + u < pc.n;
-          const size_t pb = (size_t)pc.slot(use ? k0 + u : pc.n - 1) * P.heads_per_wg;
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const bool ok = use && g0 + g < nh;
-            const size_t ph = pb + (g0 + g < nh ? g0 + g : g0);
-            const float2 ml = load_coherent2(P.part_ml + ph * 2);
-            m[g][u] = ok ? ml.x : -INFINITY;
-            l[g][u] = ok ? ml.y : 0.f;
-#pragma unroll
-            for (int e = 0; e < PER; ++e) {
-              const float x = load_coherent(P.part_o + ph * D + lane + 64 * e);
-              v[g][u][e] = ok ? x : 0.f;
-            }
-          }
-        }
-#pragma unroll
-        for (int g = 0; g < 4; ++g) merge_round(M[g], den[g], num[g], m[g], l[g], v[g]);
-      }
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        if (g0 + g >= nh) break;
-        const float inv = den[g] > 0.f ? P.v_scale / den[g] : 0.f;
-        uint16_t* out = (uint16_t*)P.out + ((size_t)r.s * P.num_q_heads + h0 + g0 + g) * D;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) out[lane + 64 * e] = bf16_rne(num[g][e] * inv);
-      }
-    }
-  }
 }
 
 // Merge of the rows cut by range boundaries.  One wave per (sequence,
@@ -737,7 +631,7 @@ hipError_t launch_sd(const DecodeParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((decode_stream_kernel<D, DEPTH, false, FP8, BS>), dim3(p.stream_wgs), dim3(kThreads), 0, stream, p);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.arrive) return e;  // cut rows merged by their last wave
+  if (e != hipSuccess) return e;
   const dim3 grid((p.num_q_heads + 3) / 4, p.num_seqs);
   hipLaunchKernelGGL((decode_stream_reduce_kernel<D>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();

@@ -12,7 +12,6 @@ constexpr int kBlock = 16;      // tokens per tile: the unit every kernel stream
 constexpr int kWaves = 4;       // waves per decode workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxStreamSeqs = 4096;  // sequences one streaming launch can take (LDS prefix sums)
-constexpr int kMaxStreamWaves = 16384;  // waves of a streaming grid (one arrival counter each)
 constexpr int kMaxPrefixPieces = 8;    // key chunks of the shared-prefix pass
 
 // Geometry and arguments of one decode launch, resolved on the host.
@@ -40,8 +39,6 @@ struct DecodeParams {
   int32_t depth;                // blocks of K/V a wave keeps in flight ahead of the one it computes
   int32_t* prefix;              // [S + 1] tiles before each sequence's row     (streaming only)
   int32_t stream_wgs;           // persistent workgroups of a streaming launch   (streaming only)
-  int32_t* arrive;              // [waves] arrival counters of cut rows, zero between launches;
-                                // NULL: a merge kernel merges them              (streaming only)
   const void* k_new;            // [S][Hkv][D] new token per sequence        (fused write only)
   const void* v_new;            // [S][Hkv][D]                               (fused write only)
   const int32_t* slot_mapping;  // [S]; NULL: attention only                 (fused write only)

@@ -188,7 +188,7 @@ static int32_t stream_workgroups(int32_t head_dim, int32_t depth, bool fused, bo
 static bool stream_fits(int32_t num_seqs, int32_t max_tiles, int32_t head_groups, int32_t wgs) {
   const double entries = (double)num_seqs * max_tiles;
   const double waves = (double)wgs * kvp::kWaves;
-  return num_seqs <= kvp::kMaxStreamSeqs && waves <= kvp::kMaxStreamWaves && entries < 2147483647.0 &&
+  return num_seqs <= kvp::kMaxStreamSeqs && entries < 2147483647.0 &&
          entries * head_groups * (waves + 1.0) < 4503599627370496.0;  // 2^52
 }
 
@@ -293,27 +293,20 @@ static int32_t plan(kvp_pool pool, int32_t num_seqs, int32_t num_q_heads, int32_
 
 static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-// Every workspace starts with the streaming kernel's arrival counters (one
-// per wave of its grid), zero before a workspace's first use and left zero
-// by every launch; no other use of the workspace writes them, so one
-// workspace can serve every variant in turn.
-constexpr size_t kSyncBytes = (size_t)kvp::kMaxStreamWaves * sizeof(int32_t);
-
 // Workspace of the partitioned kernels: unnormalised partial outputs and
-// their (max, sum) pairs per (sequence, query head, partition), after the
-// counters.
+// their (max, sum) pairs per (sequence, query head, partition).
 static size_t grid_workspace(const kvp::DecodeParams& p, int32_t head_dim, size_t* o_off, size_t* ml_off) {
   if (p.num_parts <= 1) {
     *o_off = *ml_off = 0;
     return 0;
   }
   const size_t rows = (size_t)p.num_seqs * p.num_q_heads * p.num_parts;
-  *o_off = kSyncBytes;
-  *ml_off = kSyncBytes + align256(rows * head_dim * sizeof(float));
+  *o_off = 0;
+  *ml_off = align256(rows * head_dim * sizeof(float));
   return *ml_off + rows * 2 * sizeof(float);
 }
 
-// Workspace of the streaming kernel: the arrival counters, prefix sums, then
+// Workspace of the streaming kernel: prefix sums, then
 // two partial slots per wave for up to heads_per_wg heads ((max, sum) pairs
 // and outputs), then the shared-prefix pieces: one per (sequence, query
 // head) from the prefix pass and one per (row, head) for tails a single wave
@@ -339,7 +332,7 @@ static StreamLayout stream_workspace(const kvp::DecodeParams& p, int32_t head_di
   const size_t slots = (size_t)p.stream_wgs * kvp::kWaves * 2 * p.heads_per_wg;
   const size_t qh = (size_t)p.num_seqs * p.num_q_heads;
   const size_t rows = (size_t)p.num_kv_heads * p.qgroups * p.num_seqs * p.heads_per_wg;
-  L.prefix = kSyncBytes;
+  L.prefix = 0;
   L.ml = L.prefix + align256((size_t)(p.num_seqs + 1) * sizeof(int32_t));
   L.o = L.ml + align256(slots * 2 * sizeof(float));
   const size_t pieces = prefix_pieces_wanted(p);
@@ -432,11 +425,6 @@ static int32_t decode(kvp_pool pool, const kvp_decode_args* a, const void* k_new
     if (!aligned(a->workspace, 256)) return fail(KVP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
     char* w = (char*)a->workspace;
     if (path == PATH_STREAM) {
-      // cut rows are merged by a second kernel, or with KVP_STREAM_MERGE=inkernel
-      // (and no shared prefix, whose merge pass takes every row) by their last wave
-      const char* mk = getenv("KVP_STREAM_MERGE");
-      const bool in_kernel = p.prefix_blocks == 0 && mk && std::strcmp(mk, "inkernel") == 0;
-      p.arrive = in_kernel ? (int32_t*)w : nullptr;
       p.prefix = (int32_t*)(w + SL.prefix);
       p.part_ml = (float*)(w + SL.ml);
       p.part_o = (float*)(w + SL.o);

@@ -156,11 +156,9 @@ def paged_decode_workspace_bytes(pool: KVPool, num_seqs: int, num_q_heads: int, 
 def make_workspace(pool: KVPool, num_seqs: int, num_q_heads: int, max_blocks_per_seq: int,
                    partition_tokens: int = 0) -> Optional[torch.Tensor]:
     """Workspace for split launches of these sizes (None when a single pass
-    suffices), zero-filled as the library requires before its first use
-    (calls leave its counters at zero, so it can be reused as is).  Calls
-    that share one workspace must not overlap."""
+    suffices).  Calls that share one workspace must not overlap."""
     n = paged_decode_workspace_bytes(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens)
-    return torch.zeros(n, dtype=torch.uint8, device=pool.device) if n else None
+    return torch.empty(n, dtype=torch.uint8, device=pool.device) if n else None
 
 
 def _decode_args(pool: KVPool, layer: int, q: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,

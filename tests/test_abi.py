@@ -139,7 +139,7 @@ def test_decode_rejects_bad_arguments_before_launch(ops):
     assert call(max_blocks_per_seq=64, partition_tokens=256) == E.KVP_ERR_WORKSPACE_TOO_SMALL
     need = ops.lib.paged_decode_workspace_bytes(h, 2, 8, 64, 256)
     rows = 2 * 8 * 4
-    assert need == 65536 + rows * 64 * 4 + rows * 2 * 4  # arrival counters, partial outputs, (max, sum) pairs
+    assert need == rows * 64 * 4 + rows * 2 * 4  # partial outputs and their (max, sum) pairs
     assert ops.lib.paged_decode_workspace_bytes(h, 2, 8, 4, 256) == 0
     assert call(num_seqs=0) == 0  # nothing to do
     ops.lib.kv_pool_destroy(h)
