@@ -166,3 +166,15 @@ def test_cascade_scale_sign_and_zero(gpu, scale):
     ref = reference(w)
     compare(out_c, ref, "bf16", f"cascade scale {scale}")
     close_to_plain(out_c, out_p, ref, f"cascade scale {scale}")
+
+
+def test_cascade_long_prefix(gpu):
+    """A shared prefix longer than 4096 tiles (4500 blocks, 72000 tokens):
+    the prefix pass walks any number of table entries, in chunks."""
+    w = W.shared_prefix(960, 4500 * 16, [0, 5, 40], 8, 2, 64)
+    say("long prefix", w.num_blocks, "blocks")
+    dev = Dev(w)
+    out_c = dev.attend(shared_prefix_blocks=4500)
+    ref = reference(w)
+    compare(out_c, ref, "bf16", "cascade long prefix")
+    close_to_plain(out_c, dev.attend(), ref, "long prefix")
