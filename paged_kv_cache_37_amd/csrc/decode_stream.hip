@@ -56,8 +56,8 @@ __device__ __forceinline__ long long floor_div(long long num, long long den) {
 // Pieces of a cut row, merged in wave order kMergeChunk at a time: each
 // round takes the round's largest max, rescales what was merged so far once,
 // then adds the round's pieces (max m, sum l, unnormalised o; an absent
-// piece is m = -inf, l = 0, o = 0).  Both merge kernels use it, so they
-// give the same bits.
+// piece is m = -inf, l = 0, o = 0).  The merge kernel folds the shared
+// prefix's chunk pieces and a row's wave pieces with it.
 constexpr int kMergeChunk = 8;
 
 template <int PER, int CH>

@@ -27,11 +27,22 @@
 //                 group dim' puts the even dims first, then the odd ones,
 //                 so the 16 lanes reading dims 2 col (or 2 col + 1) read
 //                 16 consecutive 16-byte rows (no LDS bank conflicts)
-// with the base-2 online softmax of the decode kernels.  An FP8 pool's codes
-// are widened to bf16 when a step is staged into LDS, so the operand reads
-// are the bf16 path's.  P is rounded to
-// bf16 once (the result stays within the bf16 tolerance; decode's two-term
-// P keeps split-K invariance, which prefill does not need).
+// with the base-2 online softmax of the decode kernels: scores c (K . q)
+// with c = |scale| log2(e) > 0 (a negative scale flips the queries' signs),
+// the running max raised only past a slack, the row sums an MFMA of P with
+// a ones operand.  An FP8 pool's codes are widened to bf16 when a step is
+// staged into LDS, so the operand reads are the bf16 path's.  P is rounded
+// to bf16 once (the result stays within the bf16 tolerance; decode's
+// two-term P keeps split-K invariance, which prefill does not need).
+//
+// The key walk is three loops over steps: leading steps that need masks
+// (window start, first slots, bad tiles), the unmasked interior (one basic
+// block apart from the rare rescale, so softmax and MFMAs interleave), and
+// trailing masked steps (the causal diagonal, the last block).
+//
+// The same kernel (PREFIX) runs the shared-prefix pass of cascade decode:
+// every sequence's decode query as a row, a chunk of the shared prefix as
+// the keys, two-term P like the decode kernels, a partial result out.
 #include "mfma_tile.h"
 
 namespace kvp {
