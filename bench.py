@@ -27,6 +27,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -48,11 +49,20 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def _code_only(src: str) -> str:
+    """Source text without comments and blank space, so that a comment edit
+    does not mark the profiled kernels as changed (string literals in these
+    files hold no comment markers)."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def kernel_hash() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "paged_kv_cache_37_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "paged_kv_cache_37_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
