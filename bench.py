@@ -359,7 +359,7 @@ def main() -> int:
 
     import workloads as W
     from paged_kv_cache_37_amd import ops
-    from paged_kv_cache_37_amd.blockpool import shared_prefix_blocks
+    from paged_kv_cache_37_amd.blockpool import rows_share_blocks, shared_prefix_blocks
 
     dev = torch.device("cuda:0")
     # an FP8 pool holds half the bytes per layer: twice the slices for the same footprint
@@ -397,7 +397,10 @@ def main() -> int:
     # blocks every row shares (a cached prompt prefix): attended once for the batch
     shared = 0 if args.no_shared_prefix else shared_prefix_blocks(np.asarray(w.block_tables_after), w.seq_lens_after,
                                                                   block_size=w.block_size)
-    log(f"shared prefix: {shared} blocks")
+    # blocks listed by several rows past that prefix: tiles read with cached loads
+    reuse = rows_share_blocks(np.asarray(w.block_tables_after), w.seq_lens_after, prefix_blocks=shared,
+                              block_size=w.block_size, window=w.window)
+    log(f"shared prefix: {shared} blocks; other blocks shared between rows: {reuse}")
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
 
@@ -407,12 +410,12 @@ def main() -> int:
     def attend(layer):
         ops.paged_decode_attention(pool, layer, q, tables, lens, w.scale, out=out, sliding_window=w.window,
                                    partition_tokens=args.partition_tokens, variant=args.variant, workspace=ws,
-                                   stream=stream, shared_prefix_blocks=shared)
+                                   stream=stream, shared_prefix_blocks=shared, shared_blocks=reuse)
 
     def fused(layer):
         ops.paged_decode_step(pool, layer, q, tables, lens, w.scale, k_new, v_new, slots, out=out,
                               sliding_window=w.window, partition_tokens=args.partition_tokens, variant=args.variant,
-                              workspace=ws, stream=stream, shared_prefix_blocks=shared)
+                              workspace=ws, stream=stream, shared_prefix_blocks=shared, shared_blocks=reuse)
 
     def step(i):
         if args.unfused:
@@ -512,6 +515,7 @@ def main() -> int:
             "partition_tokens": args.partition_tokens,
             "fused_step": not args.unfused,
             "shared_prefix_blocks": shared,
+            "shared_blocks": bool(reuse),
             "seed": w.seed,
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),

@@ -205,6 +205,9 @@ typedef struct {
   int32_t shared_prefix_blocks; /* 0, or: the first this-many entries of every
                                    row are the same full blocks (a shared
                                    prompt prefix); see paged_decode_attention */
+  int32_t shared_blocks;        /* nonzero: some block past the shared prefix
+                                   is listed by more than one row; a hint that
+                                   changes no result (see paged_decode_attention) */
 } kvp_decode_args;
 
 /*
@@ -270,6 +273,19 @@ int32_t paged_decode_attention(kvp_pool pool, const kvp_decode_args* args, hipSt
  *   max_blocks_per_seq (KVP_ERR_INVALID_ARG otherwise); if the promise does
  *   not hold the outputs are unspecified (memory is still only read inside
  *   the pool and the table rows).
+ *
+ *   Blocks read by several rows.  By default the STREAM variant reads the
+ *   K/V tiles with non-temporal loads: when every block of the batch is
+ *   listed by one row only (the case without sharing, and the private
+ *   tails of a cascade), each line is read once and streaming it past the
+ *   caches is faster.  Rows may also share blocks outside the prefix
+ *   passed as shared_prefix_blocks ([Optimizing] "Copy-on-Write (CoW) for
+ *   Parallel Sampling and Prefix Caching": sequences of one prompt list the
+ *   same physical blocks until they write to them; the host's reference
+ *   counts show it).  shared_blocks != 0 says so: tiles are then read with
+ *   ordinary cached loads, and rows that share a block find it in the L2
+ *   cache.  The hint changes no output bit, only speed; the other variants
+ *   always use cached loads.
  */
 
 /*

@@ -76,6 +76,7 @@ class DecodeArgs(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("shared_prefix_blocks", ctypes.c_int32),
+        ("shared_blocks", ctypes.c_int32),
     ]
 
 

@@ -411,6 +411,31 @@ def paging_waste_slots(num_tokens: int, block_size: int = 16) -> int:
     return (-num_tokens) % block_size
 
 
+def rows_share_blocks(rows: Sequence[Sequence[int]], seq_lens: Sequence[int], prefix_blocks: int = 0,
+                      block_size: int = 16, window: int = 0) -> bool:
+    """Whether some physical block is listed by more than one row past the
+    first `prefix_blocks` entries (the part of each row decode attention
+    reads itself): sequences of one prompt keep listing the same blocks
+    until copy-on-write gives them their own ([Optimizing] "Copy-on-Write
+    (CoW) for Parallel Sampling and Prefix Caching"; the reference counts of
+    the pool show the same).  paged_decode_attention's shared_blocks hint.
+    Only the entries holding attended positions count (with a sliding
+    window a row lists the blocks covering the last `window` positions)."""
+    seen = set()
+    for r, ctx in zip(rows, seq_lens):
+        ctx = int(ctx)
+        if ctx <= 0:
+            continue
+        first = max(0, ctx - window) if window > 0 else 0
+        used = (ctx - 1) // block_size - first // block_size + 1
+        for b in r[prefix_blocks:used]:
+            b = int(b)
+            if b in seen:
+                return True
+            seen.add(b)
+    return False
+
+
 def shared_prefix_blocks(rows: Sequence[Sequence[int]], seq_lens: Sequence[int], block_size: int = 16) -> int:
     """Leading table entries that name the same physical block in every row
     and are full, attended blocks in every sequence: the part of a batch's

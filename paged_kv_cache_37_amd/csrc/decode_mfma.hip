@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kThreads, KVP_MFMA_WAVES_PER_EU) void decode_mfma_k
   int my_id = 0;
   if (BS == 0 && lane < P.part_blocks && jl < P.max_blocks) my_id = row[jl];
   MfmaRow<D> st;
-  st.load_q((const uint16_t*)P.q, (size_t)s * P.num_q_heads + h0, nh, lane);
+  st.template load_q<FP8>((const uint16_t*)P.q, (size_t)s * P.num_q_heads + h0, nh, lane);
   const RowSpan rs = row_span(ctx, P.window, P.max_blocks, BS);
   const int t0 = BS ? rs.t0 : 0;
   if (BS != 0 && lane < P.part_blocks && jl < rs.nblocks) my_id = row[(t0 + jl) >> BS];
@@ -68,7 +68,7 @@ __global__ __launch_bounds__(kThreads, KVP_MFMA_WAVES_PER_EU) void decode_mfma_k
   const int nbp = min(P.part_blocks, rs.nblocks - jb);
 
   const void* pool = P.pool_layer;
-  const MfmaLanes la = mfma_lanes<D, BS>(P.num_kv_heads, kvh, lane);
+  const MfmaLanes la = mfma_lanes<D, BS, FP8>(P.num_kv_heads, kvh, lane);
   st.reset();
   const int so = rs.start_off;
   const int send = rs.start_off + rs.n;
@@ -77,8 +77,8 @@ __global__ __launch_bounds__(kThreads, KVP_MFMA_WAVES_PER_EU) void decode_mfma_k
   const int cnt = nbp > wave ? (nbp - wave + kWaves - 1) / kWaves : 0;
   auto issue = [&](int k, MfmaTiles<D, FP8>& t) {
     const int kc = k < cnt ? k : cnt - 1;  // past the end: re-read the last block (a cache hit)
-    mfma_issue<BS>(t, pool, la, __builtin_amdgcn_readlane(my_id, wave + kc * kWaves),
-                   (t0 + jb + wave + kc * kWaves) & ((1 << BS) - 1), P.num_blocks);
+    mfma_issue<BS, false>(t, pool, la, __builtin_amdgcn_readlane(my_id, wave + kc * kWaves),
+                          (t0 + jb + wave + kc * kWaves) & ((1 << BS) - 1), P.num_blocks);
   };
 
   // Software pipeline: the loads of block k + DEPTH are issued before block k

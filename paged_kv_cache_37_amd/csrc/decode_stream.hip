@@ -128,7 +128,9 @@ struct StreamTile {
 // own last block), so no ordering between waves is needed.  Into an FP8
 // pool the new token goes as its codes (the same rounding as cache_write),
 // and the attention uses those codes.
-template <int D, int DEPTH, bool FUSED, bool FP8, int BS>  // BS = log2(block size / 16)
+// NT: the tiles are read with non-temporal loads (no block of the batch is
+// listed by two rows), else with cached ones.
+template <int D, int DEPTH, bool FUSED, bool FP8, int BS, bool NT>  // BS = log2(block size / 16)
 __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stream_kernel(const DecodeParams P) {
   constexpr int NBUF = DEPTH + 1;
   __shared__ int pre[kMaxStreamSeqs + 1];  // pre[s] = tiles of sequences < s
@@ -236,14 +238,12 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
   int nt0 = t0_of(nr.s);
   int ids_n = lane < nr.nb ? tid(nr.s, nt0, lane) : 0;
   constexpr int SUB = (1 << BS) - 1;
-  MfmaLanes ila = mfma_lanes<D, BS>(P.num_kv_heads, ir.hg / P.qgroups, lane);
+  MfmaLanes ila = mfma_lanes<D, BS, FP8>(P.num_kv_heads, ir.hg / P.qgroups, lane);
   int issued = 0;
 
   auto issue = [&](StreamTile<D, FP8>& x) {
-    if (issued >= n_tiles) {  // past the range: re-issue the last tile (a cache hit), same context
-      mfma_issue<BS>(x.t, pool, ila,
-                     __builtin_amdgcn_readlane(ij - 1 - ids_base < 64 ? ids_a : ids_b, (ij - 1 - ids_base) & 63),
-                     (it0 + ptiles + ij - 1) & SUB, P.num_blocks);
+    if (issued >= n_tiles) {  // past the range: loads of a line just read (the current row's queries)
+      mfma_issue_hot(x.t, q + ((size_t)ir.s * P.num_q_heads + head0(ir.hg)) * D);
       x.j = -1;
       return;
     }
@@ -258,14 +258,14 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
       nr = row_after(ir);
       nt0 = t0_of(nr.s);
       ids_n = lane < nr.nb ? tid(nr.s, nt0, lane) : 0;
-      ila = mfma_lanes<D, BS>(P.num_kv_heads, ir.hg / P.qgroups, lane);
+      ila = mfma_lanes<D, BS, FP8>(P.num_kv_heads, ir.hg / P.qgroups, lane);
     } else if (ij - ids_base == 64) {  // next chunk of 64 tiles: rotate, fetch the one after
       ids_a = ids_b;
       ids_base += 64;
       ids_b = ids_base + 64 + lane < ir.nb ? tid(ir.s, it0, ids_base + 64 + lane) : 0;
     }
-    mfma_issue<BS>(x.t, pool, ila, __builtin_amdgcn_readlane(ids_a, ij - ids_base), (it0 + ptiles + ij) & SUB,
-                   P.num_blocks);
+    mfma_issue<BS, NT>(x.t, pool, ila, __builtin_amdgcn_readlane(ids_a, ij - ids_base), (it0 + ptiles + ij) & SUB,
+                       P.num_blocks);
     x.j = ij;
     x.row_id = irow_id;
     ++ij;
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
   int c_h0 = head0(cr.hg), c_nh = heads(cr.hg);
   RowSpan crs = row_span(P.seq_lens[cr.s], P.window, P.max_blocks, BS);
   MfmaRow<D> st;
-  st.load_q(q, (size_t)cr.s * P.num_q_heads + c_h0, c_nh, lane);
+  st.template load_q<FP8>(q, (size_t)cr.s * P.num_q_heads + c_h0, c_nh, lane);
   st.reset();
   // queries and length of the next row, fetched ahead
   RowCtx qn = row_after(cr);
@@ -286,9 +286,10 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
   uint4_v q_next[D / 32];
   {
     const int g = lane & 15, nh_n = heads(qn.hg);
-    const uint16_t* qp = q + ((size_t)qn.s * P.num_q_heads + head0(qn.hg) + g) * D + 8 * (lane >> 4);
+    const uint16_t* qp = q + ((size_t)qn.s * P.num_q_heads + head0(qn.hg) + g) * D;
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) q_next[kk] = g < nh_n ? *(const uint4_v*)(qp + 32 * kk) : uint4_v{0, 0, 0, 0};
+    for (int kk = 0; kk < D / 32; ++kk)
+      q_next[kk] = g < nh_n ? *(const uint4_v*)(qp + qk_dim<FP8>(kk, lane >> 4)) : uint4_v{0, 0, 0, 0};
   }
 
   auto finish_row = [&]() {
@@ -379,7 +380,7 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
       const unsigned vc = fp8_quant2(vn, P.inv_v_scale);  // codes of dims 2 lane, +1
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) {
-        const int src = 4 * kk + q4;
+        const int src = qk_dim<true>(kk, q4) >> 3;  // lane holding the codes of MFMA kk's dims
         const uint2_v v = {(unsigned)__shfl((int)kc.x, src), (unsigned)__shfl((int)kc.y, src)};
         if (j == o) t.k[kk] = v;
       }
@@ -404,7 +405,7 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
     } else {
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) {
-        const int src = 4 * kk + q4;  // lane holding dims 32 kk + 8 q4 .. +7
+        const int src = qk_dim<false>(kk, q4) >> 3;  // lane holding dims 32 kk + 8 q4 .. +7
         const uint4_v v = {(unsigned)__shfl((int)kn.x, src), (unsigned)__shfl((int)kn.y, src),
                            (unsigned)__shfl((int)kn.z, src), (unsigned)__shfl((int)kn.w, src)};
         if (j == o) t.k[kk] = v;
@@ -456,9 +457,10 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
       qn = row_after(cr);
       ctx_next = P.seq_lens[qn.s];
       const int g = lane & 15, nh_n = heads(qn.hg);
-      const uint16_t* qp = q + ((size_t)qn.s * P.num_q_heads + head0(qn.hg) + g) * D + 8 * (lane >> 4);
+      const uint16_t* qp = q + ((size_t)qn.s * P.num_q_heads + head0(qn.hg) + g) * D;
 #pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) q_next[kk] = g < nh_n ? *(const uint4_v*)(qp + 32 * kk) : uint4_v{0, 0, 0, 0};
+      for (int kk = 0; kk < D / 32; ++kk)
+        q_next[kk] = g < nh_n ? *(const uint4_v*)(qp + qk_dim<FP8>(kk, lane >> 4)) : uint4_v{0, 0, 0, 0};
       load_new(qn, kn_next, vn_next, slot_next);
     }
     const int J = ptiles + x.j;  // the tile's place in the row span
@@ -617,19 +619,26 @@ hipError_t launch_prefix(const DecodeParams& p, int head_dim, hipStream_t stream
   return launch_prefix_pass(f, head_dim, p.kv_fp8 != 0, stream);
 }
 
+template <int D, int DEPTH, bool FP8, int BS, bool NT>
+void launch_sk(const DecodeParams& p, hipStream_t stream) {
+  if (p.slot_mapping) {
+    // the fused step runs at ring depth 1: the new token takes the registers of a deeper ring
+    hipLaunchKernelGGL((decode_stream_kernel<D, 1, true, FP8, BS, NT>), dim3(p.stream_wgs), dim3(kThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((decode_stream_kernel<D, DEPTH, false, FP8, BS, NT>), dim3(p.stream_wgs), dim3(kThreads), 0, stream,
+                       p);
+  }
+}
+
 template <int D, int DEPTH, bool FP8, int BS>
 hipError_t launch_sd(const DecodeParams& p, hipStream_t stream) {
+  if (p.slot_mapping && DEPTH != 1) return hipErrorInvalidValue;
   if (p.prefix_blocks > 0) {
     const hipError_t e = launch_prefix(p, D, stream);
     if (e != hipSuccess) return e;
   }
-  if (p.slot_mapping) {
-    // the fused step runs at ring depth 1: the new token takes the registers of a deeper ring
-    if constexpr (DEPTH != 1) return hipErrorInvalidValue;
-    else hipLaunchKernelGGL((decode_stream_kernel<D, 1, true, FP8, BS>), dim3(p.stream_wgs), dim3(kThreads), 0, stream, p);
-  } else {
-    hipLaunchKernelGGL((decode_stream_kernel<D, DEPTH, false, FP8, BS>), dim3(p.stream_wgs), dim3(kThreads), 0, stream, p);
-  }
+  if (p.nt_loads) launch_sk<D, DEPTH, FP8, BS, true>(p, stream);
+  else launch_sk<D, DEPTH, FP8, BS, false>(p, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid((p.num_q_heads + 3) / 4, p.num_seqs);
@@ -652,23 +661,24 @@ hipError_t launch_st(const DecodeParams& p, hipStream_t stream) {
   return p.bshift ? launch_s<D, false, 1>(p, stream) : launch_s<D, false, 0>(p, stream);
 }
 
-template <int D, bool FP8, int BS>
+template <int D, bool FP8, int BS, bool NT>
 const void* symbol_of(int depth, bool fused) {
-  if (fused) return depth == 1 ? (const void*)decode_stream_kernel<D, 1, true, FP8, BS> : nullptr;
-  return depth == 1 ? (const void*)decode_stream_kernel<D, 1, false, FP8, BS>
-                    : (const void*)decode_stream_kernel<D, 2, false, FP8, BS>;
+  if (fused) return depth == 1 ? (const void*)decode_stream_kernel<D, 1, true, FP8, BS, NT> : nullptr;
+  return depth == 1 ? (const void*)decode_stream_kernel<D, 1, false, FP8, BS, NT>
+                    : (const void*)decode_stream_kernel<D, 2, false, FP8, BS, NT>;
 }
 
-template <int D>
+template <int D, bool NT>
 const void* symbol_d(int depth, bool fused, bool fp8, int bshift) {
-  if (fp8) return bshift ? symbol_of<D, true, 1>(depth, fused) : symbol_of<D, true, 0>(depth, fused);
-  return bshift ? symbol_of<D, false, 1>(depth, fused) : symbol_of<D, false, 0>(depth, fused);
+  if (fp8) return bshift ? symbol_of<D, true, 1, NT>(depth, fused) : symbol_of<D, true, 0, NT>(depth, fused);
+  return bshift ? symbol_of<D, false, 1, NT>(depth, fused) : symbol_of<D, false, 0, NT>(depth, fused);
 }
 
 }  // namespace
 
-const void* stream_kernel_symbol(int head_dim, int depth, bool fused, bool fp8, int bshift) {
-  return head_dim == 128 ? symbol_d<128>(depth, fused, fp8, bshift) : symbol_d<64>(depth, fused, fp8, bshift);
+const void* stream_kernel_symbol(int head_dim, int depth, bool fused, bool fp8, int bshift, bool nt) {
+  if (nt) return head_dim == 128 ? symbol_d<128, true>(depth, fused, fp8, bshift) : symbol_d<64, true>(depth, fused, fp8, bshift);
+  return head_dim == 128 ? symbol_d<128, false>(depth, fused, fp8, bshift) : symbol_d<64, false>(depth, fused, fp8, bshift);
 }
 
 hipError_t launch_decode_stream(const DecodeParams& p, int head_dim, hipStream_t stream) {

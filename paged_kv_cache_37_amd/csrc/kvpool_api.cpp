@@ -168,10 +168,16 @@ static int32_t stream_workgroups(int32_t head_dim, int32_t depth, bool fused, bo
     return cached_wgs;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kvp::stream_kernel_symbol(head_dim, depth, fused, fp8, bshift),
-                                                   kvp::kThreads, 0) != hipSuccess ||
-      per_cu <= 0)
-    return 0;
+  // the cached-load and non-temporal instances launch the same grid (the
+  // smaller of their occupancies), so one workspace size serves both
+  for (bool nt : {true, false}) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kvp::stream_kernel_symbol(head_dim, depth, fused, fp8, bshift, nt),
+                                                     kvp::kThreads, 0) != hipSuccess ||
+        n <= 0)
+      return 0;
+    per_cu = nt ? n : std::min(per_cu, n);
+  }
   cached_dev = dev;
   cached_d = head_dim;
   cached_depth = depth;
@@ -443,6 +449,7 @@ static int32_t decode(kvp_pool pool, const kvp_decode_args* a, const void* k_new
   p.block_tables = a->block_tables;
   p.seq_lens = a->seq_lens;
   p.window = a->sliding_window;
+  p.nt_loads = path == PATH_STREAM && a->shared_blocks == 0;
   // FP8 codes: K's scale joins the softmax scale, V's the final normalisation
   const bool fp8 = d.dtype == KVP_FP8_E4M3;
   p.kv_fp8 = fp8;

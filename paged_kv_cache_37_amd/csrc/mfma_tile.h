@@ -13,10 +13,17 @@
 // operands of two PV MFMAs (column j of MFMA 2m+e is dimension 32m+2j+e).
 // The accumulator of PV MFMA n, register r, lane l is therefore
 //   O[head 4q + r][dim 32(n/2) + 2(l%16) + n%2].
-// An FP8 pool has the same layout with one-byte E4M3 codes: a lane loads
-// 8 bytes per operand and widens them to the 8 bf16 values above (exact),
-// so the MFMAs are the same; the K scale is folded into the softmax scale
-// and the V scale into the final normalisation by the callers.
+// An FP8 pool has the same layout with one-byte E4M3 codes: a lane widens
+// 8 codes per operand to the 8 bf16 values above (exact), so the MFMAs are
+// the same; the K scale is folded into the softmax scale and the V scale
+// into the final normalisation by the callers.  FP8 K is loaded 16 codes
+// per lane (dims 64 (kk / 2) + 16 q .. +15: the first 8 for QK MFMA kk
+// even, the rest for kk odd), so that every load takes 64-byte runs of
+// the K rows as with bf16; the queries follow the same dim order (qk_dim).
+//
+// Tile loads are ordinary cached loads or non-temporal ones (`nt`): a
+// batch whose blocks each belong to one row reads every line once, and
+// non-temporal loads then stream them past the caches.
 #pragma once
 
 #include <type_traits>
@@ -50,25 +57,40 @@ struct MfmaLanes {
   size_t blk_stride;  // elements per physical block (all heads, K and V)
   size_t k_off;       // this head's K tile inside a block
   size_t v_rel;       // V tile = K tile + v_rel
-  int k_lane;         // this lane's K element offset (+ 32 kk)
+  int k_lane;         // this lane's K element offset (+ 32 kk; FP8: + 64 per 16-code load)
   int v_lane;         // this lane's V element offset (+ 128 m)
 };
 
-template <int D, int BS>  // BS = log2(block size / 16)
+// First of the 8 dims that lanes of row group q supply to QK MFMA kk (the
+// K operand and the query operand alike).
+template <bool FP8>
+__device__ __forceinline__ constexpr int qk_dim(int kk, int q) {
+  return FP8 ? 64 * (kk >> 1) + 16 * q + 8 * (kk & 1) : 32 * kk + 8 * q;
+}
+
+template <int D, int BS, bool FP8>  // BS = log2(block size / 16)
 __device__ __forceinline__ MfmaLanes mfma_lanes(int num_kv_heads, int kvh, int lane) {
   const size_t tile = (size_t)(16 << BS) * D;
   MfmaLanes a;
   a.blk_stride = 2 * (size_t)num_kv_heads * tile;
   a.k_off = (size_t)kvh * tile;
   a.v_rel = (size_t)num_kv_heads * tile;
-  a.k_lane = (lane & 15) * D + 8 * (lane >> 4);
+  a.k_lane = (lane & 15) * D + qk_dim<FP8>(0, lane >> 4);
   a.v_lane = ((lane >> 4) * D + 2 * (lane & 15)) * 4;
   return a;
 }
 
+// A tile load, cached or non-temporal (a compile-time choice: the two
+// forms of one load would otherwise be merged into the cached one).
+template <bool NT, typename T>
+__device__ __forceinline__ T tile_load(const T* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
 // Issue the loads of tile `sub` (< 1 << BS) of physical block `id` (the
 // block id is checked against the pool size here).
-template <int BS, int D, bool FP8>
+template <int BS, bool NT, int D, bool FP8>
 __device__ __forceinline__ void mfma_issue(MfmaTiles<D, FP8>& t, const void* __restrict__ pool, const MfmaLanes& a,
                                            int id, int sub, int num_blocks) {
   using E = std::conditional_t<FP8, uint8_t, uint16_t>;
@@ -76,10 +98,45 @@ __device__ __forceinline__ void mfma_issue(MfmaTiles<D, FP8>& t, const void* __r
   t.bad = (unsigned)id >= (unsigned)num_blocks;
   if (t.bad) id = 0;
   const E* kt = (const E*)pool + (size_t)id * a.blk_stride + (size_t)(BS ? sub : 0) * 16 * D + a.k_off;
+  if constexpr (FP8) {
 #pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk) t.k[kk] = *(const Op*)(kt + a.k_lane + 32 * kk);
+    for (int k2 = 0; k2 < D / 64; ++k2) {
+      const uint4_v c = tile_load<NT>((const uint4_v*)(kt + a.k_lane + 64 * k2));
+      t.k[2 * k2] = uint2_v{c.x, c.y};
+      t.k[2 * k2 + 1] = uint2_v{c.z, c.w};
+    }
+  } else {
 #pragma unroll
-  for (int m = 0; m < D / 32; ++m) t.v[m] = *(const Op*)(kt + a.v_rel + a.v_lane + 128 * m);
+    for (int kk = 0; kk < D / 32; ++kk) t.k[kk] = tile_load<NT>((const Op*)(kt + a.k_lane + 32 * kk));
+  }
+#pragma unroll
+  for (int m = 0; m < D / 32; ++m) t.v[m] = tile_load<NT>((const Op*)(kt + a.v_rel + a.v_lane + 128 * m));
+}
+
+// As many loads as mfma_issue issues, each one dword of the 128 bytes at
+// `hot` (16-byte aligned, a line the wave has just read, so a cache hit):
+// ring slots past the end of a wave's tiles keep the loop's load count
+// without reading a tile again.  Dword loads cannot be merged with the
+// tile loads they stand beside (which would lose the non-temporal hint).
+// Their values are never used.
+template <int D, bool FP8>
+__device__ __forceinline__ void mfma_issue_hot(MfmaTiles<D, FP8>& t, const void* __restrict__ hot) {
+  const unsigned* h = (const unsigned*)hot;
+  if constexpr (FP8) {
+#pragma unroll
+    for (int k2 = 0; k2 < D / 64; ++k2) {
+      t.k[2 * k2] = uint2_v{h[k2], 0u};
+      t.k[2 * k2 + 1] = uint2_v{0u, 0u};
+    }
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) t.v[m] = uint2_v{h[16 + m], 0u};
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) t.k[kk] = uint4_v{h[kk], 0u, 0u, 0u};
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) t.v[m] = uint4_v{h[16 + m], 0u, 0u, 0u};
+  }
+  t.bad = true;
 }
 
 // Running softmax state of one wave for up to 16 query heads of a group.
@@ -97,12 +154,15 @@ struct MfmaRow {
     for (int n = 0; n < D / 16; ++n) acc[n] = float4_v{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Queries of heads h0 .. h0+nh-1 of sequence s (zero for the padding columns).
+  // Queries of heads h0 .. h0+nh-1 of sequence s (zero for the padding
+  // columns), in the dim order of the K operand of an FP8 or bf16 pool.
+  template <bool FP8>
   __device__ __forceinline__ void load_q(const uint16_t* __restrict__ q, size_t row_base, int nh, int lane) {
     const int g = lane & 15;
-    const uint16_t* qp = q + (row_base + g) * D + 8 * (lane >> 4);
+    const uint16_t* qp = q + (row_base + g) * D;
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) qop[kk] = g < nh ? *(const uint4_v*)(qp + 32 * kk) : uint4_v{0, 0, 0, 0};
+    for (int kk = 0; kk < D / 32; ++kk)
+      qop[kk] = g < nh ? *(const uint4_v*)(qp + qk_dim<FP8>(kk, lane >> 4)) : uint4_v{0, 0, 0, 0};
   }
 
   // One tile: tile J of a row span whose attended slots are [so, send)

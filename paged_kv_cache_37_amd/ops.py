@@ -163,7 +163,7 @@ def make_workspace(pool: KVPool, num_seqs: int, num_q_heads: int, max_blocks_per
 
 def _decode_args(pool: KVPool, layer: int, q: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
                  scale: float, out: Optional[torch.Tensor], sliding_window: int, partition_tokens: int, variant: str,
-                 workspace: Optional[torch.Tensor], shared_prefix_blocks: int = 0):
+                 workspace: Optional[torch.Tensor], shared_prefix_blocks: int = 0, shared_blocks: bool = False):
     if q.dim() != 3:
         raise ValueError("q must be [num_seqs, num_q_heads, head_dim]")
     S, Hq, D = q.shape
@@ -192,6 +192,7 @@ def _decode_args(pool: KVPool, layer: int, q: torch.Tensor, block_tables: torch.
         workspace=workspace.data_ptr() if workspace is not None else None,
         workspace_bytes=workspace.numel() * workspace.element_size() if workspace is not None else 0,
         shared_prefix_blocks=shared_prefix_blocks,
+        shared_blocks=1 if shared_blocks else 0,
     )
     return args, out
 
@@ -201,13 +202,15 @@ def paged_decode_attention(pool: KVPool, layer: int, q: torch.Tensor, block_tabl
                            sliding_window: int = 0, partition_tokens: int = 0, variant: str = "auto",
                            workspace: Optional[torch.Tensor] = None,
                            stream: Optional[torch.cuda.Stream] = None,
-                           shared_prefix_blocks: int = 0) -> torch.Tensor:
+                           shared_prefix_blocks: int = 0, shared_blocks: bool = False) -> torch.Tensor:
     """Decode attention of q [S, Hq, D] over the pool through block_tables
     [S, max_blocks] and seq_lens [S]; returns out [S, Hq, D].  With
     shared_prefix_blocks = P > 0 the first P entries of every row must be
-    the same full blocks: the prefix is attended once for all sequences."""
+    the same full blocks: the prefix is attended once for all sequences.
+    shared_blocks: some block past that prefix is listed by several rows
+    (tiles are then read with cached loads; the result is the same)."""
     args, out = _decode_args(pool, layer, q, block_tables, seq_lens, scale, out, sliding_window, partition_tokens,
-                             variant, workspace, shared_prefix_blocks)
+                             variant, workspace, shared_prefix_blocks, shared_blocks)
     check(lib.paged_decode_attention(pool.handle, ctypes.byref(args), _stream(pool.device, stream)),
           "paged_decode_attention")
     return out
@@ -217,12 +220,13 @@ def paged_decode_step(pool: KVPool, layer: int, q: torch.Tensor, block_tables: t
                       seq_lens: torch.Tensor, scale: float, k_new: torch.Tensor, v_new: torch.Tensor,
                       slot_mapping: torch.Tensor, out: Optional[torch.Tensor] = None, sliding_window: int = 0,
                       partition_tokens: int = 0, variant: str = "auto", workspace: Optional[torch.Tensor] = None,
-                      stream: Optional[torch.cuda.Stream] = None, shared_prefix_blocks: int = 0) -> torch.Tensor:
+                      stream: Optional[torch.cuda.Stream] = None, shared_prefix_blocks: int = 0,
+                      shared_blocks: bool = False) -> torch.Tensor:
     """Store each sequence's new token (k_new/v_new [S, Hkv, D] at
     slot_mapping [S], the slot of position seq_lens[s]-1) and attend with it;
     the same result as cache_write followed by paged_decode_attention."""
     args, out = _decode_args(pool, layer, q, block_tables, seq_lens, scale, out, sliding_window, partition_tokens,
-                             variant, workspace, shared_prefix_blocks)
+                             variant, workspace, shared_prefix_blocks, shared_blocks)
     shape = (q.shape[0], pool.num_kv_heads, pool.head_dim)
     _need(k_new, "k_new", pool.act_dtype, pool.device, shape)
     _need(v_new, "v_new", pool.act_dtype, pool.device, shape)

@@ -68,10 +68,13 @@ def test_cascade_shapes(gpu, prefix, Hq, Hkv, D):
     assert shared_prefix_blocks(np.asarray(w.block_tables), w.seq_lens) == P
     dev = Dev(w)
     out_c = dev.attend(shared_prefix_blocks=P)
-    out_p = dev.attend()
+    out_p = dev.attend(shared_blocks=True)  # every row lists the prefix: cached tile loads
     ref = reference(w)
     compare(out_c, ref, "bf16", f"cascade prefix {prefix} G {Hq // Hkv} D {D}")
     close_to_plain(out_c, out_p, ref, f"prefix {prefix}")
+    # the hint changes no bit: the tails without it, and the whole rows with or without it
+    assert torch.equal(out_c.view(torch.int16), dev.attend(shared_prefix_blocks=P, shared_blocks=True).view(torch.int16))
+    assert torch.equal(out_p.view(torch.int16), dev.attend().view(torch.int16))
 
 
 @pytest.mark.parametrize("prefix,Hq,Hkv,D", [(2048, 32, 8, 128), (256, 8, 2, 64)])

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_helpers import Dev, compare, host_to_torch, reference, say, to_f64, torch_to_bits
+from gpu_helpers import Dev, compare, host_to_torch, reference, say, to_f64, torch_dtype, torch_to_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -431,3 +431,37 @@ def test_workspace_is_reusable(gpu):
     for variant in ("mfma", "valu", "stream", "mfma", "stream"):
         out = dev.attend(variant=variant, partition_tokens=128 if variant != "stream" else 0, workspace=ws)
         compare(out, ref, "bf16", f"reuse/{variant}")
+
+
+@pytest.mark.parametrize("dtype,B,D,window", [("bf16", 16, 128, 0), ("fp8", 16, 128, 0), ("bf16", 32, 64, 0),
+                                              ("fp8", 32, 128, 40), ("bf16", 16, 128, 33), ("fp8", 16, 64, 0)])
+def test_shared_blocks_hint_changes_no_bit(gpu, dtype, B, D, window):
+    """The streaming kernel reads tiles with non-temporal loads by default
+    and with cached loads under the shared_blocks hint; the outputs are the
+    same bits, for attention and for the fused step (pool included), and
+    match the oracle."""
+    lens = [0, 1, 15, 16, 17, 31, 33, 100, 257, 700, 1500, 2048]
+    w = W.custom(7100 + B + D + window, lens, num_q_heads=8, num_kv_heads=2, head_dim=D, dtype=dtype, window=window,
+                 block_size=B, extra_blocks=len(lens))
+    say("shared_blocks hint", dtype, B, D, window)
+    devs = [Dev(w), Dev(w)]
+    outs = [d.attend(variant="stream", shared_blocks=hint) for d, hint in zip(devs, (False, True))]
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    compare(outs[0], reference(w), "bf16", f"stream {dtype} B{B} D{D} w{window}")
+    W.with_next_token(w, w.unused_blocks)
+    dt = torch_dtype(w)
+    steps = []
+    for d, hint in zip(devs, (False, True)):
+        steps.append(d.ops.paged_decode_step(d.pool, 0, d.q, torch.from_numpy(np.ascontiguousarray(w.block_tables_after)).cuda(),
+                                             torch.from_numpy(w.seq_lens_after).cuda(), w.scale,
+                                             host_to_torch(w.k_new, dt).cuda(), host_to_torch(w.v_new, dt).cuda(),
+                                             torch.from_numpy(w.slot_mapping).cuda(), sliding_window=w.window,
+                                             shared_blocks=hint))
+    torch.cuda.synchronize()
+    assert torch.equal(steps[0].view(torch.int16), steps[1].view(torch.int16))
+    pools = [torch_to_bits(d.pool.to_logical()) for d in devs]
+    assert pools[0].tobytes() == pools[1].tobytes()
+    pool_ref = oracle.cache_write(w.pool, 0, w.k_new, w.v_new, w.slot_mapping, w.k_scale, w.v_scale)
+    assert pools[0].tobytes() == np.ascontiguousarray(pool_ref).tobytes()
+    compare(steps[0], reference(w, pool=pool_ref, tables=w.block_tables_after, lens=w.seq_lens_after), "bf16",
+            f"step {dtype} B{B} D{D} w{window}")
