@@ -247,3 +247,38 @@ def test_prefill_rejects_bad_arguments_before_launch(ops):
     assert ops.lib.paged_prefill_step(h, ctypes.byref(a), None, 0x7000, 0x8000, None) == E.KVP_ERR_INVALID_ARG
     ops.lib.kv_pool_destroy(h)
     ops.lib.kv_pool_destroy(h32)
+
+
+def test_struct_layouts_match_the_header(ops, tmp_path):
+    """The ctypes mirrors of the header's argument structs have the C
+    compiler's sizes and field offsets (a small C program built against
+    include/kvpool.h prints them)."""
+    import shutil
+    import subprocess
+
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    structs = {"kvp_pool_desc": ops._lib.PoolDesc, "kvp_decode_args": ops.DecodeArgs,
+               "kvp_prefill_args": ops._lib.PrefillArgs}
+    lines = ["#include <stddef.h>", "#include <stdio.h>", '#include "kvpool.h"', "int main(void) {"]
+    for name, cls in structs.items():
+        lines.append(f'  printf("{name} size %zu\\n", sizeof({name}));')
+        for f, _ in cls._fields_:
+            lines.append(f'  printf("{name} {f} %zu\\n", offsetof({name}, {f}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    hip_inc = os.environ.get("ROCM_PATH", "/opt/rocm") + "/include"
+    subprocess.run([cc, "-std=c11", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(root, "include"), "-I", hip_inc,
+                    str(src), "-o", str(exe)], check=True, capture_output=True)
+    got = {}
+    for line in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.splitlines():
+        name, field, value = line.split()
+        got[(name, field)] = int(value)
+    for name, cls in structs.items():
+        assert got[(name, "size")] == ctypes.sizeof(cls), name
+        for f, _ in cls._fields_:
+            assert got[(name, f)] == getattr(cls, f).offset, (name, f)
