@@ -19,7 +19,9 @@
 //
 // Ranges are contiguous per XCD (workgroup i runs on XCD i mod 8): the
 // tiles of one head group, which share physical blocks across sequences
-// with a common prefix, stay in one XCD's L2.
+// with a common prefix, stay in one XCD's L2.  Tiles are read with
+// non-temporal loads (NT) when no block is listed by two rows, each line
+// then being read once, and with cached loads when rows share blocks.
 #include "mfma_tile.h"
 
 namespace kvp {
