@@ -465,3 +465,46 @@ def test_shared_blocks_hint_changes_no_bit(gpu, dtype, B, D, window):
     assert pools[0].tobytes() == np.ascontiguousarray(pool_ref).tobytes()
     compare(steps[0], reference(w, pool=pool_ref, tables=w.block_tables_after, lens=w.seq_lens_after), "bf16",
             f"step {dtype} B{B} D{D} w{window}")
+
+
+@pytest.mark.parametrize("dtype,B,D", [("bf16", 16, 128), ("bf16", 32, 64), ("f32", 16, 64), ("fp8", 16, 128),
+                                       ("fp8", 32, 128)])
+def test_cache_write_slot_patterns(gpu, dtype, B, D):
+    """Token groups of four that fill one V quad in order are written as one
+    transposed store per dimension, every other pattern token by token: a
+    batch mixing whole quads, quads cut by padding or by the pool's end,
+    shifted, reversed and partly repeated groups, and a ragged tail, written
+    bit-exact against the oracle's scatter."""
+    rng = np.random.default_rng(7400 + B + D)
+    w = W.custom(7400 + B + D, [B * 6], num_q_heads=4, num_kv_heads=2, head_dim=D, dtype=dtype, block_size=B,
+                 pool_factor=3.0)
+    NS = w.num_blocks * B
+    b0, b1, b2 = (int(x) * B for x in w.unused_blocks[:3])
+    last = NS - 4  # the pool's last quad
+    groups = [
+        [b0, b0 + 1, b0 + 2, b0 + 3],                # whole quad
+        [b0 + 4, b0 + 5, b0 + 6, b0 + 7],            # the next one
+        [b0 + 8, b0 + 9, -1, b0 + 11],               # padding inside
+        [b0 + 13, b0 + 14, b0 + 15, b2 + 8],        # shifted by one
+        [b1 + 7, b1 + 6, b1 + 5, b1 + 4],            # reversed
+        [b1, b1 + 1, b1 + 2, NS + 2],                # last slot outside the pool
+        [last, last + 1, last + 2, last + 3],        # the pool's last quad
+        [b2 + B - 4, b2 + B - 3, b2 + B - 2, b2 + B - 1],  # a block's last quad
+        [b2, b2 + 1, b2 + 2],                        # ragged tail: three tokens
+    ]
+    slots = np.array([s for g in groups for s in g], dtype=np.int32)
+    T = len(slots)
+    say("cache_write slot patterns", dtype, B, D, T)
+    shape = (T, w.num_kv_heads, D)
+    if dtype == "f32":
+        k, v = rng.standard_normal(shape).astype(np.float32), rng.standard_normal(shape).astype(np.float32)
+    else:
+        k, v = W.f32_to_bf16_bits(rng.standard_normal(shape)), W.f32_to_bf16_bits(rng.standard_normal(shape))
+    dev = Dev(w)
+    dt = torch_dtype(w)
+    dev.ops.cache_write(dev.pool, 0, host_to_torch(k, dt).cuda(), host_to_torch(v, dt).cuda(),
+                        torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    keep = (slots >= 0) & (slots < NS)
+    expect = oracle.cache_write(w.pool, 0, k[keep], v[keep], slots[keep], w.k_scale, w.v_scale)
+    assert torch_to_bits(dev.pool.to_logical()).tobytes() == np.ascontiguousarray(expect).tobytes()
