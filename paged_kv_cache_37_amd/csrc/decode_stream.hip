@@ -486,7 +486,9 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
 #pragma unroll
     for (int u = 0; u < NBUF; ++u) {
       if (k0 + u >= n_tiles) break;
+      __builtin_amdgcn_s_setprio(1);  // the next tile's loads go out ahead of the other wave's compute
       issue(buf[(u + DEPTH) % NBUF]);
+      __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
       compute(buf[u]);
     }
