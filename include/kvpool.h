@@ -274,8 +274,8 @@ int32_t paged_decode_attention(kvp_pool pool, const kvp_decode_args* args, hipSt
  *   not hold the outputs are unspecified (memory is still only read inside
  *   the pool and the table rows).
  *
- *   Blocks read by several rows.  By default the STREAM variant reads the
- *   K/V tiles with non-temporal loads: when every block of the batch is
+ *   Blocks read by several rows.  By default the STREAM and MFMA variants
+ *   read the K/V tiles with non-temporal loads: when every block of the batch is
  *   listed by one row only (the case without sharing, and the private
  *   tails of a cascade), each line is read once and streaming it past the
  *   caches is faster.  Rows may also share blocks outside the prefix
@@ -284,8 +284,8 @@ int32_t paged_decode_attention(kvp_pool pool, const kvp_decode_args* args, hipSt
  *   same physical blocks until they write to them; the host's reference
  *   counts show it).  shared_blocks != 0 says so: tiles are then read with
  *   ordinary cached loads, and rows that share a block find it in the L2
- *   cache.  The hint changes no output bit, only speed; the other variants
- *   always use cached loads.
+ *   cache.  The hint changes no output bit, only speed; the VALU variant
+ *   always uses cached loads.
  */
 
 /*

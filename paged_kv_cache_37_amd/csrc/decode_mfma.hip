@@ -11,7 +11,9 @@
 // mfma_tile.h (S^T = K Q^T for the whole query-head group, online softmax,
 // O += P V).  The waves' (max, sum, O) merge in LDS; a row held by one
 // partition is normalised and stored at once, otherwise its partial result
-// goes to the workspace for decode_reduce.
+// goes to the workspace for decode_reduce.  Tiles are read with
+// non-temporal loads (NT) when no block is listed by two rows, each line
+// then being read once, and with cached loads when rows share blocks.
 #include "mfma_tile.h"
 
 namespace kvp {
@@ -22,7 +24,7 @@ namespace {
 #define KVP_MFMA_WAVES_PER_EU 2
 #endif
 
-template <int D, int DEPTH, bool FP8, int BS>  // BS = log2(block size / 16)
+template <int D, int DEPTH, bool FP8, int BS, bool NT>  // BS = log2(block size / 16)
 __global__ __launch_bounds__(kThreads, KVP_MFMA_WAVES_PER_EU) void decode_mfma_kernel(const DecodeParams P) {
   constexpr int NBUF = DEPTH + 1;
   __shared__ float o_s[kWaves][16][D + 1];
@@ -76,9 +78,12 @@ __global__ __launch_bounds__(kThreads, KVP_MFMA_WAVES_PER_EU) void decode_mfma_k
   // Tiles of this wave: wave, wave + 4, ...; `cnt` of them.
   const int cnt = nbp > wave ? (nbp - wave + kWaves - 1) / kWaves : 0;
   auto issue = [&](int k, MfmaTiles<D, FP8>& t) {
-    const int kc = k < cnt ? k : cnt - 1;  // past the end: re-read the last block (a cache hit)
-    mfma_issue<BS, false>(t, pool, la, __builtin_amdgcn_readlane(my_id, wave + kc * kWaves),
-                          (t0 + jb + wave + kc * kWaves) & ((1 << BS) - 1), P.num_blocks);
+    if (k >= cnt) {  // past the end: loads of a line just read (this row's queries)
+      mfma_issue_hot(t, (const uint16_t*)P.q + ((size_t)s * P.num_q_heads + h0) * D);
+      return;
+    }
+    mfma_issue<BS, NT>(t, pool, la, __builtin_amdgcn_readlane(my_id, wave + k * kWaves),
+                       (t0 + jb + wave + k * kWaves) & ((1 << BS) - 1), P.num_blocks);
   };
 
   // Software pipeline: the loads of block k + DEPTH are issued before block k
@@ -117,23 +122,28 @@ __global__ __launch_bounds__(kThreads, KVP_MFMA_WAVES_PER_EU) void decode_mfma_k
   finish_partition<uint16_t, D, 16>(P, o_s, m_s, l_s, s, h0, nh, part, nparts);
 }
 
-template <int D, bool FP8, int BS>
+template <int D, bool FP8, int BS, bool NT>
 hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid(p.num_kv_heads * p.qgroups, p.num_seqs, p.num_parts);
   const dim3 block(kThreads);
   switch (p.depth) {
-    case 1: hipLaunchKernelGGL((decode_mfma_kernel<D, 1, FP8, BS>), grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((decode_mfma_kernel<D, 2, FP8, BS>), grid, block, 0, stream, p); break;
-    case 3: hipLaunchKernelGGL((decode_mfma_kernel<D, 3, FP8, BS>), grid, block, 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((decode_mfma_kernel<D, 1, FP8, BS, NT>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((decode_mfma_kernel<D, 2, FP8, BS, NT>), grid, block, 0, stream, p); break;
+    case 3: hipLaunchKernelGGL((decode_mfma_kernel<D, 3, FP8, BS, NT>), grid, block, 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+template <int D, bool NT>
+hipError_t launch_dn(const DecodeParams& p, hipStream_t stream) {
+  if (p.kv_fp8) return p.bshift ? launch_d<D, true, 1, NT>(p, stream) : launch_d<D, true, 0, NT>(p, stream);
+  return p.bshift ? launch_d<D, false, 1, NT>(p, stream) : launch_d<D, false, 0, NT>(p, stream);
+}
+
 template <int D>
 hipError_t launch_dt(const DecodeParams& p, hipStream_t stream) {
-  if (p.kv_fp8) return p.bshift ? launch_d<D, true, 1>(p, stream) : launch_d<D, true, 0>(p, stream);
-  return p.bshift ? launch_d<D, false, 1>(p, stream) : launch_d<D, false, 0>(p, stream);
+  return p.nt_loads ? launch_dn<D, true>(p, stream) : launch_dn<D, false>(p, stream);
 }
 
 }  // namespace

@@ -49,7 +49,7 @@ struct DecodeParams {
   float* pre_ml;                // [pieces][S][Hq][2] prefix pass: (max, sum)          (cascade only)
   float* row_o;                 // [rows][heads_per_wg][D] tails held whole by a wave  (cascade only)
   float* row_ml;                // [rows][heads_per_wg][2]                             (cascade only)
-  int32_t nt_loads;             // tiles read with non-temporal loads (no block read by two rows)  (streaming only)
+  int32_t nt_loads;             // tiles read with non-temporal loads (no block read by two rows)  (matrix-core kernels)
   int32_t kv_fp8;               // the pool holds E4M3 codes (K scale folded into scale_log2)
   float v_scale;                // multiplies every output (FP8 V codes); 1 otherwise
   float inv_k_scale;            // 1 / k_scale, 1 / v_scale: quantizing the fused write's new token

@@ -449,7 +449,7 @@ static int32_t decode(kvp_pool pool, const kvp_decode_args* a, const void* k_new
   p.block_tables = a->block_tables;
   p.seq_lens = a->seq_lens;
   p.window = a->sliding_window;
-  p.nt_loads = path == PATH_STREAM && a->shared_blocks == 0;
+  p.nt_loads = path != PATH_VALU && a->shared_blocks == 0;
   // FP8 codes: K's scale joins the softmax scale, V's the final normalisation
   const bool fp8 = d.dtype == KVP_FP8_E4M3;
   p.kv_fp8 = fp8;

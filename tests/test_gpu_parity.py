@@ -448,6 +448,10 @@ def test_shared_blocks_hint_changes_no_bit(gpu, dtype, B, D, window):
     outs = [d.attend(variant="stream", shared_blocks=hint) for d, hint in zip(devs, (False, True))]
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
     compare(outs[0], reference(w), "bf16", f"stream {dtype} B{B} D{D} w{window}")
+    # the partitioned kernel (split into 256-token partitions) likewise
+    parts = [d.attend(variant="mfma", partition_tokens=256, shared_blocks=hint) for d, hint in zip(devs, (False, True))]
+    assert torch.equal(parts[0].view(torch.int16), parts[1].view(torch.int16))
+    compare(parts[0], reference(w), "bf16", f"mfma {dtype} B{B} D{D} w{window}")
     W.with_next_token(w, w.unused_blocks)
     dt = torch_dtype(w)
     steps = []
