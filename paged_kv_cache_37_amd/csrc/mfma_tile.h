@@ -21,9 +21,9 @@
 // even, the rest for kk odd), so that every load takes 64-byte runs of
 // the K rows as with bf16; the queries follow the same dim order (qk_dim).
 //
-// Tile loads are ordinary cached loads or non-temporal ones (`nt`): a
-// batch whose blocks each belong to one row reads every line once, and
-// non-temporal loads then stream them past the caches.
+// Tile loads are ordinary cached loads or non-temporal ones (mfma_issue's
+// NT): a batch whose blocks each belong to one row reads every line once,
+// and non-temporal loads then stream them past the caches.
 #pragma once
 
 #include <type_traits>
