@@ -460,7 +460,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
       }
       const int buf = (k - k_lo) & 1;
       const bool more = k < k_hi;
-      if (more) fetch(k + 1);
+      if (more) {  // the next step's loads go out at a raised priority, ahead of the other waves' softmax
+        __builtin_amdgcn_s_setprio(1);
+        fetch(k + 1);
+        __builtin_amdgcn_s_setprio(0);
+      }
 #pragma unroll
       for (int h = 0; h < kTiles / 2; ++h) {
         const int u0 = k * kStep + 32 * h;  // span slot of the round's first key
