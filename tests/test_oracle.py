@@ -21,6 +21,7 @@ import torch
 import oracle
 import oracle.paged as op
 import workloads as W
+from indep import widen
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -41,8 +42,8 @@ def independent_gather(pool, layer, table_row, ctx, window):
     row = np.asarray(table_row)
     blocks = row[pos // B - first // B]
     offs = pos % B
-    K = op.to_f64(pool[layer, blocks, 0, offs])
-    V = op.to_f64(pool[layer, blocks, 1, offs])
+    K = widen(pool[layer, blocks, 0, offs])
+    V = widen(pool[layer, blocks, 1, offs])
     return K, V
 
 
@@ -55,7 +56,7 @@ def sdpa_reference(w_pool, layer, q, tables, seq_lens, window, scale):
         K, V = independent_gather(w_pool, layer, tables[s], int(seq_lens[s]), window)
         if K.shape[0] == 0:
             continue
-        qt = torch.from_numpy(op.to_f64(q[s])).reshape(1, Hq, 1, D)
+        qt = torch.from_numpy(widen(q[s])).reshape(1, Hq, 1, D)
         kt = torch.from_numpy(K).permute(1, 0, 2).repeat_interleave(G, dim=0).unsqueeze(0).contiguous()
         vt = torch.from_numpy(V).permute(1, 0, 2).repeat_interleave(G, dim=0).unsqueeze(0).contiguous()
         o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale)
@@ -69,15 +70,32 @@ def load_golden_attention():
 
 
 def build_case(case):
+    """Pool, queries, tables and lengths of a golden case.  A case with
+    "storage": "bf16" gives every element as a bf16 bit pattern ("0x3F80")
+    and is built as uint16 arrays, the form the oracle takes for bf16."""
     B, NB = case["block_size"], case["num_blocks"]
     Hq, Hkv, D = case["num_q_heads"], case["num_kv_heads"], case["head_dim"]
     Wn = case["window"]
-    pool = np.full((1, NB, 2, B, Hkv, D), np.nan, dtype=np.float32)
+    bf16 = case.get("storage") == "bf16"
+    if bf16:
+        elt = np.uint16
+
+        def conv(v):
+            return np.vectorize(lambda h: int(h, 16), otypes=[np.uint16])(np.asarray(v))
+
+        pool = np.full((1, NB, 2, B, Hkv, D), 0x7FC0, dtype=np.uint16)  # NaN in unused slots
+    else:
+        elt = np.float32
+
+        def conv(v):
+            return np.asarray(v, dtype=np.float32)
+
+        pool = np.full((1, NB, 2, B, Hkv, D), np.nan, dtype=np.float32)
     seqs = case["seqs"]
     width = max(len(s["table"]) for s in seqs)
     tables = np.zeros((len(seqs), width), dtype=np.int32)
     ctxs = np.array([s["ctx"] for s in seqs], dtype=np.int32)
-    q = np.array([s["q"] for s in seqs], dtype=np.float32)
+    q = np.stack([conv(s["q"]) for s in seqs]).astype(elt)
     for si, s in enumerate(seqs):
         tables[si, : len(s["table"])] = s["table"]
         ctx = s["ctx"]
@@ -93,10 +111,10 @@ def build_case(case):
                 continue
             key = s.get("keys", {}).get(str(i), fill.get("key"))
             value = s.get("values", {}).get(str(i), fill.get("value"))
-            if value == "position":
+            if isinstance(value, str) and value == "position":
                 value = np.full((Hkv, D), float(i))
-            pool[0, blk, 0, off] = np.asarray(key, dtype=np.float32)
-            pool[0, blk, 1, off] = np.asarray(value, dtype=np.float32)
+            pool[0, blk, 0, off] = conv(key)
+            pool[0, blk, 1, off] = conv(value)
     return pool, q, tables, ctxs
 
 
@@ -199,7 +217,7 @@ def test_single_key_returns_its_value():
     for s in range(w.num_seqs):
         blk = w.block_tables[s, 0]
         for h in range(w.num_q_heads):
-            assert np.array_equal(out[s, h], op.to_f64(w.pool[0, blk, 1, 0, h // G]))
+            assert np.array_equal(out[s, h], widen(w.pool[0, blk, 1, 0, h // G]))
 
 
 def test_zero_query_gives_mean_value():
@@ -237,7 +255,7 @@ def test_needle_selects_one_value():
             pool[0, blk, 0, off, kv, (2 * kv + g) % w.head_dim] = 32.0
     out = oracle.decode_attention(pool, 0, q, w.block_tables, w.seq_lens, 0, 1.0)
     for h in range(w.num_q_heads):
-        np.testing.assert_allclose(out[0, h], op.to_f64(pool[0, blk, 1, off, h // 2]), rtol=0, atol=1e-300)
+        np.testing.assert_allclose(out[0, h], widen(pool[0, blk, 1, off, h // 2]), rtol=0, atol=1e-300)
 
 
 # ---------------------------------------------------------------------------
@@ -300,7 +318,7 @@ def test_softmax_rows_sum_to_one():
     for s in range(w.num_seqs):
         K, _ = oracle.gather_kv(w.pool, 0, w.block_tables[s], 0, int(w.seq_lens[s]))
         for h in range(w.num_q_heads):
-            p = oracle.softmax_weights(op.to_f64(w.q[s, h]), K[:, h // G], w.scale)
+            p = oracle.softmax_weights(widen(w.q[s, h]), K[:, h // G], w.scale)
             assert abs(p.sum() - 1.0) <= 1e-15
             assert np.all(p >= 0)
 
@@ -381,9 +399,9 @@ def test_cache_write_then_attend_matches_contiguous():
     G = Hq // w.num_kv_heads
     for s in range(w.num_seqs):
         K, V = independent_gather(w.pool, 0, w.block_tables[s], int(w.seq_lens[s]), 0)
-        K = np.concatenate([K, op.to_f64(w.k_new[s])[None]], axis=0)
-        V = np.concatenate([V, op.to_f64(w.v_new[s])[None]], axis=0)
-        qt = torch.from_numpy(op.to_f64(w.q[s])).reshape(1, Hq, 1, D)
+        K = np.concatenate([K, widen(w.k_new[s])[None]], axis=0)
+        V = np.concatenate([V, widen(w.v_new[s])[None]], axis=0)
+        qt = torch.from_numpy(widen(w.q[s])).reshape(1, Hq, 1, D)
         kt = torch.from_numpy(K).permute(1, 0, 2).repeat_interleave(G, 0).unsqueeze(0).contiguous()
         vt = torch.from_numpy(V).permute(1, 0, 2).repeat_interleave(G, 0).unsqueeze(0).contiguous()
         ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=w.scale)
@@ -437,9 +455,9 @@ def test_copy_on_write_then_append_matches_private_history():
     for s, (K, V) in enumerate([
             (np.concatenate([hist[0], k_new]), np.concatenate([hist[1], v_new])),
             (hist[0], hist[1])]):
-        qt = torch.from_numpy(op.to_f64(q[s])).reshape(1, Hq, 1, D)
-        kt = torch.from_numpy(op.to_f64(K)).permute(1, 0, 2).repeat_interleave(G, 0).unsqueeze(0).contiguous()
-        vt = torch.from_numpy(op.to_f64(V)).permute(1, 0, 2).repeat_interleave(G, 0).unsqueeze(0).contiguous()
+        qt = torch.from_numpy(widen(q[s])).reshape(1, Hq, 1, D)
+        kt = torch.from_numpy(widen(K)).permute(1, 0, 2).repeat_interleave(G, 0).unsqueeze(0).contiguous()
+        vt = torch.from_numpy(widen(V)).permute(1, 0, 2).repeat_interleave(G, 0).unsqueeze(0).contiguous()
         ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=0.5)
         np.testing.assert_allclose(out[s], ref.reshape(Hq, D).numpy(), rtol=0, atol=1e-12)
     # the shared block itself is untouched
@@ -511,6 +529,61 @@ def test_pins_pass_for_the_oracle():
                                   "head_modulo", "no_scale", "flip_sign", "no_normalise"])
 def test_planted_mistake_is_caught(kind):
     assert not _independent_pins_pass(_mutant(kind))
+
+
+# ---------------------------------------------------------------------------
+# the oracle's widening of stored elements, against torch's own dtypes
+
+
+def test_bf16_widening_of_every_pattern():
+    """All 65,536 bf16 bit patterns widen to the float64 value torch gives
+    the same bits as a torch.bfloat16 (NaN patterns to NaN)."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):  # signalling-NaN patterns stay NaN when widened
+        got = op.to_f64(bits)
+    want = widen(bits)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))  # -0.0 stays negative
+
+
+def test_e4m3_widening_of_every_code():
+    """All 256 E4M3 codes widen to the value torch gives them as
+    torch.float8_e4m3fn (the OCP format with no infinities)."""
+    codes = np.arange(256, dtype=np.uint8)
+    got, want = op.to_f64(codes), widen(codes)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2  # S.1111.111
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def _widen_mutant(kind):
+    real = op.to_f64
+
+    def to_f64(x):
+        x = np.asarray(x)
+        if x.dtype != np.uint16:
+            return real(x)
+        if kind == "shift_15":
+            return (x.astype(np.uint32) << 15).view(np.float32).astype(np.float64)
+        if kind == "as_fp16":
+            return x.view(np.float16).astype(np.float64)
+        if kind == "bytes_swapped":
+            return real(x.byteswap())
+        raise ValueError(kind)
+
+    return to_f64
+
+
+@pytest.mark.parametrize("kind", ["shift_15", "as_fp16", "bytes_swapped"])
+def test_planted_widening_mistake_is_caught(kind, monkeypatch):
+    """A slip in how the oracle reads bf16 bits must fail a pin that reads
+    them another way: the golden bf16-pattern case and the SDPA
+    cross-check, whose gather widens through torch."""
+    monkeypatch.setattr(op, "to_f64", _widen_mutant(kind))
+    assert not _independent_pins_pass(oracle.decode_attention)
 
 
 # ---------------------------------------------------------------------------

@@ -8,8 +8,8 @@ import pytest
 import torch
 
 import oracle
-import oracle.paged as op
 import workloads as W
+from indep import widen
 
 
 def gather_positions(w, s, positions):
@@ -21,7 +21,7 @@ def gather_positions(w, s, positions):
     first = max(0, p0 + 1 - w.window) if w.window > 0 else 0
     pos = np.asarray(positions)
     blocks = np.asarray(w.block_tables[s])[pos // B - first // B]
-    return op.to_f64(w.pool[0, blocks, 0, pos % B]), op.to_f64(w.pool[0, blocks, 1, pos % B])
+    return widen(w.pool[0, blocks, 0, pos % B]), widen(w.pool[0, blocks, 1, pos % B])
 
 
 def sdpa_causal(w):
@@ -40,7 +40,7 @@ def sdpa_causal(w):
         keys = np.arange(lo.min(), ctx)
         K, V = gather_positions(w, s, keys)
         mask = (keys[None, :] >= lo[:, None]) & (keys[None, :] <= p[:, None])
-        qt = torch.from_numpy(op.to_f64(w.q[a:b])).permute(1, 0, 2).unsqueeze(0)          # [1, Hq, q, D]
+        qt = torch.from_numpy(widen(w.q[a:b])).permute(1, 0, 2).unsqueeze(0)          # [1, Hq, q, D]
         kt = torch.from_numpy(K).permute(1, 0, 2).repeat_interleave(G, 0).unsqueeze(0).contiguous()
         vt = torch.from_numpy(V).permute(1, 0, 2).repeat_interleave(G, 0).unsqueeze(0).contiguous()
         o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(mask),
@@ -97,7 +97,7 @@ def test_prefill_closed_forms():
     out = run(w)
     G = 2
     for s in range(2):
-        V0 = op.to_f64(w.pool[0, w.block_tables[s][0], 1, 0])
+        V0 = widen(w.pool[0, w.block_tables[s][0], 1, 0])
         for h in range(4):
             assert np.array_equal(out[w.cu_q_lens[s], h], V0[h // G])
     pool = w.pool.copy()
@@ -146,7 +146,7 @@ def test_planted_prefill_mistake_is_caught(kind):
                 continue
             K, V = gather_positions(w, s, np.arange(lo, hi + 1))
             for h in range(Hq):
-                z = K[:, h // 2] @ op.to_f64(w.q[w.cu_q_lens[s] + i, h]) * w.scale
+                z = K[:, h // 2] @ widen(w.q[w.cu_q_lens[s] + i, h]) * w.scale
                 e = np.exp(z - z.max())
                 out[w.cu_q_lens[s] + i, h] = e @ V[:, h // 2] / e.sum()
     assert not np.allclose(out, ref, rtol=0, atol=1e-9)
