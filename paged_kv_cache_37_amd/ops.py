@@ -20,9 +20,12 @@ _VARIANTS = {"auto": _lib.KVP_VARIANT_AUTO, "valu": _lib.KVP_VARIANT_VALU, "mfma
              "stream": _lib.KVP_VARIANT_STREAM}
 
 
+def _torch_stream(device: torch.device, stream: Optional[torch.cuda.Stream]) -> torch.cuda.Stream:
+    return stream if stream is not None else torch.cuda.current_stream(device)
+
+
 def _stream(device: torch.device, stream: Optional[torch.cuda.Stream]) -> ctypes.c_void_p:
-    s = stream if stream is not None else torch.cuda.current_stream(device)
-    return ctypes.c_void_p(s.cuda_stream)
+    return ctypes.c_void_p(_torch_stream(device, stream).cuda_stream)
 
 
 def _need(t: torch.Tensor, name: str, dtype=None, device=None, shape=None):
@@ -163,7 +166,8 @@ def make_workspace(pool: KVPool, num_seqs: int, num_q_heads: int, max_blocks_per
 
 def _decode_args(pool: KVPool, layer: int, q: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
                  scale: float, out: Optional[torch.Tensor], sliding_window: int, partition_tokens: int, variant: str,
-                 workspace: Optional[torch.Tensor], shared_prefix_blocks: int = 0, shared_blocks: bool = False):
+                 workspace: Optional[torch.Tensor], stream: Optional[torch.cuda.Stream],
+                 shared_prefix_blocks: int = 0, shared_blocks: bool = False):
     if q.dim() != 3:
         raise ValueError("q must be [num_seqs, num_q_heads, head_dim]")
     S, Hq, D = q.shape
@@ -174,16 +178,21 @@ def _decode_args(pool: KVPool, layer: int, q: torch.Tensor, block_tables: torch.
         raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
     _need(block_tables, "block_tables", torch.int32, pool.device)
     _need(seq_lens, "seq_lens", torch.int32, pool.device, (S,))
-    if out is None:
-        out = torch.empty_like(q)
-    _need(out, "out", pool.act_dtype, pool.device, tuple(q.shape))
     if variant not in _VARIANTS:
         raise ValueError(f"variant must be one of {sorted(_VARIANTS)}")
     mb = int(block_tables.shape[1])
-    if workspace is None:
-        workspace = make_workspace(pool, S, Hq, mb, partition_tokens)
-    elif workspace.device != pool.device or not workspace.is_contiguous():
+    if workspace is not None and (workspace.device != pool.device or not workspace.is_contiguous()):
         raise ValueError("workspace must be a contiguous tensor on the pool's device")
+    # Memory made here comes from the launch stream's pool: the caching
+    # allocator hands it out again only to work queued on that stream after
+    # this call's kernels (memory from another stream's pool could still be
+    # in use there, or be given to that stream's work while the kernels run).
+    with torch.cuda.stream(_torch_stream(pool.device, stream)):
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            workspace = make_workspace(pool, S, Hq, mb, partition_tokens)
+    _need(out, "out", pool.act_dtype, pool.device, tuple(q.shape))
     args = DecodeArgs(
         layer=layer, q=q.data_ptr(), out=out.data_ptr(), block_tables=block_tables.data_ptr(),
         max_blocks_per_seq=mb, seq_lens=seq_lens.data_ptr(), sliding_window=sliding_window,
@@ -210,7 +219,7 @@ def paged_decode_attention(pool: KVPool, layer: int, q: torch.Tensor, block_tabl
     shared_blocks: some block past that prefix is listed by several rows
     (tiles are then read with cached loads; the result is the same)."""
     args, out = _decode_args(pool, layer, q, block_tables, seq_lens, scale, out, sliding_window, partition_tokens,
-                             variant, workspace, shared_prefix_blocks, shared_blocks)
+                             variant, workspace, stream, shared_prefix_blocks, shared_blocks)
     check(lib.paged_decode_attention(pool.handle, ctypes.byref(args), _stream(pool.device, stream)),
           "paged_decode_attention")
     return out
@@ -226,7 +235,7 @@ def paged_decode_step(pool: KVPool, layer: int, q: torch.Tensor, block_tables: t
     slot_mapping [S], the slot of position seq_lens[s]-1) and attend with it;
     the same result as cache_write followed by paged_decode_attention."""
     args, out = _decode_args(pool, layer, q, block_tables, seq_lens, scale, out, sliding_window, partition_tokens,
-                             variant, workspace, shared_prefix_blocks, shared_blocks)
+                             variant, workspace, stream, shared_prefix_blocks, shared_blocks)
     shape = (q.shape[0], pool.num_kv_heads, pool.head_dim)
     _need(k_new, "k_new", pool.act_dtype, pool.device, shape)
     _need(v_new, "v_new", pool.act_dtype, pool.device, shape)
@@ -239,7 +248,7 @@ def paged_decode_step(pool: KVPool, layer: int, q: torch.Tensor, block_tables: t
 
 def _prefill_args(pool: KVPool, layer: int, q: torch.Tensor, cu_q_lens: torch.Tensor, block_tables: torch.Tensor,
                   seq_lens: torch.Tensor, scale: float, max_q_len: int, out: Optional[torch.Tensor],
-                  sliding_window: int):
+                  sliding_window: int, stream: Optional[torch.cuda.Stream]):
     if q.dim() != 3 or q.shape[2] != pool.head_dim:
         raise ValueError("q must be [total_q, num_q_heads, head_dim]")
     T, Hq, _ = q.shape
@@ -253,7 +262,8 @@ def _prefill_args(pool: KVPool, layer: int, q: torch.Tensor, cu_q_lens: torch.Te
         raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
     _need(block_tables, "block_tables", torch.int32, pool.device)
     if out is None:
-        out = torch.empty_like(q)
+        with torch.cuda.stream(_torch_stream(pool.device, stream)):  # the launch stream's pool, as in _decode_args
+            out = torch.empty_like(q)
     _need(out, "out", pool.act_dtype, pool.device, tuple(q.shape))
     args = PrefillArgs(layer=layer, q=q.data_ptr(), out=out.data_ptr(), cu_q_lens=cu_q_lens.data_ptr(),
                        seq_lens=seq_lens.data_ptr(), block_tables=block_tables.data_ptr(),
@@ -271,7 +281,7 @@ def paged_prefill_attention(pool: KVPool, layer: int, q: torch.Tensor, cu_q_lens
     seq_lens[s] tokens whose K/V are in the pool); max_q_len bounds every
     chunk length."""
     args, out = _prefill_args(pool, layer, q, cu_q_lens, block_tables, seq_lens, scale, max_q_len, out,
-                              sliding_window)
+                              sliding_window, stream)
     check(lib.paged_prefill_attention(pool.handle, ctypes.byref(args), _stream(pool.device, stream)),
           "paged_prefill_attention")
     return out
@@ -285,7 +295,7 @@ def paged_prefill_step(pool: KVPool, layer: int, q: torch.Tensor, cu_q_lens: tor
     """Store the chunks' K/V (k_new/v_new [T, Hkv, D] at slot_mapping [T]),
     then paged_prefill_attention."""
     args, out = _prefill_args(pool, layer, q, cu_q_lens, block_tables, seq_lens, scale, max_q_len, out,
-                              sliding_window)
+                              sliding_window, stream)
     shape = (q.shape[0], pool.num_kv_heads, pool.head_dim)
     _need(k_new, "k_new", pool.act_dtype, pool.device, shape)
     _need(v_new, "v_new", pool.act_dtype, pool.device, shape)
