@@ -116,36 +116,80 @@ def attended_slots(w) -> int:
     return int(np.unique(np.concatenate(slots)).size) if slots else 0
 
 
-def cpu_baseline(w, budget_s: float = 10.0) -> dict:
-    """Time the CPU oracle (as it is, one thread) on whole sequences of the
-    batch, pass after pass, until about `budget_s` seconds are spent."""
+# The CPU baseline runs the oracle in forked worker processes, one per host
+# core, BLAS at one thread each.  It runs before the process touches the GPU,
+# so no worker inherits a device context.  The box gives one GPU's job 16
+# cores whatever the affinity mask shows, hence the cap.
+MAX_BASELINE_WORKERS = 16
+_BASELINE = {}  # what the forked workers read: the workload and the work function
+
+
+def baseline_cores() -> int:
+    return max(1, min(len(os.sched_getaffinity(0)), MAX_BASELINE_WORKERS))
+
+
+def _baseline_worker(args):
+    """One worker: units i, i + n, i + 2n, ... of the sample (cycling) until
+    the shared deadline; returns (units done, work done, seconds)."""
     from threadpoolctl import threadpool_limits
 
-    import oracle
-
-    done, kv_bytes = 0, 0
-    per_token = 2 * w.num_kv_heads * w.head_dim * w.elt_bytes
-    valid = w.valid_tokens()
+    i, n, deadline = args
+    fn, units = _BASELINE["fn"], _BASELINE["units"]
+    done, work = 0, 0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        while time.perf_counter() - t0 < budget_s:
-            for s in range(w.num_seqs):
-                oracle.decode_attention_seq(w.pool, 0, w.q[s], w.block_tables[s], int(w.seq_lens[s]), w.window,
-                                            w.scale, k_scale=w.k_scale, v_scale=w.v_scale)
-                done += 1
-                kv_bytes += int(valid[s]) * per_token
-                if time.perf_counter() - t0 > budget_s:
-                    break
-        dt = time.perf_counter() - t0
+        k = i
+        while time.time() < deadline:
+            work += fn(units[k % len(units)])
+            done += 1
+            k += n
+        return done, work, time.perf_counter() - t0
+
+
+def run_cpu_baseline(fn, units, budget_s: float):
+    """Run fn(unit) (returning its work: bytes or FLOPs) over `units` on
+    every baseline core for about budget_s seconds.  Returns (units done,
+    work done, wall seconds, cores, mean per-core rate)."""
+    import multiprocessing
+
+    cores = baseline_cores()
+    _BASELINE.update(fn=fn, units=units)
+    with multiprocessing.get_context("fork").Pool(cores) as pool:
+        pool.map(abs, range(cores))  # workers up before the clock starts
+        t0 = time.time()
+        res = pool.map(_baseline_worker, [(i, cores, t0 + budget_s) for i in range(cores)])
+        wall = time.time() - t0
+    _BASELINE.clear()
+    done = sum(r[0] for r in res)
+    work = sum(r[1] for r in res)
+    per_core = sum(r[1] / r[2] for r in res if r[2] > 0) / cores
+    return done, work, wall, cores, per_core
+
+
+def cpu_baseline(w, budget_s: float = 10.0) -> dict:
+    """Time the CPU oracle (as it is) on whole sequences of the batch, one
+    sequence per task, on every host core for about `budget_s` seconds."""
+    import oracle
+
+    per_token = 2 * w.num_kv_heads * w.head_dim * w.elt_bytes
+    valid = w.valid_tokens()
+
+    def one_sequence(s):
+        oracle.decode_attention_seq(w.pool, 0, w.q[s], w.block_tables[s], int(w.seq_lens[s]), w.window,
+                                    w.scale, k_scale=w.k_scale, v_scale=w.v_scale)
+        return int(valid[s]) * per_token
+
+    done, kv_bytes, dt, cores, per_core = run_cpu_baseline(one_sequence, list(range(w.num_seqs)), budget_s)
     return {
         "value": kv_bytes / dt / 1e9,
         "unit": "GB/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
         "sample": f"{done} sequence-layer steps ({done / w.num_seqs:.2f} passes over the {w.num_seqs} sequences, "
-                  f"all {w.num_q_heads} query heads, layer 0; fp64 numpy, one thread): "
-                  f"{done / dt:.2f} seq-layer steps/s",
+                  f"all {w.num_q_heads} query heads, layer 0; fp64 numpy in {cores} worker processes, BLAS one "
+                  f"thread each): {done / dt:.2f} seq-layer steps/s",
         "seconds": round(dt, 3),
+        "per_core_value": round(per_core / 1e9, 4),
     }
 
 
@@ -164,38 +208,37 @@ def prefill_flops(w) -> int:
 
 
 def cpu_baseline_prefill(w, budget_s: float = 10.0) -> dict:
-    """The prefill oracle (as it is, one thread) on a bounded sample: whole
-    chunks' tokens, a few at a time, all heads, until ~budget_s."""
-    import numpy as np
-    from threadpoolctl import threadpool_limits
-
+    """The prefill oracle (as it is) on a bounded sample: one chunk token of
+    one sequence per task (all heads; the tokens of a chunk spread evenly),
+    on every host core for about budget_s seconds."""
     import oracle
 
-    flops, done = 0, 0
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < budget_s:
-            for s in range(w.num_seqs):
-                a, q_len, ctx = int(w.cu_q_lens[s]), int(w.q_lens[s]), int(w.seq_lens[s])
-                toks = list(range(done % q_len, q_len, max(1, q_len // 8)))[:8]
-                oracle.prefill_attention_seq(w.pool, 0, w.q[a:a + q_len], w.block_tables[s], ctx, w.window,
-                                             w.scale, k_scale=w.k_scale, v_scale=w.v_scale, tokens=toks)
-                for i in toks:
-                    p = ctx - q_len + i
-                    lo = max(0, p + 1 - w.window) if w.window else 0
-                    flops += 4 * w.head_dim * w.num_q_heads * (p - lo + 1)
-                done += len(toks)
-                if time.perf_counter() - t0 > budget_s:
-                    break
-        dt = time.perf_counter() - t0
+    units = []
+    for k in range(8):
+        for s in range(w.num_seqs):
+            q_len = int(w.q_lens[s])
+            if q_len:
+                units.append((s, (k * q_len) // 8))
+
+    def one_token(u):
+        s, i = u
+        a, q_len, ctx = int(w.cu_q_lens[s]), int(w.q_lens[s]), int(w.seq_lens[s])
+        oracle.prefill_attention_seq(w.pool, 0, w.q[a:a + q_len], w.block_tables[s], ctx, w.window,
+                                     w.scale, k_scale=w.k_scale, v_scale=w.v_scale, tokens=[i])
+        p = ctx - q_len + i
+        lo = max(0, p + 1 - w.window) if w.window else 0
+        return 4 * w.head_dim * w.num_q_heads * (p - lo + 1)
+
+    done, flops, dt, cores, per_core = run_cpu_baseline(one_token, units, budget_s)
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
-        "sample": f"{done} query tokens (all {w.num_q_heads} heads, eight spread over each chunk per pass; fp64 "
-                  f"numpy, one thread): {done / dt:.1f} tokens/s",
+        "sample": f"{done} query tokens (all {w.num_q_heads} heads, eight spread over each chunk; fp64 numpy in "
+                  f"{cores} worker processes, BLAS one thread each): {done / dt:.1f} tokens/s",
         "seconds": round(dt, 3),
+        "per_core_value": round(per_core / 1e12, 6),
     }
 
 
@@ -207,13 +250,17 @@ def bench_prefill(args) -> int:
     import torch
 
     import workloads as W
-    from paged_kv_cache_37_amd import ops
 
     dev = torch.device("cuda:0")
     L = args.layers or (8 if args.kv_dtype == "bf16" else 16)
     log(f"generating the chunked-prefill batch with {L} layer slice(s)")
     w = W.prefill_config(num_layers=L, dtype=args.kv_dtype, block_size=args.block_size)
     log(f"generated: {w.name}, {w.num_blocks} blocks/layer")
+    baseline = None
+    if not args.no_cpu_baseline:  # before the GPU is touched (the workers are forked)
+        log(f"timing the CPU oracle on {baseline_cores()} cores")
+        baseline = cpu_baseline_prefill(w)
+    from paged_kv_cache_37_amd import ops
     pool_dt = {"bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[w.dtype]
     pool = ops.KVPool(L, w.num_blocks, w.num_kv_heads, w.head_dim, pool_dt, dev, block_size=w.block_size)
     if w.dtype == "bf16":
@@ -309,11 +356,8 @@ def bench_prefill(args) -> int:
             "kernel": "paged_prefill_attention (prefill_kernel)",
             "flops_per_call": flops,
         },
-        "cpu_baseline": None,
+        "cpu_baseline": baseline,
     }
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle")
-        result["cpu_baseline"] = cpu_baseline_prefill(w)
     print(json.dumps(result), flush=True)
     return 0
 
@@ -358,8 +402,6 @@ def main() -> int:
         return bench_prefill(args)
 
     import workloads as W
-    from paged_kv_cache_37_amd import ops
-    from paged_kv_cache_37_amd.blockpool import rows_share_blocks, shared_prefix_blocks
 
     dev = torch.device("cuda:0")
     # an FP8 pool holds half the bytes per layer: twice the slices for the same footprint
@@ -369,6 +411,12 @@ def main() -> int:
     w = W.make(args.config, args.seed, num_layers=L, dtype=args.kv_dtype, block_size=args.block_size)
     W.with_next_token(w, w.unused_blocks)
     log(f"generated in {time.time() - t0:.1f}s: {w.name}, {w.num_blocks} blocks/layer")
+    baseline = None
+    if not args.no_cpu_baseline:  # before the GPU is touched (the workers are forked)
+        log(f"timing the CPU oracle on {baseline_cores()} cores")
+        baseline = cpu_baseline(w)
+    from paged_kv_cache_37_amd import ops
+    from paged_kv_cache_37_amd.blockpool import rows_share_blocks, shared_prefix_blocks
 
     dt = torch.float32 if w.dtype == "f32" else torch.bfloat16  # queries, outputs, new tokens
     pool_dt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[w.dtype]
@@ -536,11 +584,8 @@ def main() -> int:
             "kernel": kernel,
             "bytes_per_call": call_bytes,
         },
-        "cpu_baseline": None,
+        "cpu_baseline": baseline,
     }
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle")
-        result["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(result), flush=True)
     return 0
 
