@@ -56,7 +56,7 @@ def test_prefill_shapes(gpu, Hq, Hkv, D):
     """G = 4, 4, 1, 32, 3, 8; chunks of 1..200 tokens, fresh and continued."""
     w = W.prefill_batch(100 + Hq + D, PRIOR, QLEN, Hq, Hkv, D)
     say("prefill", Hq, Hkv, D, "T", int(w.cu_q_lens[-1]))
-    compare(PDev(w).attend(), ref_of(w), "bf16", f"prefill G{Hq // Hkv} D{D}")
+    compare(PDev(w).attend(), ref_of(w), "bf16", f"prefill G{Hq // Hkv} D{D}", bar="prefill")
 
 
 @pytest.mark.parametrize("dtype,B,window", [("bf16", 16, 40), ("bf16", 32, 0), ("bf16", 32, 40), ("fp8", 16, 0),
@@ -64,7 +64,7 @@ def test_prefill_shapes(gpu, Hq, Hkv, D):
 def test_prefill_windows_blocks_dtypes(gpu, dtype, B, window):
     w = W.prefill_batch(200 + B + window, PRIOR, QLEN, 32, 8, 128, window=window, dtype=dtype, block_size=B)
     say("prefill", dtype, B, window)
-    compare(PDev(w).attend(), ref_of(w), "bf16", f"prefill {dtype} B{B} W{window}")
+    compare(PDev(w).attend(), ref_of(w), "bf16", f"prefill {dtype} B{B} W{window}", bar="prefill")
 
 
 def test_prefill_single_token_chunks_match_decode(gpu):
@@ -74,7 +74,7 @@ def test_prefill_single_token_chunks_match_decode(gpu):
     w = W.prefill_batch(300, prior, [1] * len(prior), 32, 8, 128)
     out = PDev(w).attend()
     ref = ref_of(w)
-    compare(out, ref, "bf16", "prefill q_len 1")
+    compare(out, ref, "bf16", "prefill q_len 1", bar="prefill")
     from paged_kv_cache_37_amd import ops
 
     d = PDev(w)
@@ -104,7 +104,7 @@ def test_prefill_step_writes_then_attends(gpu):
     torch.cuda.synchronize()
     pool_ref = oracle.cache_write(w.pool, 0, k_new, v_new, slots)
     assert torch_to_bits(d.pool.to_logical()).tobytes() == np.ascontiguousarray(pool_ref).tobytes()
-    compare(out, ref_of(w, pool_ref), "bf16", "prefill step")
+    compare(out, ref_of(w, pool_ref), "bf16", "prefill step", bar="prefill")
 
 
 def test_prefill_relabelling_is_bitwise_invisible(gpu):
@@ -127,7 +127,7 @@ def test_prefill_chunk_longer_than_context(gpu):
     out = PDev(w).attend()
     ref = ref_of(w)
     assert float(out[:8].abs().max()) == 0.0
-    compare(out, ref, "bf16", "chunk longer than context")
+    compare(out, ref, "bf16", "chunk longer than context", bar="prefill")
 
 
 def test_prefill_config_sampled(gpu):
@@ -143,7 +143,7 @@ def test_prefill_config_sampled(gpu):
                                            int(w.seq_lens[s]), 0, w.scale, tokens=toks)
         rows += [a + t for t in toks]
         refs.append(ref[toks])
-    compare(out[rows], np.concatenate(refs), "bf16", "chunked-prefill batch (sampled)")
+    compare(out[rows], np.concatenate(refs), "bf16", "chunked-prefill batch (sampled)", bar="prefill")
 
 
 @pytest.mark.parametrize("scale", [-0.0884, 0.0, 2.5])
@@ -154,7 +154,7 @@ def test_prefill_scale_sign_and_zero(gpu, scale):
     w = W.prefill_batch(700, [0, 30, 300], [40, 17, 129], 16, 4, 128)
     w.scale = float(np.float32(scale))  # float32-representable, as the kernel receives it
     say("prefill scale", scale)
-    compare(PDev(w).attend(), ref_of(w), "bf16", f"prefill scale {scale}")
+    compare(PDev(w).attend(), ref_of(w), "bf16", f"prefill scale {scale}", bar="prefill")
 
 
 @pytest.mark.parametrize("bad_entry", [-1, 10 ** 6])
@@ -181,7 +181,7 @@ def test_prefill_bad_table_entry_is_skipped(gpu, bad_entry):
     w2.block_tables = t2
     w2.seq_lens = np.array([int(w.seq_lens[0]) - 16, int(w.seq_lens[1])], np.int32)
     ref = oracle.prefill_attention(w.pool, 0, w.q, w.cu_q_lens, t2, w2.seq_lens, 0, w.scale)
-    compare(out, ref, "bf16", f"prefill with table entry {bad_entry} skipped")
+    compare(out, ref, "bf16", f"prefill with table entry {bad_entry} skipped", bar="prefill")
 
 
 @pytest.mark.parametrize("Hq,Hkv,D,B,window", [(8, 2, 64, 16, 0), (16, 16, 64, 32, 24), (32, 8, 128, 32, 0)])
@@ -190,4 +190,4 @@ def test_prefill_fp8_shapes(gpu, Hq, Hkv, D, B, window):
     G = 1 and 4, 16- and 32-token blocks, with and without a window."""
     w = W.prefill_batch(900 + D + B + window, PRIOR, QLEN, Hq, Hkv, D, window=window, dtype="fp8", block_size=B)
     say("prefill fp8", Hq, Hkv, D, B, window)
-    compare(PDev(w).attend(), ref_of(w), "bf16", f"prefill fp8 G{Hq // Hkv} D{D} B{B} W{window}")
+    compare(PDev(w).attend(), ref_of(w), "bf16", f"prefill fp8 G{Hq // Hkv} D{D} B{B} W{window}", bar="prefill")

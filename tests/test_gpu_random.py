@@ -78,4 +78,4 @@ def test_random_prefill(gpu, seed):
     torch.cuda.synchronize()
     ref = oracle.prefill_attention(w.pool, 0, w.q, w.cu_q_lens, w.block_tables, w.seq_lens, w.window, w.scale,
                                    k_scale=w.k_scale, v_scale=w.v_scale)
-    compare(out, ref, "bf16", f"random prefill {seed}")
+    compare(out, ref, "bf16", f"random prefill {seed}", bar="prefill")
