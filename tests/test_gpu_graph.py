@@ -123,4 +123,4 @@ def test_prefill_in_a_graph(gpu):
     out = replay_and_check(call, q, queries(w, torch.bfloat16, 3), "prefill")
     qb = W.f32_to_bf16_bits(q.float().cpu().numpy())
     ref = oracle.prefill_attention(w.pool, 0, qb, w.cu_q_lens, w.block_tables, w.seq_lens, w.window, w.scale)
-    compare(out, ref, "bf16", "graph prefill")
+    compare(out, ref, "bf16", "graph prefill", bar="prefill")

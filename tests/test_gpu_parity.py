@@ -433,6 +433,29 @@ def test_workspace_is_reusable(gpu):
         compare(out, ref, "bf16", f"reuse/{variant}")
 
 
+def test_call_on_a_side_stream_without_workspace(gpu):
+    """Calls launched on a stream other than the current one, with out and
+    workspace made by the binding, while the current stream allocates and
+    fills memory meanwhile: every output equals the current-stream call's."""
+    w = small(36, [700, 1000, 2000, 33, 4000], Hq=8, Hkv=2)
+    dev = Dev(w)
+    runs = (("stream", 0), ("mfma", 128), ("stream", 0), ("mfma", 256))
+    base = {r: torch_to_bits(dev.attend(variant=r[0], partition_tokens=r[1])) for r in runs}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for variant, part in runs:
+        outs.append(dev.ops.paged_decode_attention(dev.pool, 0, dev.q, dev.tables, dev.lens, w.scale,
+                                                   variant=variant, partition_tokens=part, stream=side))
+        junk = torch.empty(32 << 20, dtype=torch.uint8, device="cuda")
+        junk.fill_(0xFF)
+        del junk
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for r, o in zip(runs, outs):
+        assert torch_to_bits(o).tobytes() == base[r].tobytes(), r
+
+
 @pytest.mark.parametrize("dtype,B,D,window", [("bf16", 16, 128, 0), ("fp8", 16, 128, 0), ("bf16", 32, 64, 0),
                                               ("fp8", 32, 128, 40), ("bf16", 16, 128, 33), ("fp8", 16, 64, 0)])
 def test_shared_blocks_hint_changes_no_bit(gpu, dtype, B, D, window):
