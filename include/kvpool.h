@@ -321,6 +321,31 @@ int32_t paged_decode_step(kvp_pool pool, const kvp_decode_args* args, const void
                           const void* v_new, const int32_t* slot_mapping, hipStream_t stream);
 
 /*
+ * paged_decode_step_noalloc -- paged_decode_step for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  It allocates nothing (no
+ * hipMalloc, hipFree or allocating library call): its workspace is a
+ * static array of KVP_NOALLOC_SCRATCH_BYTES in the library, one per GPU,
+ * held from the first use of the library's code on that GPU to the end of
+ * the process.  The caller still passes every input and output.
+ *
+ *   Arguments, results and errors as for paged_decode_step (same kernels,
+ *   bit-identical outputs and pool), except that args->workspace and
+ *   args->workspace_bytes are ignored.  A call whose workspace would exceed
+ *   KVP_NOALLOC_SCRATCH_BYTES (paged_decode_workspace_bytes() bounds it) is
+ *   refused with KVP_ERR_WORKSPACE_TOO_SMALL before anything is launched.
+ *   The array needs no clearing: a call writes every byte of it that it
+ *   reads.  All calls on one GPU share the array, so calls that overlap
+ *   on one GPU (on different streams, or from several threads without an
+ *   order between their streams) race and give unspecified results.  The
+ *   first call on a GPU looks the array's address up (hipGetSymbolAddress,
+ *   with the stream's device current); KVP_ERR_HIP if that fails.
+ */
+#define KVP_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int32_t paged_decode_step_noalloc(kvp_pool pool, const kvp_decode_args* args, const void* k_new,
+                                  const void* v_new, const int32_t* slot_mapping, hipStream_t stream);
+
+/*
  * kv_pool_copy_blocks -- the device side of copy-on-write, every layer.
  *   [Optimizing] "Copy-on-Write (CoW) for Parallel Sampling and Prefix
  *   Caching": before a sequence writes into a block it shares, it is given a

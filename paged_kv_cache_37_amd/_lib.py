@@ -29,6 +29,8 @@ KVP_VARIANT_VALU = 1
 KVP_VARIANT_MFMA = 2
 KVP_VARIANT_STREAM = 3
 
+NOALLOC_SCRATCH_BYTES = 64 << 20  # KVP_NOALLOC_SCRATCH_BYTES
+
 EXPORTS = (
     "kv_pool_bytes",
     "kv_pool_create",
@@ -40,6 +42,7 @@ EXPORTS = (
     "paged_decode_workspace_bytes",
     "paged_decode_attention",
     "paged_decode_step",
+    "paged_decode_step_noalloc",
     "kv_pool_copy_blocks",
     "paged_prefill_attention",
     "paged_prefill_step",
@@ -116,6 +119,7 @@ def _load() -> ctypes.CDLL:
         "paged_decode_workspace_bytes": (ctypes.c_size_t, [P, i32, i32, i32, i32]),
         "paged_decode_attention": (i32, [P, ctypes.POINTER(DecodeArgs), P]),
         "paged_decode_step": (i32, [P, ctypes.POINTER(DecodeArgs), P, P, P, P]),
+        "paged_decode_step_noalloc": (i32, [P, ctypes.POINTER(DecodeArgs), P, P, P, P]),
         "kv_pool_copy_blocks": (i32, [P, P, P, i32, P]),
         "paged_prefill_attention": (i32, [P, ctypes.POINTER(PrefillArgs), P]),
         "paged_prefill_step": (i32, [P, ctypes.POINTER(PrefillArgs), P, P, P, P]),

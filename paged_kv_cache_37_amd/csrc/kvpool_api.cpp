@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -314,9 +315,9 @@ static size_t grid_workspace(const kvp::DecodeParams& p, int32_t head_dim, size_
 
 // Workspace of the streaming kernel: prefix sums, then
 // two partial slots per wave for up to heads_per_wg heads ((max, sum) pairs
-// and outputs), then the shared-prefix pieces: one per (sequence, query
-// head) from the prefix pass and one per (row, head) for tails a single wave
-// holds.
+// and outputs), then, for a call with a shared prefix (cascade), the
+// prefix pass's pieces: one per (key chunk, sequence, query head), and one
+// per (row, head) for tails a single wave holds.
 struct StreamLayout {
   size_t prefix, ml, o, pre_ml, pre_o, row_ml, row_o, total;
 };
@@ -333,7 +334,7 @@ static int32_t prefix_pieces_wanted(const kvp::DecodeParams& p) {
   return (int32_t)std::max(1LL, std::min<long long>(want, kvp::kMaxPrefixPieces));
 }
 
-static StreamLayout stream_workspace(const kvp::DecodeParams& p, int32_t head_dim) {
+static StreamLayout stream_workspace(const kvp::DecodeParams& p, int32_t head_dim, bool cascade) {
   StreamLayout L;
   const size_t slots = (size_t)p.stream_wgs * kvp::kWaves * 2 * p.heads_per_wg;
   const size_t qh = (size_t)p.num_seqs * p.num_q_heads;
@@ -341,6 +342,11 @@ static StreamLayout stream_workspace(const kvp::DecodeParams& p, int32_t head_di
   L.prefix = 0;
   L.ml = L.prefix + align256((size_t)(p.num_seqs + 1) * sizeof(int32_t));
   L.o = L.ml + align256(slots * 2 * sizeof(float));
+  if (!cascade) {
+    L.pre_ml = L.pre_o = L.row_ml = L.row_o = 0;
+    L.total = L.o + slots * head_dim * sizeof(float);
+    return L;
+  }
   const size_t pieces = prefix_pieces_wanted(p);
   L.pre_ml = L.o + align256(slots * head_dim * sizeof(float));
   L.pre_o = L.pre_ml + align256(pieces * qh * 2 * sizeof(float));
@@ -359,12 +365,12 @@ size_t paged_decode_workspace_bytes(kvp_pool pool, int32_t num_seqs, int32_t num
     kvp::DecodeParams p;
     int32_t path;
     if (plan(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, v, &p, &path) != KVP_OK) continue;
-    size_t n = path == PATH_STREAM ? stream_workspace(p, pool->desc.head_dim).total
+    size_t n = path == PATH_STREAM ? stream_workspace(p, pool->desc.head_dim, true).total
                                    : grid_workspace(p, pool->desc.head_dim, &a, &a);
     if (path == PATH_STREAM) {  // the fused step's grid (its own occupancy) must fit too
       const bool fp8 = pool->desc.dtype == KVP_FP8_E4M3;
       p.stream_wgs = stream_workgroups(pool->desc.head_dim, 1, true, fp8, p.bshift);
-      const size_t nf = stream_workspace(p, pool->desc.head_dim).total;
+      const size_t nf = stream_workspace(p, pool->desc.head_dim, true).total;
       if (nf > n) n = nf;
     }
     if (n > need) need = n;
@@ -375,9 +381,10 @@ size_t paged_decode_workspace_bytes(kvp_pool pool, int32_t num_seqs, int32_t num
 
 // Decode attention, optionally preceded by each sequence's new-token write
 // (slots != NULL): fused into the streaming kernel, else a cache_write launch
-// first.
+// first.  scratch: the workspace is the library's own array (too small a
+// call is then refused with a message naming its limit).
 static int32_t decode(kvp_pool pool, const kvp_decode_args* a, const void* k_new, const void* v_new,
-                      const int32_t* slots, hipStream_t stream) {
+                      const int32_t* slots, hipStream_t stream, bool scratch = false) {
   if (!pool || !a) return fail(KVP_ERR_INVALID_ARG, "NULL pool or args");
   const kvp_pool_desc& d = pool->desc;
   if (a->layer < 0 || a->layer >= d.num_layers) return fail(KVP_ERR_INVALID_ARG, "layer %d out of range", a->layer);
@@ -422,9 +429,13 @@ static int32_t decode(kvp_pool pool, const kvp_decode_args* a, const void* k_new
     p.prefix_pieces = (tiles + p.prefix_chunk - 1) / p.prefix_chunk;
   }
   size_t o_off = 0, ml_off = 0;
-  const StreamLayout SL = path == PATH_STREAM ? stream_workspace(p, d.head_dim) : StreamLayout{};
+  const StreamLayout SL = path == PATH_STREAM ? stream_workspace(p, d.head_dim, p.prefix_blocks > 0) : StreamLayout{};
   const size_t ws = path == PATH_STREAM ? SL.total : grid_workspace(p, d.head_dim, &o_off, &ml_off);
   if (ws > 0) {
+    if (scratch && a->workspace_bytes < ws)
+      return fail(KVP_ERR_WORKSPACE_TOO_SMALL,
+                  "this call needs %zu bytes of scratch; the no-allocation entry point holds %zu", ws,
+                  a->workspace_bytes);
     if (!a->workspace || a->workspace_bytes < ws)
       return fail(KVP_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes needed (%zu given)", ws,
                   a->workspace ? a->workspace_bytes : (size_t)0);
@@ -486,6 +497,65 @@ int32_t paged_decode_step(kvp_pool pool, const kvp_decode_args* a, const void* k
                           const int32_t* slot_mapping, hipStream_t stream) {
   if (!k_new || !v_new || !slot_mapping) return fail(KVP_ERR_INVALID_ARG, "NULL k_new, v_new or slot_mapping");
   return decode(pool, a, k_new, v_new, slot_mapping, stream);
+}
+
+}  // extern "C"
+
+// ---- the decode step for callers that cannot allocate ----
+//
+// Its workspace is this array: one copy per GPU, resident from the load of
+// the library's code on that GPU to the end of the process.  Host code
+// never passes the array's name to a kernel (on the host it stands for a
+// host-side symbol, not a device address); it asks the runtime for the
+// array's address on each device once and passes that.
+static __device__ __align__(256) unsigned char scratch[KVP_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device `stream` runs on, looked up
+// the first time with that device current.
+int32_t scratch_for(hipStream_t stream, void** out) {
+  int dev = -1, cur = -1;
+  hipError_t e = hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return fail(KVP_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(KVP_ERR_UNSUPPORTED, "device %d past the library's table", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return fail(KVP_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(KVP_ERR_HIP, "hipSetDevice(%d): %s", dev, hipGetErrorString(e));
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess || !ptr)
+      return fail(KVP_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    if (back != hipSuccess) return fail(KVP_ERR_HIP, "hipSetDevice(%d): %s", cur, hipGetErrorString(back));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t paged_decode_step_noalloc(kvp_pool pool, const kvp_decode_args* a, const void* k_new, const void* v_new,
+                                  const int32_t* slot_mapping, hipStream_t stream) {
+  if (!pool || !a) return fail(KVP_ERR_INVALID_ARG, "NULL pool or args");
+  if (!k_new || !v_new || !slot_mapping) return fail(KVP_ERR_INVALID_ARG, "NULL k_new, v_new or slot_mapping");
+  void* ws = nullptr;
+  const int32_t st = scratch_for(stream, &ws);
+  if (st != KVP_OK) return st;
+  kvp_decode_args b = *a;  // the caller's workspace fields are ignored
+  b.workspace = ws;
+  b.workspace_bytes = KVP_NOALLOC_SCRATCH_BYTES;
+  return decode(pool, &b, k_new, v_new, slot_mapping, stream, true);
 }
 
 }  // extern "C"

@@ -167,7 +167,7 @@ def make_workspace(pool: KVPool, num_seqs: int, num_q_heads: int, max_blocks_per
 def _decode_args(pool: KVPool, layer: int, q: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
                  scale: float, out: Optional[torch.Tensor], sliding_window: int, partition_tokens: int, variant: str,
                  workspace: Optional[torch.Tensor], stream: Optional[torch.cuda.Stream],
-                 shared_prefix_blocks: int = 0, shared_blocks: bool = False):
+                 shared_prefix_blocks: int = 0, shared_blocks: bool = False, alloc: bool = True):
     if q.dim() != 3:
         raise ValueError("q must be [num_seqs, num_q_heads, head_dim]")
     S, Hq, D = q.shape
@@ -187,11 +187,14 @@ def _decode_args(pool: KVPool, layer: int, q: torch.Tensor, block_tables: torch.
     # allocator hands it out again only to work queued on that stream after
     # this call's kernels (memory from another stream's pool could still be
     # in use there, or be given to that stream's work while the kernels run).
-    with torch.cuda.stream(_torch_stream(pool.device, stream)):
-        if out is None:
-            out = torch.empty_like(q)
-        if workspace is None:
-            workspace = make_workspace(pool, S, Hq, mb, partition_tokens)
+    if alloc:
+        with torch.cuda.stream(_torch_stream(pool.device, stream)):
+            if out is None:
+                out = torch.empty_like(q)
+            if workspace is None:
+                workspace = make_workspace(pool, S, Hq, mb, partition_tokens)
+    elif out is None:
+        raise ValueError("out must be given: this call allocates nothing")
     _need(out, "out", pool.act_dtype, pool.device, tuple(q.shape))
     args = DecodeArgs(
         layer=layer, q=q.data_ptr(), out=out.data_ptr(), block_tables=block_tables.data_ptr(),
@@ -243,6 +246,27 @@ def paged_decode_step(pool: KVPool, layer: int, q: torch.Tensor, block_tables: t
     check(lib.paged_decode_step(pool.handle, ctypes.byref(args), ctypes.c_void_p(k_new.data_ptr()),
                                 ctypes.c_void_p(v_new.data_ptr()), ctypes.c_void_p(slot_mapping.data_ptr()),
                                 _stream(pool.device, stream)), "paged_decode_step")
+    return out
+
+
+def paged_decode_step_noalloc(pool: KVPool, layer: int, q: torch.Tensor, block_tables: torch.Tensor,
+                              seq_lens: torch.Tensor, scale: float, k_new: torch.Tensor, v_new: torch.Tensor,
+                              slot_mapping: torch.Tensor, out: torch.Tensor, sliding_window: int = 0,
+                              partition_tokens: int = 0, variant: str = "auto",
+                              stream: Optional[torch.cuda.Stream] = None, shared_prefix_blocks: int = 0,
+                              shared_blocks: bool = False) -> torch.Tensor:
+    """paged_decode_step without any allocation: `out` is the caller's, the
+    workspace is the library's static scratch (at most
+    NOALLOC_SCRATCH_BYTES per call; calls that overlap on one GPU race)."""
+    args, out = _decode_args(pool, layer, q, block_tables, seq_lens, scale, out, sliding_window, partition_tokens,
+                             variant, None, stream, shared_prefix_blocks, shared_blocks, alloc=False)
+    shape = (q.shape[0], pool.num_kv_heads, pool.head_dim)
+    _need(k_new, "k_new", pool.act_dtype, pool.device, shape)
+    _need(v_new, "v_new", pool.act_dtype, pool.device, shape)
+    _need(slot_mapping, "slot_mapping", torch.int32, pool.device, (q.shape[0],))
+    check(lib.paged_decode_step_noalloc(pool.handle, ctypes.byref(args), ctypes.c_void_p(k_new.data_ptr()),
+                                        ctypes.c_void_p(v_new.data_ptr()), ctypes.c_void_p(slot_mapping.data_ptr()),
+                                        _stream(pool.device, stream)), "paged_decode_step_noalloc")
     return out
 
 
@@ -319,5 +343,5 @@ def copy_blocks(pool: KVPool, src: torch.Tensor, dst: torch.Tensor,
 
 
 __all__ = ["KVPool", "KVPoolError", "kv_pool_create", "cache_write", "paged_decode_workspace_bytes",
-           "make_workspace", "paged_decode_attention", "paged_decode_step", "copy_blocks", "paged_prefill_attention",
-           "paged_prefill_step", "BLOCK_SIZE"]
+           "make_workspace", "paged_decode_attention", "paged_decode_step", "paged_decode_step_noalloc", "copy_blocks",
+           "paged_prefill_attention", "paged_prefill_step", "BLOCK_SIZE"]
