@@ -49,6 +49,7 @@ namespace kvp {
 namespace {
 
 constexpr int kPfRows = 128;         // query rows per workgroup (32 per wave)
+constexpr int kLptMaxPairs = 256;    // (sequence, query tile) pairs ranked by work in every workgroup
 constexpr int kTiles = 4;            // 16-token tiles per step
 constexpr int kStep = 16 * kTiles;   // keys per step (loaded together; computed 32 at a time)
 
@@ -83,6 +84,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
   // when a step is staged, not by each of the four waves that read them
   __shared__ __align__(16) uint16_t k_s[2][kStep * KROW];
   __shared__ __align__(16) uint16_t v_s[2][kStep * D];  // per 32-key round: [4 quads][D][2 tiles][4 keys]
+  __shared__ int lpt_cost[PREFIX ? 1 : kLptMaxPairs];
+  __shared__ int lpt_pick;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -144,28 +147,62 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
     }
   } else {
     const int SK = P.num_seqs * P.num_kv_heads;  // (sequence, KV head) groups
-    // Heaviest tiles (latest tokens, most keys) first.  Workgroup b runs on
-    // XCD b mod 8: when the groups split evenly, group g goes to XCD g mod 8,
-    // so all query tiles of a group share one L2 (its K/V fetched once) and
-    // every XCD gets one KV head of every sequence.
+    // Workgroups start in index order as slots free up, so the heaviest go
+    // first: the (sequence, query tile) pairs are ranked by the keys their
+    // rows attend (the prior context dominates), workgroup b takes the pair
+    // of rank b / Hkv and KV head b mod Hkv.  Workgroup b runs on XCD b mod
+    // 8, so with 8 KV heads XCD x holds head x of every sequence: all query
+    // tiles of a (sequence, KV head) share one L2 (its K/V fetched once).
+    // Larger batches take tiles by query-tile index, latest first.
     int qt, grp;
-    if (SK % 8 == 0) {
-      const int x = blockIdx.x & 7, k = blockIdx.x >> 3, nx = SK >> 3;
-      qt = P.qtiles - 1 - k / nx;
-      grp = x + 8 * (k - (k / nx) * nx);
+    const int npairs = P.num_seqs * P.qtiles;
+    auto pair_cost = [&](int i) {  // keys the workgroup of pair i attends; -1 if it has no rows
+      const int ps = i / P.qtiles, pq = i - ps * P.qtiles;
+      const int pc0 = P.cu_q_lens[ps], pql = P.cu_q_lens[ps + 1] - pc0, pctx = P.seq_lens[ps];
+      const int prows = max(0, min(min(pql, P.max_q_len), P.total_q - pc0)) * G;
+      if (pq * kPfRows >= prows || pc0 < 0) return -1;
+      const int pp0 = pctx - pql, plast = min(pq * kPfRows + kPfRows, prows) - 1;
+      const int pa = max(pp0 + pq * kPfRows / G, 0), pb = pp0 + plast / G;
+      if (pb < 0) return 0;
+      return pb - (P.window > 0 ? max(0, pa + 1 - P.window) : 0) + 1;
+    };
+    if (npairs <= kLptMaxPairs) {
+      for (int i = threadIdx.x; i < npairs; i += kThreads) lpt_cost[i] = pair_cost(i);
+      __syncthreads();
+      const int target = (int)(blockIdx.x / P.num_kv_heads);
+      for (int i = threadIdx.x; i < npairs; i += kThreads) {
+        const int ci = lpt_cost[i];
+        int rank = 0;
+        for (int j = 0; j < npairs; ++j) {
+          const int cj = lpt_cost[j];
+          rank += (cj > ci) | ((cj == ci) & (j < i));
+        }
+        if (rank == target) lpt_pick = i;
+      }
+      __syncthreads();
+      const int pick = lpt_pick;
+      kvh = (int)(blockIdx.x % P.num_kv_heads);
+      s = pick / P.qtiles;
+      qt = pick - s * P.qtiles;
     } else {
-      qt = P.qtiles - 1 - (int)(blockIdx.x / SK);
-      grp = blockIdx.x - (P.qtiles - 1 - qt) * SK;
+      if (SK % 8 == 0) {
+        const int x = blockIdx.x & 7, k = blockIdx.x >> 3, nx = SK >> 3;
+        qt = P.qtiles - 1 - k / nx;
+        grp = x + 8 * (k - (k / nx) * nx);
+      } else {
+        qt = P.qtiles - 1 - (int)(blockIdx.x / SK);
+        grp = blockIdx.x - (P.qtiles - 1 - qt) * SK;
+      }
+      s = grp / P.num_kv_heads;
+      kvh = grp - s * P.num_kv_heads;
     }
-    s = grp / P.num_kv_heads;
-    kvh = grp - s * P.num_kv_heads;
     c0 = P.cu_q_lens[s];
     const int q_len = P.cu_q_lens[s + 1] - c0;
     const int ctx = P.seq_lens[s];
     // rows computed: the chunk's, up to max_q_len tokens and inside q / out
     const int rows = max(0, min(min(q_len, P.max_q_len), P.total_q - c0)) * G;
     const int r_wg = qt * kPfRows;
-    if (r_wg >= rows || c0 < 0) return;  // the whole workgroup: before any barrier
+    if (r_wg >= rows || c0 < 0) return;  // the whole workgroup (uniform), before the steps' barriers
 
     // Positions: token i at p = ctx - q_len + i.  The table row starts at the
     // block holding `first`, the first key any query of the chunk attends;
