@@ -138,6 +138,7 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
   __shared__ int pre[kMaxStreamSeqs + 1];  // pre[s] = tiles of sequences < s
   __shared__ uint8_t t0s[BS ? kMaxStreamSeqs : 1];  // the first attended tile's place in its block
   __shared__ int wsum[kWaves];
+  __shared__ int ctxs[kMaxStreamSeqs];  // seq_lens, read once: the rows' spans come from here
   const int ptiles = P.prefix_blocks << BS;  // tiles of the shared prefix (cascade)
   const int S = P.num_seqs;
   const int lane = threadIdx.x & 63;
@@ -152,7 +153,9 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
     for (int i = 0; i < per; ++i) {
       const int s = s0 + i;
       if (s < S) {
-        const RowSpan rs = row_span(P.seq_lens[s], P.window, P.max_blocks, BS);
+        const int ctx = P.seq_lens[s];
+        ctxs[s] = ctx;
+        const RowSpan rs = row_span(ctx, P.window, P.max_blocks, BS);
         const int nb = max(rs.nblocks - ptiles, 0);
         pre[s + 1] = nb;
         if constexpr (BS != 0) t0s[s] = (uint8_t)rs.t0;
@@ -182,10 +185,12 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
     // publish the prefix sums for the merge pass; zero the rows of empty
     // sequences (with a shared prefix the merge pass writes every row)
     for (int i = threadIdx.x; i <= S; i += kThreads) P.prefix[i] = pre[i];
-    for (int s = 0; s < S && P.prefix_blocks == 0; ++s)
-      if (pre[s + 1] == pre[s])
-        for (int i = threadIdx.x; i < P.num_q_heads * D; i += kThreads)
-          ((uint16_t*)P.out)[(size_t)s * P.num_q_heads * D + i] = 0;
+    if (P.prefix_blocks == 0)  // each thread the empty rows among sequences t, t + 256, ...
+      for (int s = threadIdx.x; s < S; s += kThreads)
+        if (pre[s + 1] == pre[s]) {
+          uint4_v* o = (uint4_v*)((uint16_t*)P.out + (size_t)s * P.num_q_heads * D);
+          for (int i = 0; i < P.num_q_heads * D / 8; ++i) o[i] = uint4_v{0, 0, 0, 0};
+        }
   }
 
   const long long W = (long long)gridDim.x * kWaves;
@@ -278,13 +283,13 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
   RowCtx cr = row_at(t_begin);
   int crow_id = 0;
   int c_h0 = head0(cr.hg), c_nh = heads(cr.hg);
-  RowSpan crs = row_span(P.seq_lens[cr.s], P.window, P.max_blocks, BS);
+  RowSpan crs = row_span(ctxs[cr.s], P.window, P.max_blocks, BS);
   MfmaRow<D> st;
   st.template load_q<FP8>(q, (size_t)cr.s * P.num_q_heads + c_h0, c_nh, lane);
   st.reset();
   // queries and length of the next row, fetched ahead
   RowCtx qn = row_after(cr);
-  int ctx_next = P.seq_lens[qn.s];
+  int ctx_next = ctxs[qn.s];
   uint4_v q_next[D / 32];
   {
     const int g = lane & 15, nh_n = heads(qn.hg);
@@ -457,7 +462,7 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
       for (int kk = 0; kk < D / 32; ++kk) st.qop[kk] = q_next[kk];
       st.reset();
       qn = row_after(cr);
-      ctx_next = P.seq_lens[qn.s];
+      ctx_next = ctxs[qn.s];
       const int g = lane & 15, nh_n = heads(qn.hg);
       const uint16_t* qp = q + ((size_t)qn.s * P.num_q_heads + head0(qn.hg) + g) * D;
 #pragma unroll
