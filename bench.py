@@ -15,10 +15,12 @@ served from the 256 MB last-level cache.
 Prints one JSON line.  `value` is the step's algorithmic bytes (K/V of the
 attended slots, each physical slot once, queries, outputs, tables, the
 written K/V) per second;
-`roofline` relates the timed call's algorithmic bytes (the step's, or the
-attention's with --unfused) to its average duration, from HIP events on the
-launch stream around each call in a second pass of the same K steps (the
-first pass, timed as a whole, gives `value`), and the 8 TB/s HBM peak;
+`roofline` relates the timed call's algorithmic bytes to its average
+duration and the 8 TB/s HBM peak: the fused step's from the HIP events
+around the K back-to-back steps on the launch stream (the pass that also
+gives `value`); with --unfused the attention call's, from events around
+each call in a second pass of the same K steps (`call_us` in the line is
+always that second pass's per-call figure);
 `cpu_baseline` times the CPU oracle on a bounded sample of the same batch.
 """
 from __future__ import annotations
@@ -524,7 +526,12 @@ def main() -> int:
     write_bytes = 2 * S * Hkv * D * (ab + eb) + S * 4  # new K/V read, stored into the pool
     step_bytes = attn_bytes + write_bytes
     call_bytes = attn_bytes if args.unfused else step_bytes
-    achieved = call_bytes / (call_ms * 1e-3) / 1e9
+    # the timed call's average duration: for the fused step the step itself,
+    # from the events around the K back-to-back calls of the first pass (no
+    # events between calls); for --unfused the attention call between its
+    # own events
+    roof_ms = call_ms if args.unfused else ms_per_step
+    achieved = call_bytes / (roof_ms * 1e-3) / 1e9
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     variant = args.variant
     if variant == "auto":
@@ -583,6 +590,7 @@ def main() -> int:
             "traffic": traffic_from_profiles(w.name, label),
             "kernel": kernel,
             "bytes_per_call": call_bytes,
+            "call_us": round(roof_ms * 1e3, 2),
         },
         "cpu_baseline": baseline,
     }
