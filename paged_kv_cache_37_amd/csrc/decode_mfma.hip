@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kThreads, KVP_MFMA_WAVES_PER_EU) void decode_mfma_k
 #pragma unroll
   for (int n = 0; n < D / 16; ++n)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) o_s[wave][4 * q4 + r][32 * (n >> 1) + 2 * (lane & 15) + (n & 1)] = st.acc[n][r];
+    for (int r = 0; r < 4; ++r) o_s[wave][4 * q4 + r][acc_dim<FP8>(n, lane & 15)] = st.acc[n][r];
   __syncthreads();
   finish_partition<uint16_t, D, 16>(P, o_s, m_s, l_s, s, h0, nh, part, nparts);
 }

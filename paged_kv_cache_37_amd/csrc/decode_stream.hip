@@ -310,30 +310,21 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int g = 4 * q4 + r4;
-        if (g < c_nh) {
-          float2* o = (float2*)(P.row_o + (pbase + g) * D);
-#pragma unroll
-          for (int m = 0; m < D / 32; ++m)
-            o[16 * m + (lane & 15)] = make_float2(st.acc[2 * m][r4], st.acc[2 * m + 1][r4]);
-        }
+        if (g < c_nh) st.template store_partial<FP8>(P.row_o + (pbase + g) * D, r4, lane);
       }
       if (lane < c_nh) {
         P.row_ml[(pbase + lane) * 2 + 0] = st.m_run;
         P.row_ml[(pbase + lane) * 2 + 1] = l_tot;
       }
     } else if (ra >= t_begin && rb <= t_end) {
-      // the whole row is here: normalise and store (two bf16 per store)
+      // the whole row is here: normalise and store
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int g = 4 * q4 + r4;
         const float lg = __shfl(l_tot, g);
         const float inv = lg > 0.f ? P.v_scale / lg : 0.f;
-        if (g < c_nh) {
-          unsigned* o = (unsigned*)((uint16_t*)P.out + ((size_t)cr.s * P.num_q_heads + c_h0 + g) * D);
-#pragma unroll
-          for (int m = 0; m < D / 32; ++m)
-            o[16 * m + (lane & 15)] = pack_bf16x2(st.acc[2 * m][r4] * inv, st.acc[2 * m + 1][r4] * inv);
-        }
+        if (g < c_nh)
+          st.template store_out<FP8>((uint16_t*)P.out + ((size_t)cr.s * P.num_q_heads + c_h0 + g) * D, r4, inv, lane);
       }
     } else {
       const int slot = ra <= t_begin ? 0 : 1;
@@ -341,12 +332,7 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int g = 4 * q4 + r4;
-        if (g < c_nh) {
-          float2* o = (float2*)(P.part_o + (pbase + g) * D);
-#pragma unroll
-          for (int m = 0; m < D / 32; ++m)
-            o[16 * m + (lane & 15)] = make_float2(st.acc[2 * m][r4], st.acc[2 * m + 1][r4]);
-        }
+        if (g < c_nh) st.template store_partial<FP8>(P.part_o + (pbase + g) * D, r4, lane);
       }
       if (lane < c_nh) *(float2*)(P.part_ml + (pbase + lane) * 2) = make_float2(st.m_run, l_tot);
     }
@@ -393,12 +379,16 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
       }
       const int sh = 8 * (o & 3);
       const unsigned keep = ~(0xffu << sh);
+      // word e of t.v[h] holds dim 64 h + 4 j + e (its four tokens' codes)
 #pragma unroll
-      for (int m = 0; m < D / 32; ++m) {
-        const unsigned nv = (unsigned)__shfl((int)vc, 16 * m + j);  // dims 32 m + 2 j (byte 0), +1 (byte 1)
+      for (int h = 0; h < D / 64; ++h) {
+        const unsigned na = (unsigned)__shfl((int)vc, 32 * h + 2 * j);      // dims 64 h + 4 j (byte 0), +1 (byte 1)
+        const unsigned nb = (unsigned)__shfl((int)vc, 32 * h + 2 * j + 1);  // dims 64 h + 4 j + 2, +3
         if (q4 == (o >> 2)) {
-          t.v[m].x = (t.v[m].x & keep) | ((nv & 0xffu) << sh);
-          t.v[m].y = (t.v[m].y & keep) | (((nv >> 8) & 0xffu) << sh);
+          t.v[h].x = (t.v[h].x & keep) | ((na & 0xffu) << sh);
+          t.v[h].y = (t.v[h].y & keep) | (((na >> 8) & 0xffu) << sh);
+          t.v[h].z = (t.v[h].z & keep) | ((nb & 0xffu) << sh);
+          t.v[h].w = (t.v[h].w & keep) | (((nb >> 8) & 0xffu) << sh);
         }
       }
       if (writer) {

@@ -20,6 +20,10 @@
 // per lane (dims 64 (kk / 2) + 16 q .. +15: the first 8 for QK MFMA kk
 // even, the rest for kk odd), so that every load takes 64-byte runs of
 // the K rows as with bf16; the queries follow the same dim order (qk_dim).
+// FP8 V is loaded 16 codes per lane too: dims 4 (l%16) .. +3 and 64 + 4
+// (l%16) .. +3 of tokens 4q..4q+3, so PV MFMA n = 4h + e takes dim
+// 64 h + 4 (l%16) + e as column l%16 (acc_dim gives the mapping of each
+// pool type).
 //
 // Tile loads are ordinary cached loads or non-temporal ones (mfma_issue's
 // NT): a batch whose blocks each belong to one row reads every line once,
@@ -44,10 +48,18 @@ typedef __attribute__((ext_vector_type(2))) unsigned uint2_v;
 template <int D, bool FP8 = false>
 struct MfmaTiles {
   using Op = std::conditional_t<FP8, uint2_v, uint4_v>;
-  Op k[D / 32];  // token l%16, dims 32kk + 8q .. +7
-  Op v[D / 32];  // tokens 4q..4q+3 of dims 32m + 2(l%16), +1
-  bool bad;      // block id outside the pool: contributes nothing
+  static constexpr int NV = FP8 ? D / 64 : D / 32;
+  Op k[D / 32];      // token l%16, dims 32kk + 8q .. +7
+  uint4_v v[NV];     // bf16: tokens 4q..4q+3 of dims 32m + 2(l%16), +1;
+                     // FP8: the same tokens of dims 64h + 4(l%16) .. +3
+  bool bad;          // block id outside the pool: contributes nothing
 };
+
+// Output dim held by PV accumulator n of lane column c (= l%16).
+template <bool FP8>
+__device__ __forceinline__ constexpr int acc_dim(int n, int c) {
+  return FP8 ? 64 * (n >> 2) + 4 * c + (n & 3) : 32 * (n >> 1) + 2 * c + (n & 1);
+}
 
 // Per-wave addressing of one KV head's tiles inside a block.  A block of
 // 16 << BS tokens holds, per head, a K tile [B][D] and a V tile
@@ -58,7 +70,7 @@ struct MfmaLanes {
   size_t k_off;       // this head's K tile inside a block
   size_t v_rel;       // V tile = K tile + v_rel
   int k_lane;         // this lane's K element offset (+ 32 kk; FP8: + 64 per 16-code load)
-  int v_lane;         // this lane's V element offset (+ 128 m)
+  int v_lane;         // this lane's V element offset (+ 128 m; FP8: + 256 h)
 };
 
 // First of the 8 dims that lanes of row group q supply to QK MFMA kk (the
@@ -76,7 +88,7 @@ __device__ __forceinline__ MfmaLanes mfma_lanes(int num_kv_heads, int kvh, int l
   a.k_off = (size_t)kvh * tile;
   a.v_rel = (size_t)num_kv_heads * tile;
   a.k_lane = (lane & 15) * D + qk_dim<FP8>(0, lane >> 4);
-  a.v_lane = ((lane >> 4) * D + 2 * (lane & 15)) * 4;
+  a.v_lane = ((lane >> 4) * D + (FP8 ? 4 : 2) * (lane & 15)) * 4;
   return a;
 }
 
@@ -109,8 +121,13 @@ __device__ __forceinline__ void mfma_issue(MfmaTiles<D, FP8>& t, const void* __r
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) t.k[kk] = tile_load<NT>((const Op*)(kt + a.k_lane + 32 * kk));
   }
+  if constexpr (FP8) {
 #pragma unroll
-  for (int m = 0; m < D / 32; ++m) t.v[m] = tile_load<NT>((const Op*)(kt + a.v_rel + a.v_lane + 128 * m));
+    for (int h = 0; h < D / 64; ++h) t.v[h] = tile_load<NT>((const uint4_v*)(kt + a.v_rel + a.v_lane + 256 * h));
+  } else {
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) t.v[m] = tile_load<NT>((const uint4_v*)(kt + a.v_rel + a.v_lane + 128 * m));
+  }
 }
 
 // As many loads as mfma_issue issues, each one dword of the 128 bytes at
@@ -129,7 +146,7 @@ __device__ __forceinline__ void mfma_issue_hot(MfmaTiles<D, FP8>& t, const void*
       t.k[2 * k2 + 1] = uint2_v{0u, 0u};
     }
 #pragma unroll
-    for (int m = 0; m < D / 32; ++m) t.v[m] = uint2_v{h[16 + m], 0u};
+    for (int m = 0; m < D / 64; ++m) t.v[m] = uint4_v{h[16 + m], 0u, 0u, 0u};
   } else {
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) t.k[kk] = uint4_v{h[kk], 0u, 0u, 0u};
@@ -146,6 +163,39 @@ struct MfmaRow {
   float m_run;          // running max of head l%16 (base 2), uniform over row groups
   float l_run;          // this lane's share of head l%16's weight sum
   float4_v acc[D / 16];
+
+  // Row 4 (l/16) + r4 of the accumulators (one query head) as D fp32
+  // values at dst (a partial result), or times inv as D bf16 values at
+  // dst (the output); each lane stores the dims its columns hold.
+  template <bool FP8>
+  __device__ __forceinline__ void store_partial(float* dst, int r4, int lane) const {
+    const int c = lane & 15;
+    if constexpr (FP8) {
+#pragma unroll
+      for (int h = 0; h < D / 64; ++h)
+        *(float4_v*)(dst + acc_dim<true>(4 * h, c)) =
+            float4_v{acc[4 * h][r4], acc[4 * h + 1][r4], acc[4 * h + 2][r4], acc[4 * h + 3][r4]};
+    } else {
+#pragma unroll
+      for (int m = 0; m < D / 32; ++m)
+        *(float2*)(dst + acc_dim<false>(2 * m, c)) = make_float2(acc[2 * m][r4], acc[2 * m + 1][r4]);
+    }
+  }
+  template <bool FP8>
+  __device__ __forceinline__ void store_out(uint16_t* dst, int r4, float inv, int lane) const {
+    const int c = lane & 15;
+    if constexpr (FP8) {
+#pragma unroll
+      for (int h = 0; h < D / 64; ++h)
+        *(uint2_v*)(dst + acc_dim<true>(4 * h, c)) =
+            uint2_v{pack_bf16x2(acc[4 * h][r4] * inv, acc[4 * h + 1][r4] * inv),
+                    pack_bf16x2(acc[4 * h + 2][r4] * inv, acc[4 * h + 3][r4] * inv)};
+    } else {
+#pragma unroll
+      for (int m = 0; m < D / 32; ++m)
+        *(unsigned*)(dst + acc_dim<false>(2 * m, c)) = pack_bf16x2(acc[2 * m][r4] * inv, acc[2 * m + 1][r4] * inv);
+    }
+  }
 
   __device__ __forceinline__ void reset() {
     m_run = -INFINITY;
@@ -171,16 +221,20 @@ struct MfmaRow {
   __device__ __forceinline__ void step(MfmaTiles<D, FP8>& t, int J, int so, int send, int nblocks, float scale_log2,
                                        int lane) {
     const int q4 = lane >> 4;
-    uint4_v kop[D / 32], vop[D / 32];
+    // K operands as bf16; V operands (bf16: per 32-dim group m, two dims x
+    // four tokens; FP8: per output MFMA n, one dim x four tokens) as bf16
+    uint4_v kop[D / 32];
+    constexpr int NVO = FP8 ? D / 16 : D / 32;
+    std::conditional_t<FP8, uint2_v, uint4_v> vop[NVO];
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
-      if constexpr (FP8) {
-        kop[kk] = fp8_widen8(t.k[kk]);
-        vop[kk] = fp8_widen8(t.v[kk]);
-      } else {
-        kop[kk] = t.k[kk];
-        vop[kk] = t.v[kk];
-      }
+      if constexpr (FP8) kop[kk] = fp8_widen8(t.k[kk]);
+      else kop[kk] = t.k[kk];
+    }
+#pragma unroll
+    for (int i = 0; i < NVO; ++i) {
+      if constexpr (FP8) vop[i] = fp8_widen4(t.v[i >> 2][i & 3]);
+      else vop[i] = t.v[i];
     }
     float4_v sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -203,11 +257,13 @@ struct MfmaRow {
         vm[half] = (a ? 0xffffu : 0u) | (b ? 0xffff0000u : 0u);
       }
 #pragma unroll
-      for (int m = 0; m < D / 32; ++m) {
-        vop[m].x &= vm[0];
-        vop[m].y &= vm[1];
-        vop[m].z &= vm[0];
-        vop[m].w &= vm[1];
+      for (int i = 0; i < NVO; ++i) {
+        vop[i].x &= vm[0];
+        vop[i].y &= vm[1];
+        if constexpr (!FP8) {
+          vop[i].z &= vm[0];
+          vop[i].w &= vm[1];
+        }
       }
     }
     // The running max is raised only when a score exceeds it by more than
@@ -238,15 +294,24 @@ struct MfmaRow {
     const unsigned l23 = pack_bf16x2(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
     const short4_v pa_hi = __builtin_bit_cast(short4_v, uint2_v{h01, h23});
     const short4_v pa_lo = __builtin_bit_cast(short4_v, uint2_v{l01, l23});
+    if constexpr (FP8) {
 #pragma unroll
-    for (int m = 0; m < D / 32; ++m) {
-      const short8_v vv = __builtin_bit_cast(short8_v, vop[m]);
-      const short4_v v0 = __builtin_shufflevector(vv, vv, 0, 1, 2, 3);
-      const short4_v v1 = __builtin_shufflevector(vv, vv, 4, 5, 6, 7);
-      acc[2 * m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa_hi, v0, acc[2 * m], 0, 0, 0);
-      acc[2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa_hi, v1, acc[2 * m + 1], 0, 0, 0);
-      acc[2 * m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa_lo, v0, acc[2 * m], 0, 0, 0);
-      acc[2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa_lo, v1, acc[2 * m + 1], 0, 0, 0);
+      for (int n = 0; n < D / 16; ++n) {
+        const short4_v vn = __builtin_bit_cast(short4_v, vop[n]);
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa_hi, vn, acc[n], 0, 0, 0);
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa_lo, vn, acc[n], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < D / 32; ++m) {
+        const short8_v vv = __builtin_bit_cast(short8_v, vop[m]);
+        const short4_v v0 = __builtin_shufflevector(vv, vv, 0, 1, 2, 3);
+        const short4_v v1 = __builtin_shufflevector(vv, vv, 4, 5, 6, 7);
+        acc[2 * m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa_hi, v0, acc[2 * m], 0, 0, 0);
+        acc[2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa_hi, v1, acc[2 * m + 1], 0, 0, 0);
+        acc[2 * m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa_lo, v0, acc[2 * m], 0, 0, 0);
+        acc[2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa_lo, v1, acc[2 * m + 1], 0, 0, 0);
+      }
     }
   }
 };
