@@ -23,6 +23,7 @@
 // non-temporal loads (NT) when no block is listed by two rows, each line
 // then being read once, and with cached loads when rows share blocks.
 #include "mfma_tile.h"
+#include "prefill_common.h"
 
 namespace kvp {
 namespace {
@@ -132,363 +133,48 @@ struct StreamTile {
 // and the attention uses those codes.
 // NT: the tiles are read with non-temporal loads (no block of the batch is
 // listed by two rows), else with cached ones.
+// LDS of one streaming workgroup.
+template <int BS>
+struct StreamLds {
+  int pre[kMaxStreamSeqs + 1];               // pre[s] = tiles of sequences < s
+  uint8_t t0s[BS ? kMaxStreamSeqs : 1];      // the first attended tile's place in its block
+  int wsum[kWaves];
+  int ctxs[kMaxStreamSeqs];                  // seq_lens, read once: the rows' spans come from here
+};
+
 template <int D, int DEPTH, bool FUSED, bool FP8, int BS, bool NT>  // BS = log2(block size / 16)
 __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stream_kernel(const DecodeParams P) {
-  constexpr int NBUF = DEPTH + 1;
-  __shared__ int pre[kMaxStreamSeqs + 1];  // pre[s] = tiles of sequences < s
-  __shared__ uint8_t t0s[BS ? kMaxStreamSeqs : 1];  // the first attended tile's place in its block
-  __shared__ int wsum[kWaves];
-  __shared__ int ctxs[kMaxStreamSeqs];  // seq_lens, read once: the rows' spans come from here
-  const int ptiles = P.prefix_blocks << BS;  // tiles of the shared prefix (cascade)
-  const int S = P.num_seqs;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  __shared__ StreamLds<BS> lds;
+  StreamLds<BS>& L = lds;
+  const int wg = blockIdx.x, nwg = gridDim.x;
+#include "stream_body.inc"
+}
 
-  // Tiles per sequence and their prefix sums: each thread a contiguous run
-  // of sequences, a wave scan of the runs, then the waves' totals.
-  {
-    const int per = (S + kThreads - 1) / kThreads;
-    const int s0 = threadIdx.x * per;
-    int local = 0;
-    for (int i = 0; i < per; ++i) {
-      const int s = s0 + i;
-      if (s < S) {
-        const int ctx = P.seq_lens[s];
-        ctxs[s] = ctx;
-        const RowSpan rs = row_span(ctx, P.window, P.max_blocks, BS);
-        const int nb = max(rs.nblocks - ptiles, 0);
-        pre[s + 1] = nb;
-        if constexpr (BS != 0) t0s[s] = (uint8_t)rs.t0;
-        local += nb;
-      }
-    }
-    const int incl = wave_scan(local, lane);
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    int run = incl - local;
-    for (int w = 0; w < wave; ++w) run += wsum[w];
-    if (threadIdx.x == 0) pre[0] = 0;
-    for (int i = 0; i < per; ++i) {
-      const int s = s0 + i;
-      if (s < S) {
-        run += pre[s + 1];
-        pre[s + 1] = run;
-      }
-    }
-    __syncthreads();
+// Cascade decode in one launch: the first P.stream_wgs workgroups stream the
+// private tails (the body of decode_stream_kernel), the rest run the
+// shared-prefix pass (the prefill body over the prefix's key chunks).
+// Workgroups start in index order, so the prefix workgroups take the
+// compute units that streaming workgroups leave as they finish: the
+// MFMA-bound prefix pass fills the tail of the memory-bound streaming phase
+// instead of running before it.  The two share one LDS allocation.
+template <int D, int DEPTH, bool FUSED, bool FP8, int BS, bool NT>
+__global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_cascade_kernel(const DecodeParams P,
+                                                                                            const PrefillParams PF) {
+  __shared__ union {
+    StreamLds<BS> s;
+    pf::PfLds<D> p;
+  } lds;
+  if ((int)blockIdx.x < P.stream_wgs) {
+    StreamLds<BS>& L = lds.s;
+    const int wg = blockIdx.x, nwg = P.stream_wgs;
+#include "stream_body.inc"
+  } else {
+    using namespace pf;
+    constexpr bool PREFIX = true;
+    PfLds<D>& L = lds.p;
+    const int wg = (int)blockIdx.x - P.stream_wgs;
+#include "prefill_body.inc"
   }
-  const int per_row = pre[S];
-  const int HG = P.num_kv_heads * P.qgroups;
-  const long long T = (long long)per_row * HG;
-
-  if (blockIdx.x == 0) {
-    // publish the prefix sums for the merge pass; zero the rows of empty
-    // sequences (with a shared prefix the merge pass writes every row)
-    for (int i = threadIdx.x; i <= S; i += kThreads) P.prefix[i] = pre[i];
-    if (P.prefix_blocks == 0)  // each thread the empty rows among sequences t, t + 256, ...
-      for (int s = threadIdx.x; s < S; s += kThreads)
-        if (pre[s + 1] == pre[s]) {
-          uint4_v* o = (uint4_v*)((uint16_t*)P.out + (size_t)s * P.num_q_heads * D);
-          for (int i = 0; i < P.num_q_heads * D / 8; ++i) o[i] = uint4_v{0, 0, 0, 0};
-        }
-  }
-
-  const long long W = (long long)gridDim.x * kWaves;
-  const long long widx = (long long)xcd_major_index(blockIdx.x, gridDim.x) * kWaves + wave;
-  const long long t_begin = floor_div(widx * T, W), t_end = floor_div((widx + 1) * T, W);
-  const int n_tiles = (int)(t_end - t_begin);
-  if (n_tiles <= 0) return;
-
-  const void* pool = P.pool_layer;
-  const uint16_t* q = (const uint16_t*)P.q;
-
-  auto row_at = [&](long long t) {  // row holding tile t
-    RowCtx r;
-    r.hg = (int)(t / per_row);
-    const int rr = (int)(t - (long long)r.hg * per_row);
-    int lo = 0, hi = S;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (pre[mid] <= rr) lo = mid; else hi = mid;
-    }
-    r.s = lo;
-    r.nb = pre[lo + 1] - pre[lo];
-    r.a = (long long)r.hg * per_row + pre[lo];
-    return r;
-  };
-  auto row_after = [&](const RowCtx& r) {  // next non-empty row of the work list
-    return row_at(r.a + r.nb < T ? r.a + r.nb : T - 1);
-  };
-  auto head0 = [&](int hg) {
-    const int kvh = hg / P.qgroups;
-    return kvh * P.group + (hg - kvh * P.qgroups) * P.heads_per_wg;
-  };
-  auto heads = [&](int hg) {
-    const int kvh = hg / P.qgroups;
-    return min(P.heads_per_wg, P.group - (hg - kvh * P.qgroups) * P.heads_per_wg);
-  };
-
-  // Table entry holding tile j (counted after the shared prefix) of sequence
-  // s's row; t0 is the row's first tile in its block.
-  auto tid = [&](int s, int t0, int j) { return P.block_tables[(size_t)s * P.max_blocks + ((t0 + ptiles + j) >> BS)]; };
-  auto t0_of = [&](int s) { return BS ? (int)t0s[s] : 0; };
-
-  // ---- issue side: walks the range DEPTH tiles ahead of the compute ----
-  RowCtx ir = row_at(t_begin);  // row of the next tile to issue
-  int ij = (int)(t_begin - ir.a);
-  int irow_id = 0;
-  int it0 = t0_of(ir.s);
-  int ids_a = ij + lane < ir.nb ? tid(ir.s, it0, ij + lane) : 0;            // blocks of tiles ij .. ij+63
-  int ids_b = ij + 64 + lane < ir.nb ? tid(ir.s, it0, ij + 64 + lane) : 0;  // tiles ij+64 .. ij+127
-  int ids_base = ij;                                                         // tile held by lane 0 of ids_a
-  RowCtx nr = row_after(ir);                                                 // the row after, prefetched
-  int nt0 = t0_of(nr.s);
-  int ids_n = lane < nr.nb ? tid(nr.s, nt0, lane) : 0;
-  constexpr int SUB = (1 << BS) - 1;
-  MfmaLanes ila = mfma_lanes<D, BS, FP8>(P.num_kv_heads, ir.hg / P.qgroups, lane);
-  int issued = 0;
-
-  auto issue = [&](StreamTile<D, FP8>& x) {
-    if (issued >= n_tiles) {  // past the range: loads of a line just read (the current row's queries)
-      mfma_issue_hot(x.t, q + ((size_t)ir.s * P.num_q_heads + head0(ir.hg)) * D);
-      x.j = -1;
-      return;
-    }
-    if (ij == ir.nb) {  // row change: the prefetched row becomes current
-      ir = nr;
-      ij = 0;
-      ++irow_id;
-      it0 = nt0;
-      ids_a = ids_n;
-      ids_b = 64 + lane < ir.nb ? tid(ir.s, it0, 64 + lane) : 0;
-      ids_base = 0;
-      nr = row_after(ir);
-      nt0 = t0_of(nr.s);
-      ids_n = lane < nr.nb ? tid(nr.s, nt0, lane) : 0;
-      ila = mfma_lanes<D, BS, FP8>(P.num_kv_heads, ir.hg / P.qgroups, lane);
-    } else if (ij - ids_base == 64) {  // next chunk of 64 tiles: rotate, fetch the one after
-      ids_a = ids_b;
-      ids_base += 64;
-      ids_b = ids_base + 64 + lane < ir.nb ? tid(ir.s, it0, ids_base + 64 + lane) : 0;
-    }
-    mfma_issue<BS, NT>(x.t, pool, ila, __builtin_amdgcn_readlane(ids_a, ij - ids_base), (it0 + ptiles + ij) & SUB,
-                       P.num_blocks);
-    x.j = ij;
-    x.row_id = irow_id;
-    ++ij;
-    ++issued;
-  };
-
-  // ---- compute side ----
-  RowCtx cr = row_at(t_begin);
-  int crow_id = 0;
-  int c_h0 = head0(cr.hg), c_nh = heads(cr.hg);
-  RowSpan crs = row_span(ctxs[cr.s], P.window, P.max_blocks, BS);
-  MfmaRow<D> st;
-  st.template load_q<FP8>(q, (size_t)cr.s * P.num_q_heads + c_h0, c_nh, lane);
-  st.reset();
-  // queries and length of the next row, fetched ahead
-  RowCtx qn = row_after(cr);
-  int ctx_next = ctxs[qn.s];
-  uint4_v q_next[D / 32];
-  {
-    const int g = lane & 15, nh_n = heads(qn.hg);
-    const uint16_t* qp = q + ((size_t)qn.s * P.num_q_heads + head0(qn.hg) + g) * D;
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk)
-      q_next[kk] = g < nh_n ? *(const uint4_v*)(qp + qk_dim<FP8>(kk, lane >> 4)) : uint4_v{0, 0, 0, 0};
-  }
-
-  auto finish_row = [&]() {
-    const float l_tot = rows_sum(st.l_run);
-    const int q4 = lane >> 4;
-    const long long ra = cr.a, rb = cr.a + cr.nb;
-    if (ra >= t_begin && rb <= t_end && P.prefix_blocks > 0) {
-      // a whole tail of a row with a shared prefix: its partial goes to the
-      // row's own slot, for the merge with the prefix pass
-      const size_t pbase = ((size_t)cr.hg * S + cr.s) * P.heads_per_wg;
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int g = 4 * q4 + r4;
-        if (g < c_nh) st.template store_partial<FP8>(P.row_o + (pbase + g) * D, r4, lane);
-      }
-      if (lane < c_nh) {
-        P.row_ml[(pbase + lane) * 2 + 0] = st.m_run;
-        P.row_ml[(pbase + lane) * 2 + 1] = l_tot;
-      }
-    } else if (ra >= t_begin && rb <= t_end) {
-      // the whole row is here: normalise and store
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int g = 4 * q4 + r4;
-        const float lg = __shfl(l_tot, g);
-        const float inv = lg > 0.f ? P.v_scale / lg : 0.f;
-        if (g < c_nh)
-          st.template store_out<FP8>((uint16_t*)P.out + ((size_t)cr.s * P.num_q_heads + c_h0 + g) * D, r4, inv, lane);
-      }
-    } else {
-      const int slot = ra <= t_begin ? 0 : 1;
-      const size_t pbase = (size_t)(widx * 2 + slot) * P.heads_per_wg;
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int g = 4 * q4 + r4;
-        if (g < c_nh) st.template store_partial<FP8>(P.part_o + (pbase + g) * D, r4, lane);
-      }
-      if (lane < c_nh) *(float2*)(P.part_ml + (pbase + lane) * 2) = make_float2(st.m_run, l_tot);
-    }
-  };
-
-  // The new token of the current and of the next row (FUSED only): lanes
-  // 0..D/8-1 hold its key (8 dims each), lanes 0..D/2-1 its value (2 dims
-  // each), every lane its slot as loaded.  Nothing reads them before the
-  // row's last tile, so the loads never hold up the tile loads behind them.
-  uint4_v kn = {0, 0, 0, 0}, kn_next = {0, 0, 0, 0};
-  unsigned vn = 0, vn_next = 0;
-  int slot_c = -1, slot_next = -1;
-  auto load_new = [&](const RowCtx& r, uint4_v& kd, unsigned& vd, int& sd) {
-    if constexpr (FUSED) {
-      sd = P.slot_mapping[r.s];
-      const size_t tok = ((size_t)r.s * P.num_kv_heads + r.hg / P.qgroups) * D;
-      kd = lane < D / 8 ? ((const uint4_v*)((const uint16_t*)P.k_new + tok))[lane] : uint4_v{0, 0, 0, 0};
-      vd = lane < D / 2 ? ((const unsigned*)((const uint16_t*)P.v_new + tok))[lane] : 0u;
-    }
-  };
-  load_new(cr, kn, vn, slot_c);
-  load_new(qn, kn_next, vn_next, slot_next);
-
-  // The row's last block holds the new token at table slot send - 1: put
-  // its key and value into this wave's operands (layouts of mfma_tile.h),
-  // and store them into the pool once per KV head.
-  auto put_new = [&](MfmaTiles<D, FP8>& t, int slot) {
-    const int o = (crs.start_off + crs.n - 1) & (kBlock - 1);
-    const int q4 = lane >> 4, j = lane & 15;
-    constexpr int B = kBlock << BS;  // tokens per block
-    const int kvh = cr.hg / P.qgroups, b = slot >> (4 + BS), off = slot & (B - 1);
-    const bool writer = cr.hg % P.qgroups == 0;
-    const size_t blk = (size_t)b * 2 * P.num_kv_heads * B * D;
-    const size_t kt = blk + (size_t)kvh * B * D, vt = blk + (size_t)(P.num_kv_heads + kvh) * B * D;
-    const int e = ((off >> 2) * D + 2 * lane) * 4 + (off & 3);  // this lane's first V element
-    if constexpr (FP8) {
-      const uint2_v kc = fp8_quant8(kn, P.inv_k_scale);  // codes of dims 8 lane .. +7
-      const unsigned vc = fp8_quant2(vn, P.inv_v_scale);  // codes of dims 2 lane, +1
-#pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) {
-        const int src = qk_dim<true>(kk, q4) >> 3;  // lane holding the codes of MFMA kk's dims
-        const uint2_v v = {(unsigned)__shfl((int)kc.x, src), (unsigned)__shfl((int)kc.y, src)};
-        if (j == o) t.k[kk] = v;
-      }
-      const int sh = 8 * (o & 3);
-      const unsigned keep = ~(0xffu << sh);
-      // word e of t.v[h] holds dim 64 h + 4 j + e (its four tokens' codes)
-#pragma unroll
-      for (int h = 0; h < D / 64; ++h) {
-        const unsigned na = (unsigned)__shfl((int)vc, 32 * h + 2 * j);      // dims 64 h + 4 j (byte 0), +1 (byte 1)
-        const unsigned nb = (unsigned)__shfl((int)vc, 32 * h + 2 * j + 1);  // dims 64 h + 4 j + 2, +3
-        if (q4 == (o >> 2)) {
-          t.v[h].x = (t.v[h].x & keep) | ((na & 0xffu) << sh);
-          t.v[h].y = (t.v[h].y & keep) | (((na >> 8) & 0xffu) << sh);
-          t.v[h].z = (t.v[h].z & keep) | ((nb & 0xffu) << sh);
-          t.v[h].w = (t.v[h].w & keep) | (((nb >> 8) & 0xffu) << sh);
-        }
-      }
-      if (writer) {
-        uint8_t* pl = (uint8_t*)P.pool_layer;
-        if (lane < D / 8) *(uint2_v*)(pl + kt + off * D + 8 * lane) = kc;
-        if (lane < D / 2) {
-          pl[vt + e] = (uint8_t)(vc & 0xffu);
-          pl[vt + e + 4] = (uint8_t)((vc >> 8) & 0xffu);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) {
-        const int src = qk_dim<false>(kk, q4) >> 3;  // lane holding dims 32 kk + 8 q4 .. +7
-        const uint4_v v = {(unsigned)__shfl((int)kn.x, src), (unsigned)__shfl((int)kn.y, src),
-                           (unsigned)__shfl((int)kn.z, src), (unsigned)__shfl((int)kn.w, src)};
-        if (j == o) t.k[kk] = v;
-      }
-      const bool hi = (o & 1) != 0;
-      const unsigned keep = hi ? 0x0000ffffu : 0xffff0000u;
-      const int sh = hi ? 16 : 0;
-#pragma unroll
-      for (int m = 0; m < D / 32; ++m) {
-        const unsigned nv = (unsigned)__shfl((int)vn, 16 * m + j);  // dims 32 m + 2 j (low half), +1
-        if (q4 == (o >> 2)) {
-          const unsigned d0 = (nv & 0xffffu) << sh, d1 = (nv >> 16) << sh;
-          if ((o & 2) == 0) {
-            t.v[m].x = (t.v[m].x & keep) | d0;
-            t.v[m].z = (t.v[m].z & keep) | d1;
-          } else {
-            t.v[m].y = (t.v[m].y & keep) | d0;
-            t.v[m].w = (t.v[m].w & keep) | d1;
-          }
-        }
-      }
-      if (writer) {
-        uint16_t* pl = (uint16_t*)P.pool_layer;
-        if (lane < D / 8) *(uint4_v*)(pl + kt + off * D + 8 * lane) = kn;
-        if (lane < D / 2) {
-          pl[vt + e] = (uint16_t)(vn & 0xffffu);
-          pl[vt + e + 4] = (uint16_t)(vn >> 16);
-        }
-      }
-    }
-  };
-
-  auto compute = [&](StreamTile<D, FP8>& x) {
-    if (x.row_id != crow_id) {  // first tile of the next row
-      finish_row();
-      cr = qn;
-      if constexpr (FUSED) {
-        kn = kn_next;
-        vn = vn_next;
-        slot_c = slot_next;
-      }
-      ++crow_id;
-      c_h0 = head0(cr.hg);
-      c_nh = heads(cr.hg);
-      crs = row_span(ctx_next, P.window, P.max_blocks, BS);
-#pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) st.qop[kk] = q_next[kk];
-      st.reset();
-      qn = row_after(cr);
-      ctx_next = ctxs[qn.s];
-      const int g = lane & 15, nh_n = heads(qn.hg);
-      const uint16_t* qp = q + ((size_t)qn.s * P.num_q_heads + head0(qn.hg) + g) * D;
-#pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk)
-        q_next[kk] = g < nh_n ? *(const uint4_v*)(qp + qk_dim<FP8>(kk, lane >> 4)) : uint4_v{0, 0, 0, 0};
-      load_new(qn, kn_next, vn_next, slot_next);
-    }
-    const int J = ptiles + x.j;  // the tile's place in the row span
-    if constexpr (FUSED) {
-      if (J == crs.nblocks - 1) {
-        // a slot outside the pool (or negative: no new token) writes nothing
-        const int sl = __builtin_amdgcn_readfirstlane(slot_c);
-        if (sl >= 0 && sl < (P.num_blocks << (4 + BS))) put_new(x.t, sl);
-      }
-    }
-    st.step(x.t, J, crs.start_off, crs.start_off + crs.n, crs.nblocks, P.scale_log2, lane);
-  };
-
-  StreamTile<D, FP8> buf[NBUF];
-#pragma unroll
-  for (int d = 0; d < DEPTH; ++d) {
-    issue(buf[d]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  for (int k0 = 0; k0 < n_tiles; k0 += NBUF) {
-#pragma unroll
-    for (int u = 0; u < NBUF; ++u) {
-      if (k0 + u >= n_tiles) break;
-      __builtin_amdgcn_s_setprio(1);  // the next tile's loads go out ahead of the other wave's compute
-      issue(buf[(u + DEPTH) % NBUF]);
-      __builtin_amdgcn_s_setprio(0);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(buf[u]);
-    }
-  }
-  finish_row();
 }
 
 // Merge of the rows cut by range boundaries.  One wave per (sequence,
@@ -592,9 +278,9 @@ __global__ __launch_bounds__(256) void decode_stream_reduce_kernel(const DecodeP
   for (int e = 0; e < PER; ++e) out[lane + 64 * e] = bf16_rne(num[e] * inv);
 }
 
-// The shared-prefix pass on the prefill kernel: all S * G decode queries of
-// a KV head against the prefix, key chunk by key chunk.
-hipError_t launch_prefix(const DecodeParams& p, int head_dim, hipStream_t stream) {
+// Arguments of the shared-prefix pass: all S * G decode queries of a KV
+// head against the prefix, key chunk by key chunk.
+PrefillParams prefix_params(const DecodeParams& p) {
   PrefillParams f{};
   f.pool_layer = p.pool_layer;
   f.q = p.q;
@@ -615,12 +301,20 @@ hipError_t launch_prefix(const DecodeParams& p, int head_dim, hipStream_t stream
   f.prefix_chunk = p.prefix_chunk;
   f.pre_o = p.pre_o;
   f.pre_ml = p.pre_ml;
-  return launch_prefix_pass(f, head_dim, p.kv_fp8 != 0, stream);
+  return f;
 }
 
 template <int D, int DEPTH, bool FP8, int BS, bool NT>
 void launch_sk(const DecodeParams& p, hipStream_t stream) {
-  if (p.slot_mapping) {
+  if (p.prefix_blocks > 0) {
+    const PrefillParams f = prefix_params(p);
+    const unsigned grid = (unsigned)p.stream_wgs + (unsigned)(f.num_kv_heads * f.qtiles * f.prefix_pieces);
+    if (p.slot_mapping)
+      hipLaunchKernelGGL((decode_cascade_kernel<D, 1, true, FP8, BS, NT>), dim3(grid), dim3(kThreads), 0, stream, p, f);
+    else
+      hipLaunchKernelGGL((decode_cascade_kernel<D, DEPTH, false, FP8, BS, NT>), dim3(grid), dim3(kThreads), 0, stream, p,
+                         f);
+  } else if (p.slot_mapping) {
     // the fused step runs at ring depth 1: the new token takes the registers of a deeper ring
     hipLaunchKernelGGL((decode_stream_kernel<D, 1, true, FP8, BS, NT>), dim3(p.stream_wgs), dim3(kThreads), 0, stream, p);
   } else {
@@ -632,10 +326,9 @@ void launch_sk(const DecodeParams& p, hipStream_t stream) {
 template <int D, int DEPTH, bool FP8, int BS>
 hipError_t launch_sd(const DecodeParams& p, hipStream_t stream) {
   if (p.slot_mapping && DEPTH != 1) return hipErrorInvalidValue;
-  if (p.prefix_blocks > 0) {
-    const hipError_t e = launch_prefix(p, D, stream);
-    if (e != hipSuccess) return e;
-  }
+  if (p.prefix_blocks > 0 && (long long)p.num_kv_heads * ((p.num_seqs * p.group + 127) / 128) * p.prefix_pieces +
+                                     p.stream_wgs > 0x7fffffffLL)
+    return hipErrorInvalidValue;
   if (p.nt_loads) launch_sk<D, DEPTH, FP8, BS, true>(p, stream);
   else launch_sk<D, DEPTH, FP8, BS, false>(p, stream);
   hipError_t e = hipGetLastError();
@@ -660,24 +353,40 @@ hipError_t launch_st(const DecodeParams& p, hipStream_t stream) {
   return p.bshift ? launch_s<D, false, 1>(p, stream) : launch_s<D, false, 0>(p, stream);
 }
 
-template <int D, bool FP8, int BS, bool NT>
+template <int D, bool FP8, int BS, bool NT, bool CASCADE>
 const void* symbol_of(int depth, bool fused) {
-  if (fused) return depth == 1 ? (const void*)decode_stream_kernel<D, 1, true, FP8, BS, NT> : nullptr;
-  return depth == 1 ? (const void*)decode_stream_kernel<D, 1, false, FP8, BS, NT>
-                    : (const void*)decode_stream_kernel<D, 2, false, FP8, BS, NT>;
+  if constexpr (CASCADE) {
+    if (fused) return depth == 1 ? (const void*)decode_cascade_kernel<D, 1, true, FP8, BS, NT> : nullptr;
+    return depth == 1 ? (const void*)decode_cascade_kernel<D, 1, false, FP8, BS, NT>
+                      : (const void*)decode_cascade_kernel<D, 2, false, FP8, BS, NT>;
+  } else {
+    if (fused) return depth == 1 ? (const void*)decode_stream_kernel<D, 1, true, FP8, BS, NT> : nullptr;
+    return depth == 1 ? (const void*)decode_stream_kernel<D, 1, false, FP8, BS, NT>
+                      : (const void*)decode_stream_kernel<D, 2, false, FP8, BS, NT>;
+  }
 }
 
-template <int D, bool NT>
+template <int D, bool NT, bool CASCADE>
 const void* symbol_d(int depth, bool fused, bool fp8, int bshift) {
-  if (fp8) return bshift ? symbol_of<D, true, 1, NT>(depth, fused) : symbol_of<D, true, 0, NT>(depth, fused);
-  return bshift ? symbol_of<D, false, 1, NT>(depth, fused) : symbol_of<D, false, 0, NT>(depth, fused);
+  if (fp8)
+    return bshift ? symbol_of<D, true, 1, NT, CASCADE>(depth, fused) : symbol_of<D, true, 0, NT, CASCADE>(depth, fused);
+  return bshift ? symbol_of<D, false, 1, NT, CASCADE>(depth, fused) : symbol_of<D, false, 0, NT, CASCADE>(depth, fused);
+}
+
+template <bool CASCADE>
+const void* symbol_c(int head_dim, int depth, bool fused, bool fp8, int bshift, bool nt) {
+  if (nt)
+    return head_dim == 128 ? symbol_d<128, true, CASCADE>(depth, fused, fp8, bshift)
+                           : symbol_d<64, true, CASCADE>(depth, fused, fp8, bshift);
+  return head_dim == 128 ? symbol_d<128, false, CASCADE>(depth, fused, fp8, bshift)
+                         : symbol_d<64, false, CASCADE>(depth, fused, fp8, bshift);
 }
 
 }  // namespace
 
-const void* stream_kernel_symbol(int head_dim, int depth, bool fused, bool fp8, int bshift, bool nt) {
-  if (nt) return head_dim == 128 ? symbol_d<128, true>(depth, fused, fp8, bshift) : symbol_d<64, true>(depth, fused, fp8, bshift);
-  return head_dim == 128 ? symbol_d<128, false>(depth, fused, fp8, bshift) : symbol_d<64, false>(depth, fused, fp8, bshift);
+const void* stream_kernel_symbol(int head_dim, int depth, bool fused, bool fp8, int bshift, bool nt, bool cascade) {
+  return cascade ? symbol_c<true>(head_dim, depth, fused, fp8, bshift, nt)
+                 : symbol_c<false>(head_dim, depth, fused, fp8, bshift, nt);
 }
 
 hipError_t launch_decode_stream(const DecodeParams& p, int head_dim, hipStream_t stream) {

@@ -132,9 +132,9 @@ hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t s
 hipError_t launch_decode_reduce(const DecodeParams& p, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_decode_stream(const DecodeParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, bool fp8, hipStream_t stream);
-hipError_t launch_prefix_pass(const PrefillParams& p, int head_dim, bool fp8, hipStream_t stream);
-// The streaming kernel instance a launch would use (for occupancy queries);
-// nullptr for one that is never launched (the fused step runs at depth 1).
-const void* stream_kernel_symbol(int head_dim, int depth, bool fused, bool fp8, int bshift, bool nt);
+// The streaming kernel instance a launch would use (for occupancy queries;
+// cascade: the one that also runs the shared-prefix pass); nullptr for one
+// that is never launched (the fused step runs at depth 1).
+const void* stream_kernel_symbol(int head_dim, int depth, bool fused, bool fp8, int bshift, bool nt, bool cascade);
 
 }  // namespace kvp

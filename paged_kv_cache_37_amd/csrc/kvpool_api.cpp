@@ -157,27 +157,31 @@ int32_t cache_write(kvp_pool pool, int32_t layer, const void* k_new, const void*
 }
 
 // Resident workgroups of the streaming kernel on the current device:
-// compute units x workgroups per compute unit at the kernel's occupancy.
-// 0 if there is no device to ask.
-static int32_t stream_workgroups(int32_t head_dim, int32_t depth, bool fused, bool fp8, int32_t bshift) {
+// compute units x workgroups per compute unit at the kernel's occupancy
+// (cascade: the kernel that also runs the shared-prefix pass).  0 if there
+// is no device to ask.
+static int32_t stream_workgroups(int32_t head_dim, int32_t depth, bool fused, bool fp8, int32_t bshift,
+                                 bool cascade = false) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   static thread_local int cached_dev = -1, cached_d = 0, cached_depth = 0, cached_wgs = 0, cached_bs = 0;
-  static thread_local bool cached_fused = false, cached_fp8 = false;
+  static thread_local bool cached_fused = false, cached_fp8 = false, cached_cascade = false;
   if (dev == cached_dev && head_dim == cached_d && depth == cached_depth && fused == cached_fused &&
-      fp8 == cached_fp8 && bshift == cached_bs)
+      fp8 == cached_fp8 && bshift == cached_bs && cascade == cached_cascade)
     return cached_wgs;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
   // the cached-load and non-temporal instances launch the same grid (the
   // smaller of their occupancies), so one workspace size serves both
+  per_cu = 1 << 30;
   for (bool nt : {true, false}) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kvp::stream_kernel_symbol(head_dim, depth, fused, fp8, bshift, nt),
-                                                     kvp::kThreads, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, kvp::stream_kernel_symbol(head_dim, depth, fused, fp8, bshift, nt, cascade), kvp::kThreads, 0) !=
+            hipSuccess ||
         n <= 0)
       return 0;
-    per_cu = nt ? n : std::min(per_cu, n);
+    per_cu = std::min(per_cu, n);
   }
   cached_dev = dev;
   cached_d = head_dim;
@@ -185,6 +189,7 @@ static int32_t stream_workgroups(int32_t head_dim, int32_t depth, bool fused, bo
   cached_fused = fused;
   cached_fp8 = fp8;
   cached_bs = bshift;
+  cached_cascade = cascade;
   cached_wgs = cus * per_cu;
   return cached_wgs;
 }
@@ -367,11 +372,15 @@ size_t paged_decode_workspace_bytes(kvp_pool pool, int32_t num_seqs, int32_t num
     if (plan(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, v, &p, &path) != KVP_OK) continue;
     size_t n = path == PATH_STREAM ? stream_workspace(p, pool->desc.head_dim, true).total
                                    : grid_workspace(p, pool->desc.head_dim, &a, &a);
-    if (path == PATH_STREAM) {  // the fused step's grid (its own occupancy) must fit too
+    if (path == PATH_STREAM) {  // the grids of the fused step and of the cascade (their own occupancies) must fit too
       const bool fp8 = pool->desc.dtype == KVP_FP8_E4M3;
-      p.stream_wgs = stream_workgroups(pool->desc.head_dim, 1, true, fp8, p.bshift);
-      const size_t nf = stream_workspace(p, pool->desc.head_dim, true).total;
-      if (nf > n) n = nf;
+      for (int fused = 0; fused < 2; ++fused)
+        for (int cascade = 0; cascade < 2; ++cascade) {
+          p.stream_wgs = stream_workgroups(pool->desc.head_dim, fused ? 1 : p.depth, fused != 0, fp8, p.bshift,
+                                           cascade != 0);
+          const size_t nf = stream_workspace(p, pool->desc.head_dim, true).total;
+          if (nf > n) n = nf;
+        }
     }
     if (n > need) need = n;
   }
@@ -420,6 +429,10 @@ static int32_t decode(kvp_pool pool, const kvp_decode_args* a, const void* k_new
   // the shared-prefix pass is a STREAM feature for full-context rows; elsewhere the hint is ignored
   if (path == PATH_STREAM && a->sliding_window == 0) p.prefix_blocks = a->shared_prefix_blocks;
   if (p.prefix_blocks > 0) {
+    // one launch runs the tails and the prefix pass: the grid of that kernel
+    p.stream_wgs = stream_workgroups(d.head_dim, p.depth, p.slot_mapping != nullptr, d.dtype == KVP_FP8_E4M3, p.bshift,
+                                     true);
+    if (p.stream_wgs <= 0) return fail(KVP_ERR_HIP, "cannot size the streaming grid (no device?)");
     // split the prefix's keys into chunks of whole 4-tile steps (the
     // workspace holds as many pieces as prefix_pieces_wanted gives)
     const int32_t tiles = p.prefix_blocks << p.bshift;
