@@ -41,10 +41,9 @@ PREFILL_METRIC = "paged prefill attention: achieved TFLOP/s (% of dense bf16 MFM
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 (no sparsity)
 DEFAULT_LAYERS = {1: 1, 2: 2, 3: 1, 4: 4, 5: 2, 6: 1}  # layer slices so that each step reads >= ~1 GB
-KERNEL_SOURCES = ("decode_stream.hip", "prefill.hip", "copy_blocks.hip", "decode_mfma.hip",
-                  "decode_valu.hip",
-                  "decode_reduce.hip", "cache_write.hip", "mfma_tile.h", "decode_common.h", "internal.h",
-                  "fp8.h", "kvpool_api.cpp")
+KERNEL_SOURCES = ("decode_stream.hip", "stream_body.inc", "prefill.hip", "prefill_body.inc", "prefill_common.h",
+                  "copy_blocks.hip", "decode_mfma.hip", "decode_valu.hip", "decode_reduce.hip", "cache_write.hip",
+                  "mfma_tile.h", "decode_common.h", "internal.h", "fp8.h", "kvpool_api.cpp")
 
 
 def log(*a):
