@@ -76,11 +76,14 @@ class KVPool:
         check(lib.kv_pool_create(ctypes.byref(self.desc), ctypes.c_void_p(self.storage.data_ptr()),
                                  self.nbytes, ctypes.byref(handle)), "kv_pool_create")
         self.handle = handle
+        # held by the pool itself: at interpreter exit the module's globals
+        # may be cleared before the last pool is collected
+        self._destroy = lib.kv_pool_destroy
 
     def __del__(self):
         h = getattr(self, "handle", None)
         if h is not None and h.value:
-            lib.kv_pool_destroy(h)
+            self._destroy(h)
             self.handle = None
 
     # -- layout helpers (host side; loading and inspecting pools) --------
