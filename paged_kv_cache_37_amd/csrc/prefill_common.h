@@ -60,6 +60,18 @@ constexpr int kStep = 16 * kTiles;   // keys per step (loaded together; computed
 template <bool FP8>
 using Elt = std::conditional_t<FP8, uint8_t, uint16_t>;
 
+// Position of 16-byte chunk c (dims 8c .. 8c + 7) within LDS K row r: the
+// chunk index XOR the row's low bits.  A QK operand read has lane l take
+// chunk 4 kk + l / 16 of row l % 16; unswizzled rows of 256 bytes put all
+// 16 rows on the same banks, and rows padded to 272 bytes still read at
+// half of the LDS rate on gfx950 (measured: 128 of ~250 bytes per clock),
+// while this layout reads at the full rate, and so do the row-wise stores
+// that fill it.
+template <int D>
+__device__ __forceinline__ int k_chunk(int r, int c) {
+  return c ^ (r & (D / 8 - 1));
+}
+
 
 // Wave-wide min / max, returned as a scalar (uniform) value.
 __device__ __forceinline__ int wave_min(int v) {
@@ -78,7 +90,7 @@ __device__ __forceinline__ int wave_max(int v) {
 // that read them.
 template <int D>
 struct PfLds {
-  __align__(16) uint16_t k_s[2][kStep * (D + 8)];  // K rows padded by 16 bytes, so 16 rows hit distinct banks
+  __align__(16) uint16_t k_s[2][kStep * D];        // K rows, 16-byte chunks swizzled (k_chunk)
   __align__(16) uint16_t v_s[2][kStep * D];        // per 32-key round: [4 quads][D][2 tiles][4 keys]
   int lpt_cost[kLptMaxPairs];
   int lpt_pick;
