@@ -111,6 +111,8 @@ struct RowCtx {
   int hg, s;      // head group, sequence
   int nb;         // table entries (tiles) of the row
   long long a;    // first tile of the row in the work list
+  int kvh;        // KV head of the head group
+  int h0, nh;     // its first query head and how many it serves
 };
 
 // Tile ring entry: loads in flight plus the tile's place in its row.
