@@ -85,7 +85,8 @@ __device__ __forceinline__ void merge_round(float& M, float& den, float (&num)[P
 }
 
 // The pieces of a cut row [a, a + nb) of the work list (T tiles over W
-// waves), in wave order.  With T >= W every range holds a tile, so they are
+// waves), in wave order, found from the split alone (the merge uses it
+// when T < W; otherwise the first pass records where each row's pieces are).  With T >= W every range holds a tile, so they are
 // waves w_first .. w_last: the first holds the row as its last row (slot 1)
 // unless its range starts at the row, every later one as its first (slot 0).
 // With T < W a range holds at most one tile, and each of the row's tiles is
@@ -93,6 +94,7 @@ __device__ __forceinline__ void merge_round(float& M, float& den, float (&num)[P
 struct CutPieces {
   long long a, T, W, w_first, w_last;
   int n, slot_first;
+  CutPieces() = default;
   __device__ __forceinline__ CutPieces(long long a_, int nb, long long T_, long long W_) : a(a_), T(T_), W(W_) {
     w_first = floor_div((a + 1) * W - 1, T);
     w_last = floor_div((a + nb) * W - 1, T);
@@ -181,15 +183,17 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_casc
 
 // Merge of the rows cut by range boundaries.  One wave per (sequence,
 // query head): the row's tiles [a, b) were covered by the waves w_first ..
-// w_last; each left its partial in slot 0 (the row held the wave's first
-// tile) or slot 1 (the row was the wave's last).  Rows inside one wave were
-// stored by the first pass.  The partials' loads go out eight at a time.
+// w_last (recorded by the first pass); each left its partial in slot 0 (the
+// row held the wave's first tile) or slot 1 (the row was the wave's last).
+// Rows inside one wave were stored by the first pass.  The partials' loads go out eight at a time.
+// At most 64 VGPRs (8 waves per SIMD): every wave of the largest merge
+// here (256 sequences x 32 heads) is resident at once.
 // With a shared prefix every row is merged here: the prefix pass's piece,
 // then either the row's own slot (a tail inside one wave) or the wave
 // slots (a tail cut by range boundaries); a row with no tail is the prefix
 // piece alone.
 template <int D>
-__global__ __launch_bounds__(256) void decode_stream_reduce_kernel(const DecodeParams P) {
+__global__ __launch_bounds__(256, 8) void decode_stream_reduce_kernel(const DecodeParams P) {
   const int s = blockIdx.y;
   const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (h >= P.num_q_heads) return;
@@ -199,6 +203,12 @@ __global__ __launch_bounds__(256) void decode_stream_reduce_kernel(const DecodeP
   const int kvh = h / P.group, g_in = h - kvh * P.group;
   const int qg = g_in / P.heads_per_wg, hh = g_in - qg * P.heads_per_wg;
   const int hg = kvh * P.qgroups + qg;
+
+  // the row's place in the work list and its pieces (written by the first
+  // pass), loaded first: with a shared prefix the pieces below go out while
+  // they travel
+  const int pre_s = P.prefix[s], nb = P.prefix[s + 1] - pre_s, per_row = P.prefix[S];
+  const int2 cut = *(const int2*)(P.cuts + 2 * ((size_t)hg * S + s));
 
   constexpr int PER = D / 64;
   float M = -INFINITY, den = 0.f, num[PER];
@@ -232,7 +242,6 @@ __global__ __launch_bounds__(256) void decode_stream_reduce_kernel(const DecodeP
     for (int e = 0; e < PER; ++e) ro[e] = P.row_o[rb * D + lane + 64 * e];
     merge_round(M, den, num, m, l, v);
   }
-  const int pre_s = P.prefix[s], nb = P.prefix[s + 1] - pre_s, per_row = P.prefix[S];
   if (nb == 0 && !cascade) return;
   // merge one more piece (max m, sum l, unnormalised o)
   auto add = [&](float m, float l, const float* o) {
@@ -248,19 +257,33 @@ __global__ __launch_bounds__(256) void decode_stream_reduce_kernel(const DecodeP
   if (nb > 0) {
     const long long T = (long long)per_row * P.num_kv_heads * P.qgroups;
     const long long W = (long long)P.stream_wgs * kWaves;
-    const long long a = (long long)hg * per_row + pre_s;
-    const CutPieces pc(a, nb, T, W);
-    if (pc.n == 1) {
+    // With T >= W every wave holds a tile: the pieces are the waves from
+    // the one holding the row's first tile (its recorded piece) to the one
+    // holding its last, no division needed.  With T < W some waves hold
+    // none, and CutPieces locates each of the row's tiles.
+    const bool dense = T >= W;
+    const int first = cut.x;
+    int n = dense ? cut.y - (first >> 1) + 1 : 0;
+    CutPieces pc;
+    if (!dense) {
+      pc = CutPieces((long long)hg * per_row + pre_s, nb, T, W);
+      n = pc.n;
+    }
+    auto slot = [&](int k) -> unsigned {
+      if (dense) return k == 0 ? (unsigned)first : (unsigned)((first >> 1) + k) * 2u;
+      return (unsigned)pc.slot(k);
+    };
+    if (n == 1) {
       if (!cascade) return;  // stored by the first pass
       add(rm, rl, ro);       // the tail one wave held whole
     } else {
       constexpr int CH = kMergeChunk;
-      for (int k0 = 0; k0 < pc.n; k0 += CH) {
+      for (int k0 = 0; k0 < n; k0 += CH) {
         float m[CH], l[CH], v[CH][PER];
 #pragma unroll
         for (int u = 0; u < CH; ++u) {
-          const bool use = k0 + u < pc.n;
-          const size_t pb = (size_t)pc.slot(use ? k0 + u : pc.n - 1) * P.heads_per_wg + hh;
+          const bool use = k0 + u < n;
+          const unsigned pb = slot(use ? k0 + u : n - 1) * (unsigned)P.heads_per_wg + hh;
           const float2 ml = *(const float2*)(P.part_ml + pb * 2);
           m[u] = use ? ml.x : -INFINITY;
           l[u] = use ? ml.y : 0.f;

@@ -38,6 +38,7 @@ struct DecodeParams {
   float scale_log2;             // scale * log2(e): scores are kept in base 2
   int32_t depth;                // blocks of K/V a wave keeps in flight ahead of the one it computes
   int32_t* prefix;              // [S + 1] tiles before each sequence's row     (streaming only)
+  int32_t* cuts;                // [HG][S][2] per row: first piece (wave * 2 + slot), last wave  (streaming only)
   int32_t stream_wgs;           // persistent workgroups of a streaming launch   (streaming only)
   const void* k_new;            // [S][Hkv][D] new token per sequence        (fused write only)
   const void* v_new;            // [S][Hkv][D]                               (fused write only)

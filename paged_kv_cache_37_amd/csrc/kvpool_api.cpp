@@ -318,13 +318,14 @@ static size_t grid_workspace(const kvp::DecodeParams& p, int32_t head_dim, size_
   return *ml_off + rows * 2 * sizeof(float);
 }
 
-// Workspace of the streaming kernel: prefix sums, then
+// Workspace of the streaming kernel: prefix sums, the rows' piece ranges
+// (first piece, last wave), then
 // two partial slots per wave for up to heads_per_wg heads ((max, sum) pairs
 // and outputs), then, for a call with a shared prefix (cascade), the
 // prefix pass's pieces: one per (key chunk, sequence, query head), and one
 // per (row, head) for tails a single wave holds.
 struct StreamLayout {
-  size_t prefix, ml, o, pre_ml, pre_o, row_ml, row_o, total;
+  size_t prefix, cuts, ml, o, pre_ml, pre_o, row_ml, row_o, total;
 };
 
 // Key chunks of the shared-prefix pass: enough that the pass has about as
@@ -345,7 +346,8 @@ static StreamLayout stream_workspace(const kvp::DecodeParams& p, int32_t head_di
   const size_t qh = (size_t)p.num_seqs * p.num_q_heads;
   const size_t rows = (size_t)p.num_kv_heads * p.qgroups * p.num_seqs * p.heads_per_wg;
   L.prefix = 0;
-  L.ml = L.prefix + align256((size_t)(p.num_seqs + 1) * sizeof(int32_t));
+  L.cuts = L.prefix + align256((size_t)(p.num_seqs + 1) * sizeof(int32_t));
+  L.ml = L.cuts + align256((size_t)p.num_kv_heads * p.qgroups * p.num_seqs * 2 * sizeof(int32_t));
   L.o = L.ml + align256(slots * 2 * sizeof(float));
   if (!cascade) {
     L.pre_ml = L.pre_o = L.row_ml = L.row_o = 0;
@@ -456,6 +458,7 @@ static int32_t decode(kvp_pool pool, const kvp_decode_args* a, const void* k_new
     char* w = (char*)a->workspace;
     if (path == PATH_STREAM) {
       p.prefix = (int32_t*)(w + SL.prefix);
+      p.cuts = (int32_t*)(w + SL.cuts);
       p.part_ml = (float*)(w + SL.ml);
       p.part_o = (float*)(w + SL.o);
       p.pre_ml = (float*)(w + SL.pre_ml);
