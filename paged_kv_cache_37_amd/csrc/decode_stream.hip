@@ -94,7 +94,6 @@ __device__ __forceinline__ void merge_round(float& M, float& den, float (&num)[P
 struct CutPieces {
   long long a, T, W, w_first, w_last;
   int n, slot_first;
-  CutPieces() = default;
   __device__ __forceinline__ CutPieces(long long a_, int nb, long long T_, long long W_) : a(a_), T(T_), W(W_) {
     w_first = floor_div((a + 1) * W - 1, T);
     w_last = floor_div((a + nb) * W - 1, T);
@@ -220,26 +219,27 @@ __global__ __launch_bounds__(256, 8) void decode_stream_reduce_kernel(const Deco
   if (cascade) {
     // the prefix pass's pieces (one per key chunk, in chunk order)
     static_assert(kMaxPrefixPieces <= kMergeChunk, "one merge round takes every prefix piece");
-    const size_t qh = (size_t)s * P.num_q_heads + h, pstride = (size_t)S * P.num_q_heads;
+    // (element offsets into the workspace fit 32 bits: the host sizes it)
+    const unsigned qh = (unsigned)s * P.num_q_heads + h, pstride = (unsigned)S * P.num_q_heads;
     float m[kMergeChunk], l[kMergeChunk], v[kMergeChunk][PER];
 #pragma unroll
     for (int u = 0; u < kMergeChunk; ++u) {
       const bool use = u < P.prefix_pieces;
-      const size_t pq = qh + (use ? u : 0) * pstride;
-      const float2 ml = *(const float2*)(P.pre_ml + pq * 2);
+      const unsigned pq = qh + (use ? u : 0) * pstride;
+      const float2 ml = *(const float2*)(P.pre_ml + pq * 2u);
       m[u] = use ? ml.x : -INFINITY;
       l[u] = use ? ml.y : 0.f;
 #pragma unroll
       for (int e = 0; e < PER; ++e) {
-        const float x = P.pre_o[pq * D + lane + 64 * e];
+        const float x = P.pre_o[pq * (unsigned)D + lane + 64 * e];
         v[u][e] = use ? x : 0.f;
       }
     }
-    const size_t rb = ((size_t)hg * S + s) * P.heads_per_wg + hh;
-    rm = P.row_ml[rb * 2];
-    rl = P.row_ml[rb * 2 + 1];
+    const unsigned rb = ((unsigned)hg * S + s) * P.heads_per_wg + hh;
+    rm = P.row_ml[rb * 2u];
+    rl = P.row_ml[rb * 2u + 1u];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) ro[e] = P.row_o[rb * D + lane + 64 * e];
+    for (int e = 0; e < PER; ++e) ro[e] = P.row_o[rb * (unsigned)D + lane + 64 * e];
     merge_round(M, den, num, m, l, v);
   }
   if (nb == 0 && !cascade) return;
@@ -254,46 +254,51 @@ __global__ __launch_bounds__(256, 8) void decode_stream_reduce_kernel(const Deco
     M = Mc;
   };
 
+  // merge the pieces slot(0) .. slot(n - 1) in rounds of kMergeChunk
+  auto merge_pieces = [&](int n, auto slot) {
+    constexpr int CH = kMergeChunk;
+    for (int k0 = 0; k0 < n; k0 += CH) {
+      float m[CH], l[CH], v[CH][PER];
+#pragma unroll
+      for (int u = 0; u < CH; ++u) {
+        const bool use = k0 + u < n;
+        const unsigned pb = slot(use ? k0 + u : n - 1) * (unsigned)P.heads_per_wg + hh;
+        const float2 ml = *(const float2*)(P.part_ml + pb * 2u);
+        m[u] = use ? ml.x : -INFINITY;
+        l[u] = use ? ml.y : 0.f;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+          const float x = P.part_o[pb * (unsigned)D + lane + 64 * e];
+          v[u][e] = use ? x : 0.f;
+        }
+      }
+      merge_round(M, den, num, m, l, v);
+    }
+  };
+
   if (nb > 0) {
     const long long T = (long long)per_row * P.num_kv_heads * P.qgroups;
     const long long W = (long long)P.stream_wgs * kWaves;
-    // With T >= W every wave holds a tile: the pieces are the waves from
-    // the one holding the row's first tile (its recorded piece) to the one
-    // holding its last, no division needed.  With T < W some waves hold
-    // none, and CutPieces locates each of the row's tiles.
-    const bool dense = T >= W;
-    const int first = cut.x;
-    int n = dense ? cut.y - (first >> 1) + 1 : 0;
-    CutPieces pc;
-    if (!dense) {
-      pc = CutPieces((long long)hg * per_row + pre_s, nb, T, W);
-      n = pc.n;
-    }
-    auto slot = [&](int k) -> unsigned {
-      if (dense) return k == 0 ? (unsigned)first : (unsigned)((first >> 1) + k) * 2u;
-      return (unsigned)pc.slot(k);
-    };
-    if (n == 1) {
-      if (!cascade) return;  // stored by the first pass
-      add(rm, rl, ro);       // the tail one wave held whole
+    if (T >= W) {
+      // every wave holds a tile: the pieces are the waves from the one
+      // holding the row's first tile (its recorded piece) to the one holding
+      // its last, every later one in slot 0
+      const unsigned first = (unsigned)cut.x;
+      const int n = cut.y - (int)(first >> 1) + 1;
+      if (n == 1) {
+        if (!cascade) return;  // stored by the first pass
+        add(rm, rl, ro);       // the tail one wave held whole
+      } else {
+        merge_pieces(n, [&](int k) { return k == 0 ? first : ((first >> 1) + (unsigned)k) * 2u; });
+      }
     } else {
-      constexpr int CH = kMergeChunk;
-      for (int k0 = 0; k0 < n; k0 += CH) {
-        float m[CH], l[CH], v[CH][PER];
-#pragma unroll
-        for (int u = 0; u < CH; ++u) {
-          const bool use = k0 + u < n;
-          const unsigned pb = slot(use ? k0 + u : n - 1) * (unsigned)P.heads_per_wg + hh;
-          const float2 ml = *(const float2*)(P.part_ml + pb * 2);
-          m[u] = use ? ml.x : -INFINITY;
-          l[u] = use ? ml.y : 0.f;
-#pragma unroll
-          for (int e = 0; e < PER; ++e) {
-            const float x = P.part_o[pb * D + lane + 64 * e];
-            v[u][e] = use ? x : 0.f;
-          }
-        }
-        merge_round(M, den, num, m, l, v);
+      // some waves hold no tile: CutPieces locates each of the row's tiles
+      const CutPieces pc((long long)hg * per_row + pre_s, nb, T, W);
+      if (pc.n == 1) {
+        if (!cascade) return;
+        add(rm, rl, ro);
+      } else {
+        merge_pieces(pc.n, [&](int k) { return (unsigned)pc.slot(k); });
       }
     }
   }

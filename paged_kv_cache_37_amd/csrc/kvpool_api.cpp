@@ -446,6 +446,8 @@ static int32_t decode(kvp_pool pool, const kvp_decode_args* a, const void* k_new
   size_t o_off = 0, ml_off = 0;
   const StreamLayout SL = path == PATH_STREAM ? stream_workspace(p, d.head_dim, p.prefix_blocks > 0) : StreamLayout{};
   const size_t ws = path == PATH_STREAM ? SL.total : grid_workspace(p, d.head_dim, &o_off, &ml_off);
+  if (path == PATH_STREAM && ws / sizeof(float) >= 0xffffffffull)  // the merge kernel's 32-bit element offsets
+    return fail(KVP_ERR_UNSUPPORTED, "the STREAM variant's workspace would exceed 2^32 floats");
   if (ws > 0) {
     if (scratch && a->workspace_bytes < ws)
       return fail(KVP_ERR_WORKSPACE_TOO_SMALL,
