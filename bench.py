@@ -537,8 +537,13 @@ def main() -> int:
         variant = "valu" if w.dtype == "f32" else ("mfma" if args.partition_tokens else "stream")
     path = "cascade" if shared and variant == "stream" and not w.window else variant
     label = f"decode_{path}" if args.unfused else f"decode_{path}_step"
-    kernel = ("paged_decode_attention (decode + merge launches)" if args.unfused else
-              "paged_decode_step (" + ("fused write + decode, merge launches)" if variant == "stream"
+    # the streaming launch merges cut rows itself when no row crosses an XCD
+    # (KV heads a multiple of 8, one head group per KV head, no shared prefix)
+    one_launch = (variant == "stream" and not shared and w.num_kv_heads % 8 == 0
+                  and w.num_q_heads // w.num_kv_heads <= 16 and os.environ.get("KVP_LAUNCH_MERGE", "1") != "0")
+    merge = "merged in the same launch" if one_launch else "merge launches"
+    kernel = (f"paged_decode_attention (decode, {merge})" if args.unfused else
+              "paged_decode_step (" + (f"fused write + decode, {merge})" if variant == "stream"
                                        else "cache_write, decode, merge launches)"))
 
     result = {

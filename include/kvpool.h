@@ -245,7 +245,16 @@ size_t paged_decode_workspace_bytes(kvp_pool pool, int32_t num_seqs, int32_t num
  *   bytes, contents need no initialisation) and a second kernel on the
  *   same stream merges them.  The STREAM variant splits the batch's tiles
  *   evenly over its waves; the rows cut between waves are merged the same
- *   way.  Calls that share one workspace must not overlap.
+ *   way, or, when no row crosses an XCD (num_kv_heads a multiple of 8, at
+ *   most 16 query heads per KV head, no shared prefix), inside the same
+ *   launch by workgroups that start as the streaming ones finish; those
+ *   keep per-call marks in the workspace, written and cleared within each
+ *   call (left zero; marks of other contents are practically never taken
+ *   for a call's own, so no initialisation is needed either).  Calls that
+ *   share one workspace must not overlap.
+ *
+ *   Environment: KVP_LAUNCH_MERGE=0 (read at each call) keeps the separate
+ *   merge kernel.
  *
  *   Environment: KVP_DECODE_DEPTH (1..3 for the MFMA variant, 1..2 for
  *   the others) overrides how many blocks each wave keeps in flight ahead

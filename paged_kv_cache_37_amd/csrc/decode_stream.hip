@@ -145,11 +145,133 @@ struct StreamLds {
   int ctxs[kMaxStreamSeqs];                  // seq_lens, read once: the rows' spans come from here
 };
 
+// Loads of another wave's partial results, through the L2 of this XCD
+// (agent-scope loads miss the compute unit's L1).
+__device__ __forceinline__ float l2_load(const float* p) {
+  return __builtin_bit_cast(float, __hip_atomic_load((const unsigned*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ uint64_t l2_load(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+constexpr int kMergePolls = 1 << 18;  // a bound on each wait for a piece (~0.1 s), far past any wait of a call
+
+// The merge of the cut rows inside the streaming launch (P.merge_wgs > 0),
+// for batches whose rows never cross an XCD: the KV heads split evenly over
+// the 8 XCDs (Hkv % 8 == 0, one head group per KV head) and the streaming
+// grid a multiple of 8 workgroups, so the waves of XCD x (workgroups x, x
+// + 8, ...) stream exactly KV heads [x Hkv / 8, (x + 1) Hkv / 8).  Merge
+// workgroup m runs on XCD m mod 8 (launched after every streaming
+// workgroup, it starts on a compute unit one of them has left) and takes
+// four query heads of that XCD for one sequence.  A wave stores its
+// partials, waits for its stores, then writes this call's mark (P.epoch)
+// beside each (slot, head); the merging wave waits for the marks of the
+// row's pieces, reads them through the shared L2, merges them as the merge
+// kernel does (the same rounds, so the same bits), stores the output and
+// clears the marks.  The streaming workgroups are all dispatched before any
+// merge workgroup (in-order dispatch), so every wait ends.
+template <int D, int BS>
+__device__ __forceinline__ void merge_in_launch(const DecodeParams& P, int m, StreamLds<BS>& L) {
+  const int S = P.num_seqs;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // prefix sums of the rows' tiles, as the streaming workgroups compute them
+  {
+    const int per = (S + kThreads - 1) / kThreads;
+    const int s0 = threadIdx.x * per;
+    int local = 0;
+    for (int i = 0; i < per; ++i) {
+      const int s = s0 + i;
+      if (s < S) {
+        const RowSpan rs = row_span(P.seq_lens[s], P.window, P.max_blocks, BS);
+        L.pre[s + 1] = rs.nblocks;
+        local += rs.nblocks;
+      }
+    }
+    const int incl = wave_scan(local, lane);
+    if (lane == 63) L.wsum[wave] = incl;
+    __syncthreads();
+    int run = incl - local;
+    for (int w = 0; w < wave; ++w) run += L.wsum[w];
+    if (threadIdx.x == 0) L.pre[0] = 0;
+    for (int i = 0; i < per; ++i) {
+      const int s = s0 + i;
+      if (s < S) {
+        run += L.pre[s + 1];
+        L.pre[s + 1] = run;
+      }
+    }
+    __syncthreads();
+  }
+  // this wave's (sequence, query head)
+  const int hpx = P.num_q_heads / 8;  // query heads of one XCD
+  const int wps = (hpx + 3) / 4;      // merge workgroups per (XCD, sequence)
+  const int x = m & 7, k = m >> 3;
+  const int s = k / wps, j = 4 * (k - s * wps) + wave;
+  if (s >= S || j >= hpx) return;
+  const int h = x * hpx + j;
+  const int kvh = h / P.group, hh = h - kvh * P.group;  // one head group per KV head here
+  const int per_row = L.pre[S], nb = L.pre[s + 1] - L.pre[s];
+  if (nb == 0) return;  // an empty row: zeroed by the first streaming workgroup
+  const long long T = (long long)per_row * P.num_kv_heads, W = (long long)P.stream_wgs * kWaves;
+  const CutPieces pc((long long)kvh * per_row + L.pre[s], nb, T, W);
+  const int n = pc.n;
+  if (n == 1) return;  // the row lay inside one wave's range: stored there
+  const unsigned hpw = (unsigned)P.heads_per_wg;
+  // wait for the pieces' marks, 64 at a time
+  for (int k0 = 0; k0 < n; k0 += 64) {
+    const int kk = k0 + lane;
+    const unsigned pb = kk < n ? (unsigned)pc.slot(kk) * hpw + hh : 0u;
+    bool ready = kk >= n;
+    for (int it = 0; it < kMergePolls; ++it) {
+      if (!ready) ready = l2_load(P.flags + pb) == P.epoch;
+      if (__all(ready)) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  constexpr int PER = D / 64;
+  float M = -INFINITY, den = 0.f, num[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) num[e] = 0.f;
+  constexpr int CH = kMergeChunk;
+  for (int k0 = 0; k0 < n; k0 += CH) {
+    float mm[CH], l[CH], v[CH][PER];
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const bool use = k0 + u < n;
+      const unsigned pb = (unsigned)pc.slot(use ? k0 + u : n - 1) * hpw + hh;
+      const float a = l2_load(P.part_ml + pb * 2u), b = l2_load(P.part_ml + pb * 2u + 1u);
+      mm[u] = use ? a : -INFINITY;
+      l[u] = use ? b : 0.f;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const float xv = l2_load(P.part_o + pb * (unsigned)D + lane + 64 * e);
+        v[u][e] = use ? xv : 0.f;
+      }
+    }
+    merge_round(M, den, num, mm, l, v);
+  }
+  const float inv = den > 0.f ? P.v_scale / den : 0.f;
+  uint16_t* out = (uint16_t*)P.out + ((size_t)s * P.num_q_heads + h) * D;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) out[lane + 64 * e] = bf16_rne(num[e] * inv);
+  // clear the marks for the next call
+  for (int k0 = 0; k0 < n; k0 += 64) {
+    const int kk = k0 + lane;
+    if (kk < n) P.flags[(unsigned)pc.slot(kk) * hpw + hh] = 0;
+  }
+}
+
 template <int D, int DEPTH, bool FUSED, bool FP8, int BS, bool NT>  // BS = log2(block size / 16)
 __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stream_kernel(const DecodeParams P) {
   __shared__ StreamLds<BS> lds;
   StreamLds<BS>& L = lds;
-  const int wg = blockIdx.x, nwg = gridDim.x;
+  if ((int)blockIdx.x >= P.stream_wgs) {  // a merge workgroup (P.merge_wgs > 0)
+    merge_in_launch<D, BS>(P, (int)blockIdx.x - P.stream_wgs, L);
+    return;
+  }
+  const int wg = blockIdx.x, nwg = P.stream_wgs;
 #include "stream_body.inc"
 }
 
@@ -346,10 +468,11 @@ void launch_sk(const DecodeParams& p, hipStream_t stream) {
                          f);
   } else if (p.slot_mapping) {
     // the fused step runs at ring depth 1: the new token takes the registers of a deeper ring
-    hipLaunchKernelGGL((decode_stream_kernel<D, 1, true, FP8, BS, NT>), dim3(p.stream_wgs), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((decode_stream_kernel<D, 1, true, FP8, BS, NT>), dim3(p.stream_wgs + p.merge_wgs), dim3(kThreads),
+                       0, stream, p);
   } else {
-    hipLaunchKernelGGL((decode_stream_kernel<D, DEPTH, false, FP8, BS, NT>), dim3(p.stream_wgs), dim3(kThreads), 0, stream,
-                       p);
+    hipLaunchKernelGGL((decode_stream_kernel<D, DEPTH, false, FP8, BS, NT>), dim3(p.stream_wgs + p.merge_wgs),
+                       dim3(kThreads), 0, stream, p);
   }
 }
 
@@ -363,6 +486,7 @@ hipError_t launch_sd(const DecodeParams& p, hipStream_t stream) {
   else launch_sk<D, DEPTH, FP8, BS, false>(p, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (p.merge_wgs > 0) return hipSuccess;  // merged inside the launch
   const dim3 grid((p.num_q_heads + 3) / 4, p.num_seqs);
   hipLaunchKernelGGL((decode_stream_reduce_kernel<D>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();

@@ -39,6 +39,10 @@ struct DecodeParams {
   int32_t depth;                // blocks of K/V a wave keeps in flight ahead of the one it computes
   int32_t* prefix;              // [S + 1] tiles before each sequence's row     (streaming only)
   int32_t* cuts;                // [HG][S][2] per row: first piece (wave * 2 + slot), last wave  (streaming only)
+  int32_t merge_wgs;            // > 0: the streaming launch merges the cut rows itself, in these
+                                // workgroups after the streaming ones (streaming only)
+  uint64_t epoch;               // this call's ready mark for the in-launch merge (never 0)
+  uint64_t* flags;              // [waves * 2][heads_per_wg] a piece's ready mark, cleared by its merge
   int32_t stream_wgs;           // persistent workgroups of a streaming launch   (streaming only)
   const void* k_new;            // [S][Hkv][D] new token per sequence        (fused write only)
   const void* v_new;            // [S][Hkv][D]                               (fused write only)

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -319,13 +320,14 @@ static size_t grid_workspace(const kvp::DecodeParams& p, int32_t head_dim, size_
 }
 
 // Workspace of the streaming kernel: prefix sums, the rows' piece ranges
-// (first piece, last wave), then
+// (first piece, last wave), the in-launch merge's ready marks (one per
+// partial slot and head: zero outside a call), then
 // two partial slots per wave for up to heads_per_wg heads ((max, sum) pairs
 // and outputs), then, for a call with a shared prefix (cascade), the
 // prefix pass's pieces: one per (key chunk, sequence, query head), and one
 // per (row, head) for tails a single wave holds.
 struct StreamLayout {
-  size_t prefix, cuts, ml, o, pre_ml, pre_o, row_ml, row_o, total;
+  size_t prefix, cuts, flags, ml, o, pre_ml, pre_o, row_ml, row_o, total;
 };
 
 // Key chunks of the shared-prefix pass: enough that the pass has about as
@@ -347,7 +349,8 @@ static StreamLayout stream_workspace(const kvp::DecodeParams& p, int32_t head_di
   const size_t rows = (size_t)p.num_kv_heads * p.qgroups * p.num_seqs * p.heads_per_wg;
   L.prefix = 0;
   L.cuts = L.prefix + align256((size_t)(p.num_seqs + 1) * sizeof(int32_t));
-  L.ml = L.cuts + align256((size_t)p.num_kv_heads * p.qgroups * p.num_seqs * 2 * sizeof(int32_t));
+  L.flags = L.cuts + align256((size_t)p.num_kv_heads * p.qgroups * p.num_seqs * 2 * sizeof(int32_t));
+  L.ml = L.flags + align256(slots * sizeof(uint64_t));
   L.o = L.ml + align256(slots * 2 * sizeof(float));
   if (!cascade) {
     L.pre_ml = L.pre_o = L.row_ml = L.row_o = 0;
@@ -388,6 +391,18 @@ size_t paged_decode_workspace_bytes(kvp_pool pool, int32_t num_seqs, int32_t num
   }
   g_err[0] = '\0';
   return need;
+}
+
+// Marks of successive calls: splitmix64 of a process-wide counter (nonzero),
+// so that a mark left by another use of the memory is practically never
+// this call's.
+static uint64_t next_epoch() {
+  static std::atomic<uint64_t> counter{0x9e3779b97f4a7c15ull};
+  uint64_t z = counter.fetch_add(0x9e3779b97f4a7c15ull) + 0x9e3779b97f4a7c15ull;
+  z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+  z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+  z ^= z >> 31;
+  return z ? z : 1;
 }
 
 // Decode attention, optionally preceded by each sequence's new-token write
@@ -443,6 +458,20 @@ static int32_t decode(kvp_pool pool, const kvp_decode_args* a, const void* k_new
     p.prefix_chunk = (per + 3) / 4 * 4;
     p.prefix_pieces = (tiles + p.prefix_chunk - 1) / p.prefix_chunk;
   }
+  // The streaming launch merges the cut rows itself when no row crosses an
+  // XCD (KV heads split evenly over the 8 XCDs, one head group each, the
+  // grid a multiple of 8 workgroups); KVP_LAUNCH_MERGE=0 (read at each
+  // call) keeps the separate merge kernel.
+  if (path == PATH_STREAM && p.prefix_blocks == 0 && p.qgroups == 1 && d.num_kv_heads % 8 == 0 &&
+      p.stream_wgs % 8 == 0) {
+    const char* ev = getenv("KVP_LAUNCH_MERGE");
+    if (!(ev && atoi(ev) == 0)) {
+      const long long wps = (a->num_q_heads / 8 + 3) / 4;
+      const long long mw = 8LL * a->num_seqs * wps;
+      if (mw + p.stream_wgs <= 0x7fffffffLL) p.merge_wgs = (int32_t)mw;
+    }
+  }
+  if (p.merge_wgs > 0) p.epoch = next_epoch();
   size_t o_off = 0, ml_off = 0;
   const StreamLayout SL = path == PATH_STREAM ? stream_workspace(p, d.head_dim, p.prefix_blocks > 0) : StreamLayout{};
   const size_t ws = path == PATH_STREAM ? SL.total : grid_workspace(p, d.head_dim, &o_off, &ml_off);
@@ -461,6 +490,7 @@ static int32_t decode(kvp_pool pool, const kvp_decode_args* a, const void* k_new
     if (path == PATH_STREAM) {
       p.prefix = (int32_t*)(w + SL.prefix);
       p.cuts = (int32_t*)(w + SL.cuts);
+      p.flags = (uint64_t*)(w + SL.flags);
       p.part_ml = (float*)(w + SL.ml);
       p.part_o = (float*)(w + SL.o);
       p.pre_ml = (float*)(w + SL.pre_ml);
