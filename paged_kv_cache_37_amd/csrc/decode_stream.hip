@@ -63,23 +63,26 @@ __device__ __forceinline__ long long floor_div(long long num, long long den) {
 // prefix's chunk pieces and a row's wave pieces with it.
 constexpr int kMergeChunk = 8;
 
+// The products and sums are written out (explicit fma, no contraction left
+// to the compiler), so every kernel that merges pieces gets the same bits.
 template <int PER, int CH>
 __device__ __forceinline__ void merge_round(float& M, float& den, float (&num)[PER], const float (&m)[CH],
                                             const float (&l)[CH], const float (&v)[CH][PER]) {
+#pragma clang fp contract(off)
   float Mc = M;
 #pragma unroll
   for (int u = 0; u < CH; ++u) Mc = fmaxf(Mc, m[u]);
   if (Mc == -INFINITY) return;
   const float ao = __builtin_amdgcn_exp2f(M - Mc);
-  den *= ao;
+  den = den * ao;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) num[e] *= ao;
+  for (int e = 0; e < PER; ++e) num[e] = num[e] * ao;
 #pragma unroll
   for (int u = 0; u < CH; ++u) {
     const float f = __builtin_amdgcn_exp2f(m[u] - Mc);
-    den += f * l[u];
+    den = __builtin_fmaf(f, l[u], den);
 #pragma unroll
-    for (int e = 0; e < PER; ++e) num[e] += f * v[u][e];
+    for (int e = 0; e < PER; ++e) num[e] = __builtin_fmaf(f, v[u][e], num[e]);
   }
   M = Mc;
 }
@@ -367,12 +370,13 @@ __global__ __launch_bounds__(256, 8) void decode_stream_reduce_kernel(const Deco
   if (nb == 0 && !cascade) return;
   // merge one more piece (max m, sum l, unnormalised o)
   auto add = [&](float m, float l, const float* o) {
+#pragma clang fp contract(off)
     const float Mc = fmaxf(M, m);
     if (Mc == -INFINITY) return;
     const float a = __builtin_amdgcn_exp2f(M - Mc), b = __builtin_amdgcn_exp2f(m - Mc);
-    den = den * a + l * b;
+    den = __builtin_fmaf(l, b, den * a);
 #pragma unroll
-    for (int e = 0; e < PER; ++e) num[e] = num[e] * a + o[e] * b;
+    for (int e = 0; e < PER; ++e) num[e] = __builtin_fmaf(o[e], b, num[e] * a);
     M = Mc;
   };
 
