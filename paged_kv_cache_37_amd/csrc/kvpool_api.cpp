@@ -330,19 +330,35 @@ struct StreamLayout {
   size_t prefix, cuts, flags, ml, o, pre_ml, pre_o, row_ml, row_o, total;
 };
 
-// Key chunks of the shared-prefix pass: enough that the pass has about as
-// many workgroups as the streaming grid (two per CU), at most
-// kMaxPrefixPieces; KVP_PREFIX_PIECES (1..8, read at each call) overrides.
-// The chunks actually used can be fewer (a chunk is whole 4-tile steps).
-static int32_t prefix_pieces_wanted(const kvp::DecodeParams& p) {
+// The cascade's one launch: its streaming grid and the key chunks of its
+// shared-prefix pass, for `resident` workgroup slots.  The prefix pass has
+// units = KV heads x 128-row tiles workgroups per chunk.  When the units fit
+// in a quarter of the slots, the streaming grid takes the other three
+// quarters and the chunks fill that quarter, so the memory-bound tails and
+// the matrix-bound prefix pass run side by side from the start (and the merge
+// reads fewer pieces); else the streaming grid takes every slot and the prefix
+// pass gets about as many workgroups, started on the slots the streaming
+// workgroups free.  At most kMaxPrefixPieces chunks; KVP_PREFIX_PIECES (1..8,
+// read at each call) overrides the count.  Returns the chunks wanted (those
+// actually used can be fewer: a chunk is whole 4-tile steps).
+static int32_t cascade_grid(kvp::DecodeParams& p, int32_t resident) {
   const long long units = (long long)p.num_kv_heads * ((p.num_seqs * p.group + 127) / 128);
-  long long want = units > 0 ? (p.stream_wgs + units - 1) / units : 1;
+  long long want;
+  const int32_t quarter = resident / 32 * 8;  // a multiple of 8 (the streaming grid's XCD order)
+  if (units > 0 && quarter > 0 && units <= quarter) {
+    p.stream_wgs = resident - quarter;
+    want = quarter / units;
+  } else {
+    p.stream_wgs = resident;
+    want = units > 0 ? (resident + units - 1) / units : 1;
+  }
   const char* ev = getenv("KVP_PREFIX_PIECES");
   if (ev && atoi(ev) >= 1) want = atoi(ev);
   return (int32_t)std::max(1LL, std::min<long long>(want, kvp::kMaxPrefixPieces));
 }
 
-static StreamLayout stream_workspace(const kvp::DecodeParams& p, int32_t head_dim, bool cascade) {
+// pieces: the cascade's prefix chunks (cascade_grid), else unused.
+static StreamLayout stream_workspace(const kvp::DecodeParams& p, int32_t head_dim, bool cascade, int32_t pieces = 0) {
   StreamLayout L;
   const size_t slots = (size_t)p.stream_wgs * kvp::kWaves * 2 * p.heads_per_wg;
   const size_t qh = (size_t)p.num_seqs * p.num_q_heads;
@@ -357,10 +373,9 @@ static StreamLayout stream_workspace(const kvp::DecodeParams& p, int32_t head_di
     L.total = L.o + slots * head_dim * sizeof(float);
     return L;
   }
-  const size_t pieces = prefix_pieces_wanted(p);
   L.pre_ml = L.o + align256(slots * head_dim * sizeof(float));
-  L.pre_o = L.pre_ml + align256(pieces * qh * 2 * sizeof(float));
-  L.row_ml = L.pre_o + align256(pieces * qh * head_dim * sizeof(float));
+  L.pre_o = L.pre_ml + align256((size_t)pieces * qh * 2 * sizeof(float));
+  L.row_ml = L.pre_o + align256((size_t)pieces * qh * head_dim * sizeof(float));
   L.row_o = L.row_ml + align256(rows * 2 * sizeof(float));
   L.total = L.row_o + rows * head_dim * sizeof(float);
   return L;
@@ -375,7 +390,7 @@ size_t paged_decode_workspace_bytes(kvp_pool pool, int32_t num_seqs, int32_t num
     kvp::DecodeParams p;
     int32_t path;
     if (plan(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, v, &p, &path) != KVP_OK) continue;
-    size_t n = path == PATH_STREAM ? stream_workspace(p, pool->desc.head_dim, true).total
+    size_t n = path == PATH_STREAM ? stream_workspace(p, pool->desc.head_dim, false).total
                                    : grid_workspace(p, pool->desc.head_dim, &a, &a);
     if (path == PATH_STREAM) {  // the grids of the fused step and of the cascade (their own occupancies) must fit too
       const bool fp8 = pool->desc.dtype == KVP_FP8_E4M3;
@@ -383,7 +398,8 @@ size_t paged_decode_workspace_bytes(kvp_pool pool, int32_t num_seqs, int32_t num
         for (int cascade = 0; cascade < 2; ++cascade) {
           p.stream_wgs = stream_workgroups(pool->desc.head_dim, fused ? 1 : p.depth, fused != 0, fp8, p.bshift,
                                            cascade != 0);
-          const size_t nf = stream_workspace(p, pool->desc.head_dim, true).total;
+          const int32_t pieces = cascade ? cascade_grid(p, p.stream_wgs) : 0;
+          const size_t nf = stream_workspace(p, pool->desc.head_dim, cascade != 0, pieces).total;
           if (nf > n) n = nf;
         }
     }
@@ -441,19 +457,21 @@ static int32_t decode(kvp_pool pool, const kvp_decode_args* a, const void* k_new
     p.v_new = v_new;
     p.slot_mapping = slots;
   }
+  int32_t want_pieces = 0;  // the cascade's prefix chunks (workspace layout)
   if (a->shared_prefix_blocks < 0 || a->shared_prefix_blocks > a->max_blocks_per_seq)
     return fail(KVP_ERR_INVALID_ARG, "shared_prefix_blocks must be in [0, max_blocks_per_seq]");
   // the shared-prefix pass is a STREAM feature for full-context rows; elsewhere the hint is ignored
   if (path == PATH_STREAM && a->sliding_window == 0) p.prefix_blocks = a->shared_prefix_blocks;
   if (p.prefix_blocks > 0) {
-    // one launch runs the tails and the prefix pass: the grid of that kernel
-    p.stream_wgs = stream_workgroups(d.head_dim, p.depth, p.slot_mapping != nullptr, d.dtype == KVP_FP8_E4M3, p.bshift,
-                                     true);
-    if (p.stream_wgs <= 0) return fail(KVP_ERR_HIP, "cannot size the streaming grid (no device?)");
+    // one launch runs the tails and the prefix pass: the slots of that kernel
+    const int32_t resident = stream_workgroups(d.head_dim, p.depth, p.slot_mapping != nullptr,
+                                               d.dtype == KVP_FP8_E4M3, p.bshift, true);
+    if (resident <= 0) return fail(KVP_ERR_HIP, "cannot size the streaming grid (no device?)");
     // split the prefix's keys into chunks of whole 4-tile steps (the
-    // workspace holds as many pieces as prefix_pieces_wanted gives)
+    // workspace holds as many pieces as cascade_grid wants)
     const int32_t tiles = p.prefix_blocks << p.bshift;
-    const int32_t want = prefix_pieces_wanted(p);
+    want_pieces = cascade_grid(p, resident);
+    const int32_t want = want_pieces;
     const int32_t per = (tiles + want - 1) / want;
     p.prefix_chunk = (per + 3) / 4 * 4;
     p.prefix_pieces = (tiles + p.prefix_chunk - 1) / p.prefix_chunk;
@@ -473,7 +491,8 @@ static int32_t decode(kvp_pool pool, const kvp_decode_args* a, const void* k_new
   }
   if (p.merge_wgs > 0) p.epoch = next_epoch();
   size_t o_off = 0, ml_off = 0;
-  const StreamLayout SL = path == PATH_STREAM ? stream_workspace(p, d.head_dim, p.prefix_blocks > 0) : StreamLayout{};
+  const StreamLayout SL =
+      path == PATH_STREAM ? stream_workspace(p, d.head_dim, p.prefix_blocks > 0, want_pieces) : StreamLayout{};
   const size_t ws = path == PATH_STREAM ? SL.total : grid_workspace(p, d.head_dim, &o_off, &ml_off);
   if (path == PATH_STREAM && ws / sizeof(float) >= 0xffffffffull)  // the merge kernel's 32-bit element offsets
     return fail(KVP_ERR_UNSUPPORTED, "the STREAM variant's workspace would exceed 2^32 floats");

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_helpers import Dev, compare, host_to_torch, reference, say, to_f64, torch_to_bits, ulp_bf16
+from gpu_helpers import SHARP_C, Dev, compare, host_to_torch, reference, say, to_f64, torch_to_bits, ulp_bf16
 from paged_kv_cache_37_amd.blockpool import shared_prefix_blocks
 
 pytestmark = pytest.mark.gpu
@@ -75,6 +75,37 @@ def test_cascade_shapes(gpu, prefix, Hq, Hkv, D):
     # the hint changes no bit: the tails without it, and the whole rows with or without it
     assert torch.equal(out_c.view(torch.int16), dev.attend(shared_prefix_blocks=P, shared_blocks=True).view(torch.int16))
     assert torch.equal(out_p.view(torch.int16), dev.attend().view(torch.int16))
+
+
+@pytest.mark.parametrize("S,Hq,Hkv", [(1040, 32, 8), (1100, 16, 16), (500, 32, 8)])
+def test_cascade_grid_split(gpu, S, Hq, Hkv):
+    """The launch shares its slots between the tails and the prefix pass
+    when the prefix pass's row tiles (KV heads x 128-row tiles) fit in a
+    quarter of them (500 sequences, G = 4: 128 tiles), else the tails take
+    every slot (1040 sequences: 264 tiles; MHA-shaped 1100: 144 tiles)."""
+    rng = np.random.default_rng(S + Hq)
+    tails = rng.integers(0, 48, size=S)
+    tails[:4] = [0, 1, 16, 47]
+    w = W.shared_prefix(1700 + S, 160, tails, Hq, Hkv, 128)
+    P = 10
+    assert shared_prefix_blocks(np.asarray(w.block_tables), w.seq_lens) == P
+    dev = Dev(w)
+    out_c = dev.attend(shared_prefix_blocks=P)
+    out_p = dev.attend()
+    seqs = [0, 1, 2, 3] + list(range(5, S, 97)) + [S - 1]
+    ref = reference(w, seqs=seqs)
+    compare(out_c[seqs], ref, "bf16", f"cascade S {S} Hq {Hq} Hkv {Hkv}")
+    # every row against plain decode (no oracle value for most rows): one
+    # bf16 step at the larger of the two magnitudes, plus the decode sharp
+    # bar's fp32 term (c rms(row)) for outputs that are a cancellation of
+    # terms of the row's size (over these 4M outputs a few near-zero ones
+    # differ by ~1e-5 rms)
+    a, b = to_f64(out_c), to_f64(out_p)
+    rms = np.sqrt(np.mean(b ** 2, axis=-1, keepdims=True))
+    bound = ulp_bf16(np.maximum(np.abs(a), np.abs(b))) * 1.0001 + SHARP_C["decode"] * rms
+    worst = float((np.abs(a - b) / bound).max())
+    say(f"cascade S {S} vs plain: worst", round(worst, 3), "of the bar")
+    assert worst <= 1.0
 
 
 @pytest.mark.parametrize("prefix,Hq,Hkv,D", [(2048, 32, 8, 128), (256, 8, 2, 64)])
