@@ -332,22 +332,26 @@ struct StreamLayout {
 
 // The cascade's one launch: its streaming grid and the key chunks of its
 // shared-prefix pass, for `resident` workgroup slots.  The prefix pass has
-// units = KV heads x 128-row tiles workgroups per chunk.  When the units fit
-// in a quarter of the slots, the streaming grid takes the other three
-// quarters and the chunks fill that quarter, so the memory-bound tails and
-// the matrix-bound prefix pass run side by side from the start (and the merge
-// reads fewer pieces); else the streaming grid takes every slot and the prefix
-// pass gets about as many workgroups, started on the slots the streaming
-// workgroups free.  At most kMaxPrefixPieces chunks; KVP_PREFIX_PIECES (1..8,
-// read at each call) overrides the count.  Returns the chunks wanted (those
-// actually used can be fewer: a chunk is whole 4-tile steps).
-static int32_t cascade_grid(kvp::DecodeParams& p, int32_t resident) {
+// units = KV heads x 128-row tiles workgroups per chunk.  When whole chunks
+// of units fit in the prefix pass's share of the slots (a quarter for bf16
+// pools, three eighths for FP8 ones, whose tails stream half the bytes), the
+// chunks take that share and the streaming grid the slots left, so the
+// memory-bound tails and the matrix-bound prefix pass run side by side from
+// the start (and the merge reads fewer pieces); else the streaming grid
+// takes every slot and the prefix pass gets about as many workgroups,
+// started on the slots the streaming workgroups free.  At most
+// kMaxPrefixPieces chunks; KVP_PREFIX_PIECES (1..8, read at each call)
+// overrides the count.  Returns the chunks wanted (those actually used can
+// be fewer: a chunk is whole 4-tile steps).
+static int32_t cascade_grid(kvp::DecodeParams& p, int32_t resident, bool fp8) {
   const long long units = (long long)p.num_kv_heads * ((p.num_seqs * p.group + 127) / 128);
+  const long long share = (long long)resident * (fp8 ? 3 : 2) / 8;
   long long want;
-  const int32_t quarter = resident / 32 * 8;  // a multiple of 8 (the streaming grid's XCD order)
-  if (units > 0 && quarter > 0 && units <= quarter) {
-    p.stream_wgs = resident - quarter;
-    want = quarter / units;
+  const long long split = units > 0 ? share / units : 0;
+  const long long left = (resident - split * units) / 8 * 8;  // a multiple of 8 (the streaming grid's XCD order)
+  if (split >= 1 && left >= 8) {
+    p.stream_wgs = (int32_t)left;
+    want = split;
   } else {
     p.stream_wgs = resident;
     want = units > 0 ? (resident + units - 1) / units : 1;
@@ -398,7 +402,7 @@ size_t paged_decode_workspace_bytes(kvp_pool pool, int32_t num_seqs, int32_t num
         for (int cascade = 0; cascade < 2; ++cascade) {
           p.stream_wgs = stream_workgroups(pool->desc.head_dim, fused ? 1 : p.depth, fused != 0, fp8, p.bshift,
                                            cascade != 0);
-          const int32_t pieces = cascade ? cascade_grid(p, p.stream_wgs) : 0;
+          const int32_t pieces = cascade ? cascade_grid(p, p.stream_wgs, fp8) : 0;
           const size_t nf = stream_workspace(p, pool->desc.head_dim, cascade != 0, pieces).total;
           if (nf > n) n = nf;
         }
@@ -470,7 +474,7 @@ static int32_t decode(kvp_pool pool, const kvp_decode_args* a, const void* k_new
     // split the prefix's keys into chunks of whole 4-tile steps (the
     // workspace holds as many pieces as cascade_grid wants)
     const int32_t tiles = p.prefix_blocks << p.bshift;
-    want_pieces = cascade_grid(p, resident);
+    want_pieces = cascade_grid(p, resident, d.dtype == KVP_FP8_E4M3);
     const int32_t want = want_pieces;
     const int32_t per = (tiles + want - 1) / want;
     p.prefix_chunk = (per + 3) / 4 * 4;
