@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -12,6 +13,8 @@
 #include <mutex>
 #include <new>
 #include <vector>
+
+#include <unistd.h>
 
 #include "internal.h"
 #include "kvpool.h"
@@ -413,11 +416,13 @@ size_t paged_decode_workspace_bytes(kvp_pool pool, int32_t num_seqs, int32_t num
   return need;
 }
 
-// Marks of successive calls: splitmix64 of a process-wide counter (nonzero),
-// so that a mark left by another use of the memory is practically never
-// this call's.
+// Marks of successive calls: splitmix64 of a process-wide counter (nonzero)
+// that starts from the clock and the process id, so that a mark left by
+// another call or another process is practically never this call's.
 static uint64_t next_epoch() {
-  static std::atomic<uint64_t> counter{0x9e3779b97f4a7c15ull};
+  static std::atomic<uint64_t> counter{(uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() *
+                                           0x2545f4914f6cdd1dull ^
+                                       ((uint64_t)getpid() << 32)};
   uint64_t z = counter.fetch_add(0x9e3779b97f4a7c15ull) + 0x9e3779b97f4a7c15ull;
   z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
   z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
