@@ -349,15 +349,17 @@ __global__ __launch_bounds__(256, 8) void decode_stream_reduce_kernel(const Deco
     float m[kMergeChunk], l[kMergeChunk], v[kMergeChunk][PER];
 #pragma unroll
     for (int u = 0; u < kMergeChunk; ++u) {
-      const bool use = u < P.prefix_pieces;
-      const unsigned pq = qh + (use ? u : 0) * pstride;
-      const float2 ml = *(const float2*)(P.pre_ml + pq * 2u);
-      m[u] = use ? ml.x : -INFINITY;
-      l[u] = use ? ml.y : 0.f;
+      m[u] = -INFINITY;
+      l[u] = 0.f;
 #pragma unroll
-      for (int e = 0; e < PER; ++e) {
-        const float x = P.pre_o[pq * (unsigned)D + lane + 64 * e];
-        v[u][e] = use ? x : 0.f;
+      for (int e = 0; e < PER; ++e) v[u][e] = 0.f;
+      if (u < P.prefix_pieces) {  // uniform: the absent chunks' loads are skipped
+        const unsigned pq = qh + u * pstride;
+        const float2 ml = *(const float2*)(P.pre_ml + pq * 2u);
+        m[u] = ml.x;
+        l[u] = ml.y;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) v[u][e] = P.pre_o[pq * (unsigned)D + lane + 64 * e];
       }
     }
     const unsigned rb = ((unsigned)hg * S + s) * P.heads_per_wg + hh;
