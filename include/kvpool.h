@@ -276,8 +276,12 @@ int32_t paged_decode_attention(kvp_pool pool, const kvp_decode_args* args, hipSt
  *   share the prefix's K/V tiles in LDS, and the prefix's keys are split
  *   into up to 8 chunks, each leaving its own partial result), streams only
  *   the private tails, and merges the two; the result is the same
- *   attention up to fp32 rounding (KVP_PREFIX_PIECES=1..8 sets the number
- *   of chunks, read at each call).  Other variants, and
+ *   attention up to fp32 rounding.  Both passes run in one launch: when the
+ *   prefix pass's workgroups fit in a share of the resident workgroup
+ *   slots (a quarter; three eighths for an FP8 pool) they run beside the
+ *   tails' streaming workgroups from the start, else after them
+ *   (KVP_PREFIX_PIECES=1..8 sets the number of chunks, read at each
+ *   call).  Other variants, and
  *   rows with a sliding window, ignore the hint.  P must be <=
  *   max_blocks_per_seq (KVP_ERR_INVALID_ARG otherwise); if the promise does
  *   not hold the outputs are unspecified (memory is still only read inside

@@ -280,11 +280,13 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
 
 // Cascade decode in one launch: the first P.stream_wgs workgroups stream the
 // private tails (the body of decode_stream_kernel), the rest run the
-// shared-prefix pass (the prefill body over the prefix's key chunks).
-// Workgroups start in index order, so the prefix workgroups take the
-// compute units that streaming workgroups leave as they finish: the
-// MFMA-bound prefix pass fills the tail of the memory-bound streaming phase
-// instead of running before it.  The two share one LDS allocation.
+// shared-prefix pass (the prefill body over the prefix's key chunks).  The
+// host sizes the two parts to the resident workgroup slots: when the prefix
+// pass fits in its share, all of it starts at once beside the streaming
+// workgroups, the memory-bound tails and the MFMA-bound prefix pass sharing
+// the chip; otherwise the streaming grid fills every slot and the prefix
+// workgroups, which start in index order, take the compute units the
+// streaming workgroups leave.  The two share one LDS allocation.
 template <int D, int DEPTH, bool FUSED, bool FP8, int BS, bool NT>
 __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_cascade_kernel(const DecodeParams P,
                                                                                             const PrefillParams PF) {
