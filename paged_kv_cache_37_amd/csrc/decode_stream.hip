@@ -87,6 +87,21 @@ __device__ __forceinline__ void merge_round(float& M, float& den, float (&num)[P
   M = Mc;
 }
 
+// One more piece (max m, sum l, unnormalised o) into the merge, the
+// products and sums written out like merge_round's.
+template <int PER>
+__device__ __forceinline__ void merge_one(float& M, float& den, float (&num)[PER], float m, float l,
+                                          const float (&o)[PER]) {
+#pragma clang fp contract(off)
+  const float Mc = fmaxf(M, m);
+  if (Mc == -INFINITY) return;
+  const float a = __builtin_amdgcn_exp2f(M - Mc), b = __builtin_amdgcn_exp2f(m - Mc);
+  den = __builtin_fmaf(l, b, den * a);
+#pragma unroll
+  for (int e = 0; e < PER; ++e) num[e] = __builtin_fmaf(o[e], b, num[e] * a);
+  M = Mc;
+}
+
 // The pieces of a cut row [a, a + nb) of the work list (T tiles over W
 // waves), in wave order, found from the split alone (the merge uses it
 // when T < W; otherwise the first pass records where each row's pieces are).  With T >= W every range holds a tile, so they are
@@ -311,13 +326,14 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_casc
 // query head): the row's tiles [a, b) were covered by the waves w_first ..
 // w_last (recorded by the first pass); each left its partial in slot 0 (the
 // row held the wave's first tile) or slot 1 (the row was the wave's last).
-// Rows inside one wave were stored by the first pass.  The partials' loads go out eight at a time.
-// At most 64 VGPRs (8 waves per SIMD): every wave of the largest merge
-// here (256 sequences x 32 heads) is resident at once.
-// With a shared prefix every row is merged here: the prefix pass's piece,
-// then either the row's own slot (a tail inside one wave) or the wave
-// slots (a tail cut by range boundaries); a row with no tail is the prefix
-// piece alone.
+// Rows inside one wave were stored by the first pass.  The partials' loads
+// go out eight at a time.  At most 64 VGPRs (8 waves per SIMD): every wave
+// of the largest merge here (256 sequences x 32 heads) is resident at once.
+// With a shared prefix every row is merged here: the prefix pass's chunk
+// pieces, then the row's tail: its first kRowSlots pieces were stored by
+// row, so their loads go out with the first ones (one round trip for most
+// rows), any further ones come from the wave slots; a row with no tail is
+// the prefix pieces alone.
 template <int D>
 __global__ __launch_bounds__(256, 8) void decode_stream_reduce_kernel(const DecodeParams P) {
   const int s = blockIdx.y;
@@ -329,34 +345,34 @@ __global__ __launch_bounds__(256, 8) void decode_stream_reduce_kernel(const Deco
   const int kvh = h / P.group, g_in = h - kvh * P.group;
   const int qg = g_in / P.heads_per_wg, hh = g_in - qg * P.heads_per_wg;
   const int hg = kvh * P.qgroups + qg;
+  constexpr int PER = D / 64;
+  constexpr int CH = kMergeChunk;
 
   // the row's place in the work list and its pieces (written by the first
-  // pass), loaded first: with a shared prefix the pieces below go out while
-  // they travel
+  // pass), loaded first: with a shared prefix the first prefix round's and
+  // the row's slots go out while they travel
   const int pre_s = P.prefix[s], nb = P.prefix[s + 1] - pre_s, per_row = P.prefix[S];
   const int2 cut = *(const int2*)(P.cuts + 2 * ((size_t)hg * S + s));
 
-  constexpr int PER = D / 64;
   float M = -INFINITY, den = 0.f, num[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) num[e] = 0.f;
-  // With a shared prefix, the prefix pass's piece and the row's own slot
-  // do not depend on the prefix sums: their loads go out with them.
-  float rm = -INFINITY, rl = 0.f, ro[PER];
-  if (cascade) {
-    // the prefix pass's pieces (one per key chunk, in chunk order)
-    static_assert(kMaxPrefixPieces <= kMergeChunk, "one merge round takes every prefix piece");
-    // (element offsets into the workspace fit 32 bits: the host sizes it)
-    const unsigned qh = (unsigned)s * P.num_q_heads + h, pstride = (unsigned)S * P.num_q_heads;
-    float m[kMergeChunk], l[kMergeChunk], v[kMergeChunk][PER];
+  // the prefix pass's pieces (one per key chunk, in chunk order), in rounds
+  // of PR: absent pieces change no bit of a round
+  constexpr int PR = 4;
+  static_assert(kMaxPrefixPieces <= 2 * PR && kRowSlots <= CH, "piece rounds");
+  // (element offsets into the workspace fit 32 bits: the host sizes it)
+  const unsigned qh = (unsigned)s * P.num_q_heads + h, pstride = (unsigned)S * P.num_q_heads;
+  // load round r0 of the prefix pieces into m, l, v
+  auto load_prefix = [&](int r0, float (&m)[PR], float (&l)[PR], float (&v)[PR][PER]) {
+    unsigned pq = qh + r0 * pstride;  // stepped by additions (a 64-bit multiply-add here waited for a load)
 #pragma unroll
-    for (int u = 0; u < kMergeChunk; ++u) {
+    for (int u = 0; u < PR; ++u, pq += pstride) {
       m[u] = -INFINITY;
       l[u] = 0.f;
 #pragma unroll
       for (int e = 0; e < PER; ++e) v[u][e] = 0.f;
-      if (u < P.prefix_pieces) {  // uniform: the absent chunks' loads are skipped
-        const unsigned pq = qh + u * pstride;
+      if (r0 + u < P.prefix_pieces) {  // uniform: the absent chunks' loads are skipped
         const float2 ml = *(const float2*)(P.pre_ml + pq * 2u);
         m[u] = ml.x;
         l[u] = ml.y;
@@ -364,71 +380,92 @@ __global__ __launch_bounds__(256, 8) void decode_stream_reduce_kernel(const Deco
         for (int e = 0; e < PER; ++e) v[u][e] = P.pre_o[pq * (unsigned)D + lane + 64 * e];
       }
     }
-    const unsigned rb = ((unsigned)hg * S + s) * P.heads_per_wg + hh;
-    rm = P.row_ml[rb * 2u];
-    rl = P.row_ml[rb * 2u + 1u];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) ro[e] = P.row_o[rb * (unsigned)D + lane + 64 * e];
-    merge_round(M, den, num, m, l, v);
-  }
-  if (nb == 0 && !cascade) return;
-  // merge one more piece (max m, sum l, unnormalised o)
-  auto add = [&](float m, float l, const float* o) {
-#pragma clang fp contract(off)
-    const float Mc = fmaxf(M, m);
-    if (Mc == -INFINITY) return;
-    const float a = __builtin_amdgcn_exp2f(M - Mc), b = __builtin_amdgcn_exp2f(m - Mc);
-    den = __builtin_fmaf(l, b, den * a);
-#pragma unroll
-    for (int e = 0; e < PER; ++e) num[e] = __builtin_fmaf(o[e], b, num[e] * a);
-    M = Mc;
   };
-
-  // merge the pieces slot(0) .. slot(n - 1) in rounds of kMergeChunk
-  auto merge_pieces = [&](int n, auto slot) {
-    constexpr int CH = kMergeChunk;
-    for (int k0 = 0; k0 < n; k0 += CH) {
-      float m[CH], l[CH], v[CH][PER];
+  float rsm[kRowSlots], rsl[kRowSlots], rso[kRowSlots][PER];
+  if (cascade) {
+    float pm[PR], pl[PR], pv[PR][PER];
+    load_prefix(0, pm, pl, pv);
+    const unsigned rb = (((unsigned)hg * S + s) * P.heads_per_wg + hh) * kRowSlots;
 #pragma unroll
-      for (int u = 0; u < CH; ++u) {
-        const bool use = k0 + u < n;
-        const unsigned pb = slot(use ? k0 + u : n - 1) * (unsigned)P.heads_per_wg + hh;
-        const float2 ml = *(const float2*)(P.part_ml + pb * 2u);
-        m[u] = use ? ml.x : -INFINITY;
-        l[u] = use ? ml.y : 0.f;
+    for (int k = 0; k < kRowSlots; ++k) {
+      rsm[k] = P.row_ml[(rb + k) * 2u];
+      rsl[k] = P.row_ml[(rb + k) * 2u + 1u];
 #pragma unroll
-        for (int e = 0; e < PER; ++e) {
-          const float x = P.part_o[pb * (unsigned)D + lane + 64 * e];
-          v[u][e] = use ? x : 0.f;
-        }
-      }
-      merge_round(M, den, num, m, l, v);
+      for (int e = 0; e < PER; ++e) rso[k][e] = P.row_o[(rb + k) * (unsigned)D + lane + 64 * e];
     }
-  };
+    merge_round(M, den, num, pm, pl, pv);
+    if (P.prefix_pieces > PR) {
+      load_prefix(PR, pm, pl, pv);
+      merge_round(M, den, num, pm, pl, pv);
+    }
+  } else if (nb == 0) {
+    return;
+  }
 
   if (nb > 0) {
     const long long T = (long long)per_row * P.num_kv_heads * P.qgroups;
     const long long W = (long long)P.stream_wgs * kWaves;
-    if (T >= W) {
-      // every wave holds a tile: the pieces are the waves from the one
-      // holding the row's first tile (its recorded piece) to the one holding
-      // its last, every later one in slot 0
-      const unsigned first = (unsigned)cut.x;
-      const int n = cut.y - (int)(first >> 1) + 1;
-      if (n == 1) {
-        if (!cascade) return;  // stored by the first pass
-        add(rm, rl, ro);       // the tail one wave held whole
-      } else {
-        merge_pieces(n, [&](int k) { return k == 0 ? first : ((first >> 1) + (unsigned)k) * 2u; });
-      }
+    const unsigned first = (unsigned)cut.x;
+    // every wave holds a tile (T >= W): the pieces are the waves from the
+    // one holding the row's first tile (its recorded piece) to the one
+    // holding its last, every later one in slot 0; else each tile is a
+    // piece of its own, located by CutPieces
+    const int n = T >= W ? cut.y - (int)(first >> 1) + 1 : nb;
+    if (n == 1) {
+      if (!cascade) return;  // stored by the first pass
+      merge_one(M, den, num, rsm[0], rsl[0], rso[0]);  // the tail one wave held whole
     } else {
-      // some waves hold no tile: CutPieces locates each of the row's tiles
       const CutPieces pc((long long)hg * per_row + pre_s, nb, T, W);
-      if (pc.n == 1) {
-        if (!cascade) return;
-        add(rm, rl, ro);
-      } else {
-        merge_pieces(pc.n, [&](int k) { return (unsigned)pc.slot(k); });
+      auto slot = [&](int k) -> unsigned {
+        if (T >= W) return k == 0 ? first : ((first >> 1) + (unsigned)k) * 2u;
+        return (unsigned)pc.slot(k);
+      };
+      // pieces k0 .. n-1 in rounds of CH (unused places load the last piece
+      // again: no branch around the loads); with a shared prefix the first
+      // kRowSlots come from the row's slots, and a tail of at most that many
+      // pieces needs no further load
+      auto load_piece = [&](int k, bool use, float& m, float& l, float (&v)[PER]) {
+        const unsigned pb = slot(use ? k : n - 1) * (unsigned)P.heads_per_wg + hh;
+        const float2 ml = *(const float2*)(P.part_ml + pb * 2u);
+        m = use ? ml.x : -INFINITY;
+        l = use ? ml.y : 0.f;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+          const float x = P.part_o[pb * (unsigned)D + lane + 64 * e];
+          v[e] = use ? x : 0.f;
+        }
+      };
+      int k0 = 0;
+      if (cascade) {
+        float m[CH], l[CH], v[CH][PER];
+#pragma unroll
+        for (int u = 0; u < kRowSlots; ++u) {
+          const bool use = u < n;
+          m[u] = use ? rsm[u] : -INFINITY;
+          l[u] = use ? rsl[u] : 0.f;
+#pragma unroll
+          for (int e = 0; e < PER; ++e) v[u][e] = use ? rso[u][e] : 0.f;
+        }
+        if (n <= kRowSlots) {
+#pragma unroll
+          for (int u = kRowSlots; u < CH; ++u) {
+            m[u] = -INFINITY;
+            l[u] = 0.f;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) v[u][e] = 0.f;
+          }
+        } else {
+#pragma unroll
+          for (int u = kRowSlots; u < CH; ++u) load_piece(u, u < n, m[u], l[u], v[u]);
+        }
+        merge_round(M, den, num, m, l, v);
+        k0 = CH;
+      }
+      for (; k0 < n; k0 += CH) {
+        float m[CH], l[CH], v[CH][PER];
+#pragma unroll
+        for (int u = 0; u < CH; ++u) load_piece(k0 + u, k0 + u < n, m[u], l[u], v[u]);
+        merge_round(M, den, num, m, l, v);
       }
     }
   }

@@ -13,6 +13,7 @@ constexpr int kWaves = 4;       // waves per decode workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxStreamSeqs = 4096;  // sequences one streaming launch can take (LDS prefix sums)
 constexpr int kMaxPrefixPieces = 8;    // key chunks of the shared-prefix pass
+constexpr int kRowSlots = 3;         // cascade: a row's first pieces stored by row (the merge's first loads)
 
 // Geometry and arguments of one decode launch, resolved on the host.
 struct DecodeParams {
@@ -52,8 +53,8 @@ struct DecodeParams {
   int32_t prefix_chunk;         // tiles per chunk, a multiple of 4 (cascade only)
   float* pre_o;                 // [pieces][S][Hq][D] prefix pass: unnormalised output (cascade only)
   float* pre_ml;                // [pieces][S][Hq][2] prefix pass: (max, sum)          (cascade only)
-  float* row_o;                 // [rows][heads_per_wg][D] tails held whole by a wave  (cascade only)
-  float* row_ml;                // [rows][heads_per_wg][2]                             (cascade only)
+  float* row_o;                 // [rows][heads_per_wg][kRowSlots][D] a tail's first pieces  (cascade only)
+  float* row_ml;                // [rows][heads_per_wg][kRowSlots][2]                      (cascade only)
   int32_t nt_loads;             // tiles read with non-temporal loads (no block read by two rows)  (matrix-core kernels)
   int32_t kv_fp8;               // the pool holds E4M3 codes (K scale folded into scale_log2)
   float v_scale;                // multiplies every output (FP8 V codes); 1 otherwise

@@ -383,8 +383,9 @@ static StreamLayout stream_workspace(const kvp::DecodeParams& p, int32_t head_di
   L.pre_ml = L.o + align256(slots * head_dim * sizeof(float));
   L.pre_o = L.pre_ml + align256((size_t)pieces * qh * 2 * sizeof(float));
   L.row_ml = L.pre_o + align256((size_t)pieces * qh * head_dim * sizeof(float));
-  L.row_o = L.row_ml + align256(rows * 2 * sizeof(float));
-  L.total = L.row_o + rows * head_dim * sizeof(float);
+  // a row's first kvp::kRowSlots tail pieces, by row
+  L.row_o = L.row_ml + align256(rows * kvp::kRowSlots * 2 * sizeof(float));
+  L.total = L.row_o + rows * kvp::kRowSlots * head_dim * sizeof(float);
   return L;
 }
 
