@@ -108,6 +108,33 @@ def test_cascade_grid_split(gpu, S, Hq, Hkv):
     assert worst <= 1.0
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_cascade_tails_cut_into_many_pieces(gpu, dtype):
+    """Tails long enough to span many waves' ranges (every wave holds a
+    tile): their first pieces come from the row's own slots, the rest from
+    the wave slots in several merge rounds; short tails and empty ones
+    beside them.  Against the oracle on the long rows and a sample, and
+    against plain decode on every row."""
+    rng = np.random.default_rng(41)
+    tails = rng.integers(0, 200, size=64)
+    tails[:6] = [9000, 0, 8191, 1, 4097, 16]
+    w = W.shared_prefix(4100, 512, tails, 32, 8, 128, dtype=dtype)
+    P = 32
+    assert shared_prefix_blocks(np.asarray(w.block_tables), w.seq_lens) == P
+    dev = Dev(w)
+    out_c = dev.attend(shared_prefix_blocks=P)
+    out_p = dev.attend()
+    seqs = [0, 1, 2, 3, 4, 5, 33, 63]
+    ref = reference(w, seqs=seqs)
+    compare(out_c[seqs], ref, w.dtype, f"cascade, tails cut into many pieces, {dtype}")
+    a, b = to_f64(out_c), to_f64(out_p)
+    rms = np.sqrt(np.mean(b ** 2, axis=-1, keepdims=True))
+    bound = ulp_bf16(np.maximum(np.abs(a), np.abs(b))) * 1.0001 + SHARP_C["decode"] * rms
+    worst = float((np.abs(a - b) / bound).max())
+    say(f"cascade, many pieces, {dtype} vs plain: worst", round(worst, 3), "of the bar")
+    assert worst <= 1.0
+
+
 @pytest.mark.parametrize("prefix,Hq,Hkv,D", [(2048, 32, 8, 128), (256, 8, 2, 64)])
 def test_cascade_fp8(gpu, prefix, Hq, Hkv, D):
     """FP8 pools: the prefix pass widens the same codes as the tail pass."""
