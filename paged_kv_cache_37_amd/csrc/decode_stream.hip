@@ -290,6 +290,7 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_stre
     return;
   }
   const int wg = blockIdx.x, nwg = P.stream_wgs;
+  constexpr bool CASCADE = false;
 #include "stream_body.inc"
 }
 
@@ -312,6 +313,7 @@ __global__ __launch_bounds__(kThreads, KVP_STREAM_WAVES_PER_EU) void decode_casc
   if ((int)blockIdx.x < P.stream_wgs) {
     StreamLds<BS>& L = lds.s;
     const int wg = blockIdx.x, nwg = P.stream_wgs;
+    constexpr bool CASCADE = true;
 #include "stream_body.inc"
   } else {
     using namespace pf;
