@@ -4,7 +4,10 @@ group, head_dim, window, pool dtype, block size) and checks decode
 attention (default variant), the fused write-then-attend step (pool
 bit-exact) and a chunked prefill over the same kind of batch.  The cases
 are small enough for the fp64 oracle and vary what the fixed tests hold
-apart."""
+apart.  KVP_RANDOM_DECODE_CASES and KVP_RANDOM_PREFILL_CASES raise the case
+counts (16 and 12 by default) for a longer sweep."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -15,6 +18,8 @@ from gpu_helpers import Dev, compare, host_to_torch, pool_dtype, reference, say,
 
 pytestmark = pytest.mark.gpu
 
+N_DECODE = int(os.environ.get("KVP_RANDOM_DECODE_CASES", "16"))
+N_PREFILL = int(os.environ.get("KVP_RANDOM_PREFILL_CASES", "12"))
 EDGES = [1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 255, 256, 257]
 
 
@@ -31,7 +36,7 @@ def draw(seed):
     return dict(Hkv=Hkv, Hq=Hkv * G, D=D, dtype=dtype, B=B, lens=lens, window=window)
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(N_DECODE))
 def test_random_decode_and_step(gpu, seed):
     c = draw(seed)
     say("random decode", seed, {k: v for k, v in c.items() if k != "lens"}, "S", len(c["lens"]))
@@ -54,7 +59,7 @@ def test_random_decode_and_step(gpu, seed):
         compare(out, ref, "bf16", f"random step {seed}")
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(N_PREFILL))
 def test_random_prefill(gpu, seed):
     c = draw(seed + 100)
     rng = np.random.default_rng(30_000 + seed)
